@@ -1,0 +1,198 @@
+"""Pins of the oracle's dequantisation and product (CPU only)."""
+from fractions import Fraction
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import linear as olin
+import workload
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_e2m1():
+    vals = {}
+    with open(os.path.join(GOLDEN, "e2m1_ocp_mx.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                c, v = line.split()
+                vals[int(c)] = Fraction(float(v))
+    return vals
+
+
+def _exact_e4m3(byte):
+    # Exact rational value from the OFP8 E4M3 definition (bias 7).
+    s = -1 if byte >> 7 else 1
+    e, m = (byte >> 3) & 15, byte & 7
+    if e == 0:
+        return s * Fraction(m, 8) * Fraction(1, 64)
+    return s * (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+
+
+def _bf16_fraction(bits):
+    return Fraction(float(workload.bf16_bits_to_f32(np.array([bits], np.uint16))[0]))
+
+
+def _brute_force(x_bits, packed, scales, t):
+    """Exact rationals, element by element, reading the nibbles one at a time."""
+    e2m1 = _golden_e2m1()
+    m, k = x_bits.shape
+    n = packed.shape[0]
+    tf = Fraction(float(np.float32(t)))
+    y = [[Fraction(0)] * n for _ in range(m)]
+    for i in range(m):
+        for j in range(n):
+            acc = Fraction(0)
+            for kk in range(k):
+                byte = int(packed[j, kk // 2])
+                code = (byte & 0xF) if kk % 2 == 0 else (byte >> 4)
+                w = tf * _exact_e4m3(int(scales[j, kk // 16])) * e2m1[code]
+                acc += _bf16_fraction(int(x_bits[i, kk])) * w
+            y[i][j] = acc
+    return y
+
+
+@pytest.mark.parametrize("m,n,k,seed", [(1, 1, 16, 1), (2, 3, 32, 2), (3, 5, 48, 3),
+                                        (2, 2, 256, 4), (3, 4, 64, 5)])
+def test_linear_ref_matches_exact_rationals(m, n, k, seed):
+    packed, scales = workload.random_codes(n, k, seed)
+    x = workload.activations_bf16(m, k, seed + 100, outliers=True)
+    t = 0.000123
+    y = oracle.linear_ref(x, packed, scales, t)
+    bnd = oracle.bound(x, packed, scales, t)
+    exact = _brute_force(x, packed, scales, t)
+    u = 2.0 ** -53
+    gamma = k * u / (1 - k * u)
+    for i in range(m):
+        for j in range(n):
+            err = abs(Fraction(float(y[i, j])) - exact[i][j])
+            assert err <= Fraction(gamma) * Fraction(float(bnd[i, j])) * (1 + Fraction(1, 10**6))
+
+
+def test_dequant_is_exact():
+    n, k = 4, 64
+    packed, scales = workload.random_codes(n, k, 7)
+    t = float(np.float32(3.3e-5))
+    wd = oracle.dequant(packed, scales, t)
+    e2m1 = _golden_e2m1()
+    for j in range(n):
+        for kk in range(k):
+            byte = int(packed[j, kk // 2])
+            code = (byte & 0xF) if kk % 2 == 0 else (byte >> 4)
+            exact = Fraction(t) * _exact_e4m3(int(scales[j, kk // 16])) * e2m1[code]
+            assert Fraction(float(wd[j, kk])) == exact
+
+
+def _one_hot_ok():
+    """A single non-zero nibble at (n, k) with x = e_k gives y = that weight alone."""
+    n, k = 3, 256
+    ok = True
+    for row in range(n):
+        for col in (0, 1, 2, 15, 16, 17, 31, 32, 130, 255):
+            packed = np.zeros((n, k // 2), np.uint8)
+            scales = np.full((n, k // 16), 0x38, np.uint8)           # scale 1.0
+            scales[row, col // 16] = 0x40                            # scale 2.0 on that group only
+            code = 7                                                 # e2m1 6.0
+            packed[row, col // 2] = code if col % 2 == 0 else code << 4
+            x = np.zeros((1, k), np.uint16)
+            x[0, col] = 0x3F80                                       # bf16 1.0
+            y = oracle.linear_ref(x, packed, scales, 1.0)
+            want = np.zeros((1, n))
+            want[0, row] = 12.0
+            ok &= np.array_equal(y, want)
+            # the neighbouring element of the same byte contributes nothing
+            x2 = np.zeros((1, k), np.uint16)
+            x2[0, col ^ 1] = 0x3F80
+            ok &= np.array_equal(oracle.linear_ref(x2, packed, scales, 1.0), np.zeros((1, n)))
+    return ok
+
+
+def test_layout_one_hot():
+    assert _one_hot_ok()
+
+
+def test_mutant_nibble_order_fails_one_hot(monkeypatch):
+    monkeypatch.setattr(olin, "nibble_shift", lambda k: 4 * (1 - k % 2))
+    assert not _one_hot_ok()
+
+
+def test_mutant_scale_group_fails_one_hot(monkeypatch):
+    monkeypatch.setattr(olin, "scale_index", lambda k: k // 32)
+    assert not _one_hot_ok()
+
+
+def test_unit_scales_reduce_to_plain_matmul():
+    # All group scales e4m3 1.0 and t = 1: y is x times the e2m1 code values,
+    # a small matrix of halves; numpy's float64 matmul is exact on it.
+    n, k, m = 7, 128, 3
+    g = workload.rng(5)
+    codes = g.integers(0, 16, size=(n, k), dtype=np.uint8)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    scales = np.full((n, k // 16), 0x38, np.uint8)
+    e2m1 = _golden_e2m1()
+    dense = np.array([[float(e2m1[int(c)]) for c in row] for row in codes])
+    xb = workload.activations_bf16(m, k, 6)
+    x = workload.bf16_bits_to_f32(xb).astype(np.float64)
+    # make x small integers / 2 so the matmul is exact in float64
+    x = np.round(x * 4) / 4
+    xb = workload.f32_to_bf16_bits(x.astype(np.float32))
+    assert np.array_equal(oracle.linear_ref(xb, packed, scales, 1.0), x @ dense.T)
+
+
+def test_tensor_scale_multiplies_the_weight():
+    packed, scales = workload.random_codes(5, 64, 9)
+    x = workload.activations_bf16(2, 64, 10)
+    y1 = oracle.linear_ref(x, packed, scales, 1.0)
+    y2 = oracle.linear_ref(x, packed, scales, 0.25)
+    assert np.array_equal(y2, y1 * 0.25)
+
+
+def test_column_sampling_matches_full():
+    packed, scales = workload.random_codes(300, 256, 12)
+    x = workload.activations_bf16(3, 256, 13)
+    full = oracle.linear_ref(x, packed, scales, 0.01)
+    cols = np.array([0, 5, 299, 128])
+    bfull = oracle.bound(x, packed, scales, 0.01)
+    # BLAS may block the sum differently for another shape: agree to fp64 rounding.
+    gamma = 2 * 256 * 2.0 ** -53
+    got = oracle.linear_ref(x, packed, scales, 0.01, cols)
+    assert np.all(np.abs(got - full[:, cols]) <= gamma * bfull[:, cols])
+    assert np.allclose(oracle.bound(x, packed, scales, 0.01, cols), bfull[:, cols], rtol=gamma, atol=0)
+
+
+def test_row_blocks_do_not_change_the_result(monkeypatch):
+    packed, scales = workload.random_codes(50, 64, 14)
+    x = workload.activations_bf16(2, 64, 15)
+    a = oracle.linear_ref(x, packed, scales, 0.5)
+    bnd = oracle.bound(x, packed, scales, 0.5)
+    monkeypatch.setattr(olin, "ROW_BLOCK", 7)
+    gamma = 2 * 64 * 2.0 ** -53
+    assert np.all(np.abs(oracle.linear_ref(x, packed, scales, 0.5) - a) <= gamma * bnd)
+
+
+def test_bound_is_sum_of_absolute_products():
+    packed, scales = workload.random_codes(4, 32, 16)
+    x = workload.activations_bf16(2, 32, 17)
+    bnd = oracle.bound(x, packed, scales, 1.0)
+    exact = _brute_force(x, packed, scales, 1.0)
+    assert np.all(bnd >= np.abs(np.array([[float(v) for v in r] for r in exact])))
+
+
+def test_accept_tolerance():
+    y_ref = np.array([[1.0, -2.0, 0.0]])
+    bnd = np.array([[10.0, 10.0, 0.0]])
+    assert oracle.accept(y_ref, y_ref, bnd)
+    assert oracle.accept(y_ref + np.array([[0.0199, -0.0199, 0]]), y_ref, bnd)
+    assert not oracle.accept(y_ref + np.array([[0.0201, 0, 0]]), y_ref, bnd)
+    assert oracle.accept(y_ref + np.array([[0, 0, 9e-7]]), y_ref, bnd)
+    assert not oracle.accept(y_ref + np.array([[0, 0, 2e-6]]), y_ref, bnd)
+    nan = y_ref.copy(); nan[0, 1] = np.nan
+    assert not oracle.accept(nan, y_ref, bnd)
+    assert oracle.accept(nan, nan, bnd)
+
+
+def test_bf16_rounding_fits_the_tolerance():
+    # One bf16 rounding has relative error <= 2^-9 < 2e-3.
+    assert 2.0 ** -9 < oracle.linear.REL_TOL

@@ -193,6 +193,26 @@ def test_accept_tolerance():
     assert oracle.accept(nan, nan, bnd)
 
 
-def test_bf16_rounding_fits_the_tolerance():
-    # One bf16 rounding has relative error <= 2^-9 < 2e-3.
-    assert 2.0 ** -9 < oracle.linear.REL_TOL
+def test_bf16_output_allowance_covers_exact_rounding():
+    # One dominating product: |y| equals the bound, and the nearest bf16 of the
+    # exact result misses it by almost 2^-8 of |y| -- more than 2e-3 * bound.
+    import torch
+    y_ref = np.array([[4175.84]])
+    bnd = y_ref.copy()
+    y16 = torch.from_numpy(y_ref).to(torch.bfloat16).double().numpy()
+    assert not oracle.accept(y16, y_ref, bnd, out="f32")
+    assert oracle.accept(y16, y_ref, bnd, out="bf16")
+    # random sums: the nearest bf16 of the exact result is always accepted
+    packed, scales = workload.random_codes(50, 256, 20)
+    x = workload.activations_bf16(8, 256, 21, outliers=True)
+    y_ref = oracle.linear_ref(x, packed, scales, 0.03)
+    bnd = oracle.bound(x, packed, scales, 0.03)
+    y16 = torch.from_numpy(y_ref).to(torch.bfloat16).double().numpy()
+    assert oracle.accept(y16, y_ref, bnd, out="bf16")
+    # but a full bf16 ulp off is not
+    worst = np.abs(y_ref) >= 0.9 * bnd
+    if worst.any():
+        bumped = y16 + np.where(worst, np.abs(y16) * 2.0 ** -6, 0)
+        assert not oracle.accept(bumped, y_ref, bnd, out="bf16")
+    with pytest.raises(ValueError):
+        oracle.tolerance(y_ref, bnd, out="f16")

@@ -1,0 +1,132 @@
+"""Parity of the HIP path with the fp64 oracle on the workloads' shapes, and
+bit-exact row invariance across M = 1..32 (gpu)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import verify_nvfp4_w4a16_amd as nv
+import workload
+from tests._gpu import DEV, Weight, bits, check_parity, run, to_f64, upload_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def inv_weight():
+    s = workload.INVARIANCE
+    return Weight.from_f32(workload.weights_f32(s.n, s.k, workload.SEEDS["invariance"][0]))
+
+
+@pytest.fixture(scope="module")
+def inv_x():
+    return workload.activations_bf16(32, workload.INVARIANCE.k, workload.SEEDS["invariance"][1])
+
+
+def test_single_linear_parity():
+    s = workload.SINGLE
+    ws, xs = workload.SEEDS["single"]
+    w = Weight.from_f32(workload.weights_f32(s.n, s.k, ws))
+    x = workload.activations_bf16(1, s.k, xs)
+    check_parity(run(x, w), x, w, label="single 1024x1024")
+
+
+def test_invariance_parity_every_m(inv_weight, inv_x):
+    w = inv_weight
+    y_ref = oracle.linear_ref(inv_x, w.packed, w.scales, w.t)
+    bnd = oracle.bound(inv_x, w.packed, w.scales, w.t)
+    worst = 0.0
+    for m in range(1, 33):
+        y = run(inv_x[:m], w)
+        viol = oracle.max_violation(to_f64(y), y_ref[:m], bnd[:m], "bf16")
+        worst = max(worst, viol)
+        assert viol <= 1.0, f"M={m}: max err/tol {viol}"
+    print(f"[parity] invariance 4096x4096 M=1..32 worst err/tol = {worst:.3g}", flush=True)
+
+
+def test_row_invariance_bit_exact(inv_weight, inv_x):
+    w = inv_weight
+    alone = [bits(run(inv_x[r:r + 1], w))[0].clone() for r in range(32)]
+    for m in range(1, 33):
+        y = bits(run(inv_x[:m], w))
+        for r in range(m):
+            assert torch.equal(y[r], alone[r]), f"row {r} differs at M={m}"
+    # a row's bits do not depend on its position either
+    x_rev = np.ascontiguousarray(inv_x[::-1])
+    y = bits(run(x_rev, w))
+    for r in range(32):
+        assert torch.equal(y[31 - r], alone[r])
+    print("[invariance] 4096x4096: every row bit-identical at M=1..32 and any position", flush=True)
+
+
+def test_qkv_outliers_parity_and_invariance():
+    s = workload.QKV
+    ws, xs = workload.SEEDS["qkv"]
+    w = Weight.from_f32(workload.weights_f32(s.n, s.k, ws))
+    x = workload.activations_bf16(32, s.k, xs, outliers=True)
+    check_parity(run(x, w), x, w, label="qkv 12288x4096 outliers")
+    check_parity(run(x[:16], w), x[:16], w, label="qkv 12288x4096 outliers")
+    alone = [bits(run(x[r:r + 1], w))[0].clone() for r in range(32)]
+    for m in range(16, 33):
+        y = bits(run(x[:m], w))
+        for r in range(m):
+            assert torch.equal(y[r], alone[r]), f"row {r} differs at M={m}"
+
+
+def test_round_shapes_parity():
+    rng = workload.rng(77)
+    for proj, s in enumerate(workload.ROUND_SHAPES):
+        w = Weight.from_f32(workload.weights_f32(s.n, s.k, workload.round_weight_seed(0, proj)))
+        cols = np.unique(np.concatenate([np.arange(64), np.arange(s.n - 64, s.n),
+                                         rng.integers(0, s.n, 1024)]))
+        for m in workload.ROUND_M:
+            x = workload.activations_bf16(m, s.k, workload.round_act_seed(0, proj, m))
+            check_parity(run(x, w), x, w, cols=cols, label=f"round proj{proj}")
+
+
+def test_head_fp32_parity_and_gemv_vs_mfma_rows():
+    s = workload.HEAD
+    ws, xs = workload.SEEDS["head"]
+    w = Weight.from_f32(workload.weights_f32(s.n, s.k, ws))
+    x = workload.activations_bf16(32, s.k, xs)
+    rng = workload.rng(78)
+    cols = np.unique(np.concatenate([np.arange(64), np.arange(s.n - 64, s.n),
+                                     rng.integers(0, s.n, 2048)]))
+    y1 = run(x[:1], w, torch.float32)
+    check_parity(y1, x[:1], w, cols=cols, label="head fp32 M=1")
+    y32 = run(x, w, torch.float32)
+    check_parity(y32, x, w, cols=cols, label="head fp32 M=32")
+    y5 = run(x[:5], w, torch.float32)
+    check_parity(y5, x[:5], w, cols=cols, label="head fp32 M=5")
+    same = torch.equal(bits(y32)[0], bits(y1)[0]) and torch.equal(bits(y5), bits(y32)[:5])
+    print(f"[invariance] head: M=1 (GEMV) row == M=32 row 0: {same}", flush=True)
+    assert same
+
+
+def test_random_codes_full_scale_range():
+    # Every e2m1 code and every finite non-negative scale byte, incl. subnormal
+    # scales and zero groups, with a ragged N.
+    for n, k, m in [(1, 256, 1), (17, 256, 3), (333, 1024, 32), (1000, 2048, 16), (4111, 512, 19)]:
+        packed, scales = workload.random_codes(n, k, n + k)
+        scales[:, ::5] = 0
+        w = Weight(packed, scales, 0.0371)
+        x = workload.activations_bf16(m, k, n * 3 + m, outliers=True)
+        check_parity(run(x, w), x, w, label="random codes")
+        check_parity(run(x, w, torch.float32), x, w, label="random codes fp32")
+
+
+def test_nan_scale_propagates_like_the_oracle():
+    n, k = 40, 256
+    packed, scales = workload.random_codes(n, k, 5)
+    scales[7, 3] = 0x7F
+    w = Weight(packed, scales, 1.0)
+    x = workload.activations_bf16(2, k, 6)
+    y = to_f64(run(x, w, torch.float32))
+    assert np.isnan(y[:, 7]).all() and not np.isnan(np.delete(y, 7, axis=1)).any()
+    check_parity(run(x, w, torch.float32), x, w, label="nan scale")
+
+
+def test_bf16_output_is_rounded_fp32_output(inv_weight, inv_x):
+    y32 = run(inv_x[:7], inv_weight, torch.float32)
+    y16 = run(inv_x[:7], inv_weight, torch.bfloat16)
+    assert torch.equal(y32.to(torch.bfloat16).view(torch.int16), y16.view(torch.int16))

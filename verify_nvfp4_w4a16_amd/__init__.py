@@ -1,0 +1,146 @@
+"""Python binding of libnvfp4_w4a16.so: the NVFP4 weight-only (W4A16) skinny
+product on MI355X (gfx950).
+
+Argument marshalling only: every step of the product runs in the library's HIP
+kernels, every host step (packing, shape checks) in its C++.  PyTorch supplies
+device memory and streams.  The C functions are declared, with their contracts,
+in include/nvfp4_w4a16.h; the names here are the same without the prefix.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libnvfp4_w4a16.so")
+
+OK = 0
+ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_NONFINITE = -1, -2, -3, -4, -5
+ERR_BADSCALE, ERR_HIP, ERR_DEVICE, ERR_TILEFILE, ERR_BUFFER = -6, -7, -8, -9, -10
+OUT_BF16, OUT_F32 = 0, 1
+MAX_M = 32
+K_MULTIPLE = 256
+
+EXPORTED = ("nvfp4_pack", "nvfp4_check_scales", "nvfp4_linear_shape_ok", "nvfp4_init",
+            "nvfp4_linear", "nvfp4_tile_info", "nvfp4_strerror")
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing; build it with "
+                          "`python -m verify_nvfp4_w4a16_amd.build` (no fallback exists)")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, vp, u8p = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p
+    lib.nvfp4_pack.argtypes = [vp, i64, i64, u8p, u8p, ctypes.POINTER(ctypes.c_float)]
+    lib.nvfp4_check_scales.argtypes = [u8p, i64, i64]
+    lib.nvfp4_linear_shape_ok.argtypes = [i64, i64, i64]
+    lib.nvfp4_init.argtypes = []
+    lib.nvfp4_linear.argtypes = [vp, vp, vp, ctypes.c_float, vp, i64, i64, i64, ctypes.c_int, vp]
+    lib.nvfp4_tile_info.argtypes = [i64, i64, ctypes.c_char_p, i64]
+    lib.nvfp4_strerror.argtypes = [ctypes.c_int]
+    lib.nvfp4_strerror.restype = ctypes.c_char_p
+    for name in EXPORTED:
+        if name != "nvfp4_strerror":
+            getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+_LIB = None
+
+
+def _lib() -> ctypes.CDLL:
+    """The loaded library; raises ImportError when it has not been built."""
+    global _LIB
+    if _LIB is None:
+        _LIB = _load()
+    return _LIB
+
+
+def strerror(status: int) -> str:
+    return _lib().nvfp4_strerror(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != OK:
+        raise Nvfp4Error(status, where)
+
+
+def pack(w: np.ndarray) -> tuple[np.ndarray, np.ndarray, float]:
+    """fp32 W[N, K] -> (packed [N, K/2] uint8, scales [N, K/16] uint8, tensor_scale)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    if w.ndim != 2:
+        raise ValueError("w must be 2-D [N, K]")
+    n, k = w.shape
+    packed = np.empty((n, max(k // 2, 0)), np.uint8)
+    scales = np.empty((n, max(k // 16, 0)), np.uint8)
+    t = ctypes.c_float()
+    _check(_lib().nvfp4_pack(w.ctypes.data, n, k, packed.ctypes.data, scales.ctypes.data,
+                          ctypes.byref(t)), "nvfp4_pack")
+    return packed, scales, float(t.value)
+
+
+def check_scales(scales: np.ndarray) -> int:
+    """Status of nvfp4_check_scales for a [N, K/16] scale array (OK or ERR_BADSCALE)."""
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    return _lib().nvfp4_check_scales(scales.ctypes.data, scales.shape[0], scales.shape[1] * 16)
+
+
+def linear_shape_ok(m: int, n: int, k: int) -> bool:
+    return _lib().nvfp4_linear_shape_ok(m, n, k) == OK
+
+
+def init() -> None:
+    _check(_lib().nvfp4_init(), "nvfp4_init")
+
+
+def tile_info(n: int, k: int) -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check(_lib().nvfp4_tile_info(n, k, buf, len(buf)), "nvfp4_tile_info")
+    return buf.value.decode()
+
+
+def linear_raw(x_ptr: int, w_ptr: int, s_ptr: int, tensor_scale: float, y_ptr: int,
+               m: int, n: int, k: int, y_dtype: int, stream: int) -> int:
+    """nvfp4_linear on raw device addresses; returns the status."""
+    return _lib().nvfp4_linear(x_ptr, w_ptr, s_ptr, ctypes.c_float(tensor_scale), y_ptr,
+                            m, n, k, y_dtype, stream)
+
+
+def linear(x, w_packed, scales, tensor_scale: float, out=None, out_dtype=None, stream=None):
+    """y[M, N] = x[M, K] . dequant(W)^T on the GPU (torch tensors on one device).
+
+    x: bf16 [M, K]; w_packed: uint8 [N, K/2]; scales: uint8 [N, K/16];
+    out: bf16 or float32 [M, N] (allocated when None; dtype from out_dtype,
+    default bf16).  Runs on `stream` (default: torch's current stream)."""
+    import torch
+    if x.dtype != torch.bfloat16 or w_packed.dtype != torch.uint8 or scales.dtype != torch.uint8:
+        raise TypeError("x must be bfloat16; w_packed and scales uint8")
+    if x.dim() != 2 or w_packed.dim() != 2 or scales.dim() != 2:
+        raise ValueError("x, w_packed, scales must be 2-D")
+    m, k = x.shape
+    n = w_packed.shape[0]
+    if tuple(w_packed.shape) != (n, k // 2) or tuple(scales.shape) != (n, k // 16):
+        raise ValueError(f"weight shapes {tuple(w_packed.shape)}, {tuple(scales.shape)} "
+                         f"do not match K={k}")
+    for name, tns in (("x", x), ("w_packed", w_packed), ("scales", scales)):
+        if not tns.is_cuda or not tns.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype or torch.bfloat16, device=x.device)
+    if out.dtype not in (torch.bfloat16, torch.float32) or tuple(out.shape) != (m, n) \
+            or not out.is_contiguous() or out.device != x.device:
+        raise ValueError("out must be a contiguous bf16 or float32 [M, N] tensor on x's device")
+    y_dtype = OUT_F32 if out.dtype == torch.float32 else OUT_BF16
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    _check(linear_raw(x.data_ptr(), w_packed.data_ptr(), scales.data_ptr(), tensor_scale,
+                      out.data_ptr(), m, n, k, y_dtype, stream.cuda_stream), "nvfp4_linear")
+    return out

@@ -1,0 +1,103 @@
+// (N, K)-keyed tile table and its default rule.  See tiles.h.
+#include "tiles.h"
+
+#include <cstdio>
+#include <cstdlib>
+#include <fstream>
+#include <map>
+#include <mutex>
+#include <sstream>
+#include <utility>
+
+#include "nvfp4_w4a16.h"
+
+namespace nvfp4 {
+namespace {
+
+using Key = std::pair<int64_t, int64_t>;
+
+// Built-in entries chosen by sweeping launch settings on MI355X, keeping only
+// settings whose output bits equal the default's at every row count 1..32.
+const std::map<Key, Tile>& builtin_table() {
+    static const std::map<Key, Tile> table = {};
+    return table;
+}
+
+std::map<Key, Tile>& override_table() {
+    static std::map<Key, Tile> table;
+    return table;
+}
+
+// Default: one 16-column tile per wavefront, and as many wavefronts along K
+// as keep at least two 128-k blocks each, up to 8.
+Tile default_tile(int64_t /*n*/, int64_t k) {
+    Tile t;
+    t.cols = 16;
+    int64_t blocks = k / 128;
+    int waves = 8;
+    while (waves > 1 && (blocks % waves != 0 || blocks / waves < 2)) waves /= 2;
+    t.waves = waves;
+    return t;
+}
+
+}  // namespace
+
+bool tile_valid(const Tile& t, int64_t /*n*/, int64_t k) {
+    if (t.cols != 16 && t.cols != 32 && t.cols != 64) return false;
+    if (t.waves < 1 || t.waves > 16) return false;
+    int64_t blocks = k / 128;
+    return blocks % t.waves == 0;
+}
+
+Tile tile_for(int64_t n, int64_t k) {
+    Key key{n, k};
+    auto& ov = override_table();
+    auto it = ov.find(key);
+    if (it != ov.end()) return it->second;
+    auto& bt = builtin_table();
+    auto jt = bt.find(key);
+    if (jt != bt.end() && tile_valid(jt->second, n, k)) return jt->second;
+    return default_tile(n, k);
+}
+
+static int read_override_file() {
+    const char* path = std::getenv("NVFP4_TILES");
+    if (!path || !*path) return NVFP4_OK;
+    std::ifstream in(path);
+    if (!in) return NVFP4_ERR_TILEFILE;
+    std::map<Key, Tile> table;
+    std::string line;
+    while (std::getline(in, line)) {
+        auto hash = line.find('#');
+        if (hash != std::string::npos) line.resize(hash);
+        std::istringstream ss(line);
+        int64_t n, k;
+        Tile t;
+        if (!(ss >> n)) continue;                       // blank line
+        if (!(ss >> k >> t.cols >> t.waves)) return NVFP4_ERR_TILEFILE;
+        if (nvfp4_linear_shape_ok(1, n, k) != NVFP4_OK || !tile_valid(t, n, k))
+            return NVFP4_ERR_TILEFILE;
+        table[{n, k}] = t;
+    }
+    override_table() = std::move(table);
+    return NVFP4_OK;
+}
+
+int load_tile_override() {
+    static std::once_flag once;
+    static int status = NVFP4_OK;
+    std::call_once(once, [] { status = read_override_file(); });
+    return status;
+}
+
+std::string tile_text(int64_t n, int64_t k, const Tile& t) {
+    char buf[256];
+    int64_t groups = (n + t.cols - 1) / t.cols;
+    std::snprintf(buf, sizeof buf,
+                  "N=%lld K=%lld cols=%d waves=%d k_per_wave=%lld grid=%lld block=%d",
+                  (long long)n, (long long)k, t.cols, t.waves,
+                  (long long)(k / t.waves), (long long)groups, 64 * t.waves);
+    return buf;
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,39 @@
+// Launch tiles of the NVFP4 skinny product, keyed by the weight shape (N, K).
+//
+// "10 Kernels", section 10.1: every tile table is keyed by the weight's shape,
+// never by the row count, so the reduction over K runs in the same order at 1
+// row and at 32; section 10.2 keeps a per-shape table of launch settings that
+// a sweep picked.  Here a tile fixes, for one (N, K):
+//   cols  - weight rows (output columns) one wavefront owns: 16, 32 or 64;
+//   waves - wavefronts of one workgroup, each taking an equal, contiguous
+//           share of K; their partial sums are added in wavefront order.
+// The per-output reduction order is a function of the tile only, and the tile
+// is a function of (N, K) only.
+#pragma once
+#include <cstdint>
+#include <string>
+
+namespace nvfp4 {
+
+struct Tile {
+    int cols = 16;   // 16 * C, C in {1, 2, 4}
+    int waves = 8;   // wavefronts per workgroup (split of K), 1..16
+};
+
+// Checks a tile against a shape: cols in {16, 32, 64}; waves in 1..16 and
+// dividing K / 128 (whole 128-k blocks per wavefront).
+bool tile_valid(const Tile& t, int64_t n, int64_t k);
+
+// The tile for (N, K): the override table if one was loaded, else the built-in
+// table, else the default rule.  Never depends on M.
+Tile tile_for(int64_t n, int64_t k);
+
+// Loads, once per process, the override table from the file named by the
+// environment variable NVFP4_TILES (if set), so the table is constant for the
+// life of the process.  Lines: "N K cols waves"; '#' starts a comment.
+// Returns NVFP4_OK or NVFP4_ERR_TILEFILE (the same status on every call).
+int load_tile_override();
+
+std::string tile_text(int64_t n, int64_t k, const Tile& t);
+
+}  // namespace nvfp4

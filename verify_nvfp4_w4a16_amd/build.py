@@ -23,7 +23,7 @@ HOST_SOURCES = ["host/pack.cpp", "host/tiles.cpp"]
 HIP_SOURCES = ["kernels/nvfp4_linear.hip"]
 
 # -ffp-contract=off keeps the packer's float64 steps unfused (bit-exact rule).
-HOST_FLAGS = ["-std=c++17", "-O2", "-fPIC", "-ffp-contract=off", "-Wall", "-Wextra",
+HOST_FLAGS = ["-std=c++17", "-O3", "-fPIC", "-ffp-contract=off", "-Wall", "-Wextra",
               "-pthread", "-I", INCLUDE]
 # Packed fp32 instructions are kept out of the device code on purpose.
 HIP_FLAGS = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}",

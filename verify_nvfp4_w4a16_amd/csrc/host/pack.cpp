@@ -11,6 +11,8 @@
 // global maximum is known, and each row is written by exactly one thread.
 #include "nvfp4_w4a16.h"
 
+#include <sched.h>
+
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
@@ -57,16 +59,11 @@ uint8_t e4m3_encode(double u) {
 
 // Nearest e2m1 magnitude code (0..7 for 0, .5, 1, 1.5, 2, 3, 4, 6) to a >= 0,
 // ties to the even code, saturating at 6.  The thresholds are the midpoints
-// between neighbouring magnitudes; "<=" or "<" picks the even side of a tie.
-uint8_t e2m1_encode_magnitude(double a) {
-    if (a <= 0.25) return 0;
-    if (a < 0.75) return 1;
-    if (a <= 1.25) return 2;
-    if (a < 1.75) return 3;
-    if (a <= 2.5) return 4;
-    if (a < 3.5) return 5;
-    if (a <= 5.0) return 6;
-    return 7;
+// between neighbouring magnitudes; ">" or ">=" puts a tie on the even side.
+// Counting the thresholds passed keeps the loop free of branches.
+inline uint8_t e2m1_encode_magnitude(double a) {
+    return static_cast<uint8_t>((a > 0.25) + (a >= 0.75) + (a > 1.25) + (a >= 1.75) +
+                                (a > 2.5) + (a >= 3.5) + (a > 5.0));
 }
 
 void pack_rows(const float* w, int64_t k, int64_t row0, int64_t row1, double t,
@@ -96,10 +93,26 @@ void pack_rows(const float* w, int64_t k, int64_t row0, int64_t row1, double t,
     }
 }
 
+// Threads the packer may use: the CPUs this process may run on, at most 16.
+int cpu_budget() {
+    cpu_set_t set;
+    if (sched_getaffinity(0, sizeof set, &set) == 0) return std::max(1, std::min(16, CPU_COUNT(&set)));
+    return std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+}
+
+template <class F>
+void run_parallel(int workers, F&& f) {
+    if (workers == 1) { f(0); return; }
+    std::vector<std::thread> pool;
+    pool.reserve(workers);
+    for (int i = 0; i < workers; ++i) pool.emplace_back(f, i);
+    for (auto& th : pool) th.join();
+}
+
 int worker_count(int64_t rows, int64_t k) {
-    unsigned hw = std::thread::hardware_concurrency();
+    int hw = cpu_budget();
     int64_t by_work = (rows * k) / (1 << 20) + 1;     // at least ~1M weights per thread
-    int64_t t = std::min<int64_t>(std::max(1u, hw), by_work);
+    int64_t t = std::min<int64_t>(hw, by_work);
     return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(t, rows)));
 }
 
@@ -109,30 +122,39 @@ extern "C" int nvfp4_pack(const float* w, int64_t n, int64_t k, uint8_t* w_packe
                           uint8_t* scales_e4m3, float* tensor_scale) {
     if (!w || !w_packed || !scales_e4m3 || !tensor_scale) return NVFP4_ERR_NULL;
     if (n < 1 || k < kGroup || k % kGroup) return NVFP4_ERR_SHAPE;
-    const int64_t total = n * k;
+    int workers = worker_count(n, k);
+    // Q1: the largest magnitude (a maximum is exact in any order) and the
+    // finiteness check, over row ranges in parallel.
+    std::vector<double> part_max(workers, 0.0);
+    std::vector<int> part_bad(workers, 0);
+    const int64_t per = (n + workers - 1) / workers;
+    auto scan = [&](int i) {
+        int64_t r0 = i * per, r1 = std::min(n, r0 + per);
+        double m = 0.0;
+        int bad = 0;
+        for (int64_t j = r0 * k; j < r1 * k; ++j) {
+            double a = std::fabs(double(w[j]));
+            bad |= !std::isfinite(a);
+            m = std::max(m, a);
+        }
+        part_max[i] = m;
+        part_bad[i] = bad;
+    };
+    run_parallel(workers, scan);
     double amax = 0.0;
-    for (int64_t i = 0; i < total; ++i) {
-        double a = std::fabs(double(w[i]));
-        if (!std::isfinite(a)) return NVFP4_ERR_NONFINITE;
-        amax = std::max(amax, a);
+    for (int i = 0; i < workers; ++i) {
+        if (part_bad[i]) return NVFP4_ERR_NONFINITE;
+        amax = std::max(amax, part_max[i]);
     }
     float t32 = static_cast<float>(amax / (kE2m1Max * kE4m3Max));
     if (amax == 0.0 || t32 == 0.0f) t32 = 1.0f;
     const double t = double(t32);
 
-    int workers = worker_count(n, k);
-    if (workers == 1) {
-        pack_rows(w, k, 0, n, t, w_packed, scales_e4m3);
-    } else {
-        std::vector<std::thread> pool;
-        int64_t per = (n + workers - 1) / workers;
-        for (int i = 0; i < workers; ++i) {
-            int64_t r0 = i * per, r1 = std::min(n, r0 + per);
-            if (r0 >= r1) break;
-            pool.emplace_back(pack_rows, w, k, r0, r1, t, w_packed, scales_e4m3);
-        }
-        for (auto& th : pool) th.join();
-    }
+    // Q2..Q6 row by row; each row is written by exactly one thread.
+    run_parallel(workers, [&](int i) {
+        int64_t r0 = i * per, r1 = std::min(n, r0 + per);
+        if (r0 < r1) pack_rows(w, k, r0, r1, t, w_packed, scales_e4m3);
+    });
     *tensor_scale = t32;
     return NVFP4_OK;
 }

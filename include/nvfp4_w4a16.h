@@ -51,7 +51,8 @@ enum {
     NVFP4_ERR_HIP = -7,       /* a HIP runtime call failed */
     NVFP4_ERR_DEVICE = -8,    /* the current device is not gfx950 */
     NVFP4_ERR_TILEFILE = -9,  /* the NVFP4_TILES override file is unreadable or invalid */
-    NVFP4_ERR_BUFFER = -10    /* nvfp4_tile_info: the text buffer is too small */
+    NVFP4_ERR_BUFFER = -10,   /* nvfp4_tile_info: the text buffer is too small */
+    NVFP4_ERR_TILE = -11      /* nvfp4_linear_tiled: the tile does not fit the shape */
 };
 
 /* Largest row count of one nvfp4_linear call. */
@@ -122,6 +123,22 @@ int nvfp4_init(void);
 int nvfp4_linear(const void* x_bf16, const uint8_t* w_packed,
                  const uint8_t* scales_e4m3, float tensor_scale, void* y,
                  int64_t m, int64_t n, int64_t k, int y_dtype, void* stream);
+
+/*
+ * Device, asynchronous: nvfp4_linear with an explicit launch tile instead of
+ * the (N, K) table's, for tile sweeps ("10 Kernels", section 10.2: the tables
+ * hold the launch settings a sweep picked).  cols: output columns per
+ * wavefront (16, 32 or 64); waves: wavefronts per workgroup (1..8), each
+ * summing one of `waves` equal K segments, added in segment order; unroll:
+ * 128-k blocks per pipeline step (1, 2 or 4), with K a multiple of
+ * 128 * unroll * waves.  cols and unroll never change the result's bits;
+ * waves does (it is the K segmentation).
+ * Errors: those of nvfp4_linear, and TILE for a tile that does not fit.
+ */
+int nvfp4_linear_tiled(const void* x_bf16, const uint8_t* w_packed,
+                       const uint8_t* scales_e4m3, float tensor_scale, void* y,
+                       int64_t m, int64_t n, int64_t k, int y_dtype, int cols,
+                       int waves, int unroll, void* stream);
 
 /*
  * Host.  Writes a one-line text description of the tile nvfp4_linear uses for

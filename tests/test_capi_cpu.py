@@ -37,6 +37,7 @@ def test_header_constants_match_binding():
                   (nv.ERR_NONFINITE, "NVFP4_ERR_NONFINITE"), (nv.ERR_BADSCALE, "NVFP4_ERR_BADSCALE"),
                   (nv.ERR_HIP, "NVFP4_ERR_HIP"), (nv.ERR_DEVICE, "NVFP4_ERR_DEVICE"),
                   (nv.ERR_TILEFILE, "NVFP4_ERR_TILEFILE"), (nv.ERR_BUFFER, "NVFP4_ERR_BUFFER"),
+                  (nv.ERR_TILE, "NVFP4_ERR_TILE"),
                   (nv.OUT_BF16, "NVFP4_OUT_BF16"), (nv.OUT_F32, "NVFP4_OUT_F32")]:
         assert enum(c) == py, c
     assert int(re.search(r"#define NVFP4_MAX_M (\d+)", text).group(1)) == nv.MAX_M
@@ -153,13 +154,28 @@ def test_linear_validates_before_any_device_call():
     assert lib.nvfp4_linear(a16, a16, a16, 1.0, a16 + 2, 1, 16, 256, 1, None) == nv.ERR_ALIGN
 
 
+def test_tiled_entry_validates_the_tile():
+    lib = nv._lib()
+    buf = (ctypes.c_uint8 * 64)()
+    a16 = (ctypes.addressof(buf) + 15) & ~15
+    def call(cols, waves, unroll, k=1024, m=1):
+        return lib.nvfp4_linear_tiled(a16, a16, a16, 1.0, a16, m, 16, k, 0, cols, waves, unroll, None)
+    assert call(48, 2, 2) == nv.ERR_TILE
+    assert call(16, 3, 2) == nv.ERR_TILE
+    assert call(16, 2, 3) == nv.ERR_TILE
+    assert call(16, 8, 2) == nv.ERR_TILE             # 1024 / 8 = 128 < 2 * 128
+    assert call(16, 16, 1, k=8192) == nv.ERR_TILE    # more than 8 wavefronts
+    assert call(16, 2, 2, k=100) == nv.ERR_SHAPE
+    assert call(16, 2, 2, m=0) == nv.OK              # M == 0: nothing launched
+
+
 def test_strerror_covers_every_status():
     seen = set()
-    for st in range(-10, 1):
+    for st in range(-11, 1):
         msg = nv.strerror(st)
         assert msg and msg != "unknown status"
         seen.add(msg)
-    assert len(seen) == 11
+    assert len(seen) == 12
     assert nv.strerror(-99) == "unknown status"
 
 
@@ -192,11 +208,11 @@ def _tile_info_in_fresh_process(env_value, n=1024, k=1024):
 def test_tile_override_file(tmp_path):
     # The table is read once per process, so each case runs in its own process.
     f = tmp_path / "tiles.txt"
-    f.write_text("# N K cols waves\n1024 1024 32 4\n")
-    assert "cols=32 waves=4" in _tile_info_in_fresh_process(str(f))
-    f.write_text("1024 1024 48 4\n")
+    f.write_text("# N K cols waves unroll\n1024 1024 32 4 2\n")
+    assert "cols=32 waves=4 unroll=2" in _tile_info_in_fresh_process(str(f))
+    f.write_text("1024 1024 48 4 2\n")
     assert _tile_info_in_fresh_process(str(f)) == f"status {nv.ERR_TILEFILE}"
-    f.write_text("1024 1024 16 3\n")                  # 3 does not divide 1024/128
+    f.write_text("1024 1024 16 3 2\n")                # 3 does not divide 1024/128
     assert _tile_info_in_fresh_process(str(f)) == f"status {nv.ERR_TILEFILE}"
     assert _tile_info_in_fresh_process(str(tmp_path / "missing.txt")) == f"status {nv.ERR_TILEFILE}"
     assert "cols=32" not in _tile_info_in_fresh_process(None)

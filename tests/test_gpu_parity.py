@@ -130,3 +130,22 @@ def test_bf16_output_is_rounded_fp32_output(inv_weight, inv_x):
     y32 = run(inv_x[:7], inv_weight, torch.float32)
     y16 = run(inv_x[:7], inv_weight, torch.bfloat16)
     assert torch.equal(y32.to(torch.bfloat16).view(torch.int16), y16.view(torch.int16))
+
+
+def test_launch_settings_never_change_bits():
+    # Only the K segmentation (waves) enters the arithmetic: every cols/unroll
+    # choice, persistent or per-tile kernel, gives the default tile's bits.
+    s = workload.INVARIANCE
+    w = Weight.from_f32(workload.weights_f32(s.n, s.k, 61))
+    default = nv.tile_info(s.n, s.k)
+    waves = int(default.split("waves=")[1].split()[0])
+    for m in (1, 3, 17, 32):
+        x = upload_bits(workload.activations_bf16(m, s.k, 62 + m))
+        ref = bits(nv.linear(x, w.wp, w.sc, w.t)).clone()
+        for cols in (16, 32, 64):
+            for unroll in (1, 2, 4):
+                if s.k % (128 * unroll * waves):
+                    continue
+                y = nv.linear(x, w.wp, w.sc, w.t, tile=(cols, waves, unroll))
+                torch.cuda.synchronize()
+                assert torch.equal(bits(y), ref), f"M={m} cols={cols} unroll={unroll}"

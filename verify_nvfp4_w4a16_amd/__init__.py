@@ -19,12 +19,13 @@ LIB_PATH = os.path.join(_HERE, "lib", "libnvfp4_w4a16.so")
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_NONFINITE = -1, -2, -3, -4, -5
 ERR_BADSCALE, ERR_HIP, ERR_DEVICE, ERR_TILEFILE, ERR_BUFFER = -6, -7, -8, -9, -10
+ERR_TILE = -11
 OUT_BF16, OUT_F32 = 0, 1
 MAX_M = 32
 K_MULTIPLE = 256
 
 EXPORTED = ("nvfp4_pack", "nvfp4_check_scales", "nvfp4_linear_shape_ok", "nvfp4_init",
-            "nvfp4_linear", "nvfp4_tile_info", "nvfp4_strerror")
+            "nvfp4_linear", "nvfp4_linear_tiled", "nvfp4_tile_info", "nvfp4_strerror")
 
 
 class Nvfp4Error(RuntimeError):
@@ -44,6 +45,8 @@ def _load() -> ctypes.CDLL:
     lib.nvfp4_linear_shape_ok.argtypes = [i64, i64, i64]
     lib.nvfp4_init.argtypes = []
     lib.nvfp4_linear.argtypes = [vp, vp, vp, ctypes.c_float, vp, i64, i64, i64, ctypes.c_int, vp]
+    lib.nvfp4_linear_tiled.argtypes = [vp, vp, vp, ctypes.c_float, vp, i64, i64, i64, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
     lib.nvfp4_tile_info.argtypes = [i64, i64, ctypes.c_char_p, i64]
     lib.nvfp4_strerror.argtypes = [ctypes.c_int]
     lib.nvfp4_strerror.restype = ctypes.c_char_p
@@ -114,7 +117,16 @@ def linear_raw(x_ptr: int, w_ptr: int, s_ptr: int, tensor_scale: float, y_ptr: i
                             m, n, k, y_dtype, stream)
 
 
-def linear(x, w_packed, scales, tensor_scale: float, out=None, out_dtype=None, stream=None):
+def linear_tiled_raw(x_ptr: int, w_ptr: int, s_ptr: int, tensor_scale: float, y_ptr: int,
+                     m: int, n: int, k: int, y_dtype: int, cols: int, waves: int, unroll: int,
+                     stream: int) -> int:
+    """nvfp4_linear_tiled on raw device addresses; returns the status."""
+    return _lib().nvfp4_linear_tiled(x_ptr, w_ptr, s_ptr, ctypes.c_float(tensor_scale), y_ptr,
+                                     m, n, k, y_dtype, cols, waves, unroll, stream)
+
+
+def linear(x, w_packed, scales, tensor_scale: float, out=None, out_dtype=None, stream=None,
+           tile=None):
     """y[M, N] = x[M, K] . dequant(W)^T on the GPU (torch tensors on one device).
 
     x: bf16 [M, K]; w_packed: uint8 [N, K/2]; scales: uint8 [N, K/16];
@@ -141,6 +153,13 @@ def linear(x, w_packed, scales, tensor_scale: float, out=None, out_dtype=None, s
     y_dtype = OUT_F32 if out.dtype == torch.float32 else OUT_BF16
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
-    _check(linear_raw(x.data_ptr(), w_packed.data_ptr(), scales.data_ptr(), tensor_scale,
-                      out.data_ptr(), m, n, k, y_dtype, stream.cuda_stream), "nvfp4_linear")
+    if tile is None:
+        st = linear_raw(x.data_ptr(), w_packed.data_ptr(), scales.data_ptr(), tensor_scale,
+                        out.data_ptr(), m, n, k, y_dtype, stream.cuda_stream)
+    else:
+        cols, waves, unroll = tile
+        st = linear_tiled_raw(x.data_ptr(), w_packed.data_ptr(), scales.data_ptr(), tensor_scale,
+                              out.data_ptr(), m, n, k, y_dtype, cols, waves, unroll,
+                              stream.cuda_stream)
+    _check(st, "nvfp4_linear" if tile is None else "nvfp4_linear_tiled")
     return out

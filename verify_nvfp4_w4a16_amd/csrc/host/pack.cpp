@@ -190,6 +190,7 @@ extern "C" const char* nvfp4_strerror(int status) {
         case NVFP4_ERR_DEVICE: return "current device is not gfx950 (MI355X)";
         case NVFP4_ERR_TILEFILE: return "NVFP4_TILES override file unreadable or invalid";
         case NVFP4_ERR_BUFFER: return "text buffer too small";
+        case NVFP4_ERR_TILE: return "launch tile does not fit the shape";
         default: return "unknown status";
     }
 }

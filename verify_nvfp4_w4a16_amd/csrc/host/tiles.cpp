@@ -28,15 +28,18 @@ std::map<Key, Tile>& override_table() {
     return table;
 }
 
-// Default: one 16-column tile per wavefront, and as many wavefronts along K
-// as keep at least two 128-k blocks each, up to 8.
+// Default: one 16-column tile per wavefront; K cut into at most 8 segments
+// of whole 128-k blocks (a function of K alone); up to four blocks per
+// pipeline step.
 Tile default_tile(int64_t /*n*/, int64_t k) {
     Tile t;
     t.cols = 16;
     int64_t blocks = k / 128;
     int waves = 8;
-    while (waves > 1 && (blocks % waves != 0 || blocks / waves < 2)) waves /= 2;
+    while (waves > 1 && blocks % waves != 0) waves /= 2;
     t.waves = waves;
+    int64_t per = blocks / waves;
+    t.unroll = per % 4 == 0 ? 4 : per % 2 == 0 ? 2 : 1;
     return t;
 }
 
@@ -44,9 +47,10 @@ Tile default_tile(int64_t /*n*/, int64_t k) {
 
 bool tile_valid(const Tile& t, int64_t /*n*/, int64_t k) {
     if (t.cols != 16 && t.cols != 32 && t.cols != 64) return false;
-    if (t.waves < 1 || t.waves > 16) return false;
-    int64_t blocks = k / 128;
-    return blocks % t.waves == 0;
+    if (t.waves < 1 || t.waves > 8) return false;
+    if (t.unroll != 1 && t.unroll != 2 && t.unroll != 4) return false;
+    if (k % (int64_t(128) * t.unroll * t.waves) != 0) return false;
+    return true;
 }
 
 Tile tile_for(int64_t n, int64_t k) {
@@ -74,7 +78,7 @@ static int read_override_file() {
         int64_t n, k;
         Tile t;
         if (!(ss >> n)) continue;                       // blank line
-        if (!(ss >> k >> t.cols >> t.waves)) return NVFP4_ERR_TILEFILE;
+        if (!(ss >> k >> t.cols >> t.waves >> t.unroll)) return NVFP4_ERR_TILEFILE;
         if (nvfp4_linear_shape_ok(1, n, k) != NVFP4_OK || !tile_valid(t, n, k))
             return NVFP4_ERR_TILEFILE;
         table[{n, k}] = t;
@@ -94,8 +98,8 @@ std::string tile_text(int64_t n, int64_t k, const Tile& t) {
     char buf[256];
     int64_t groups = (n + t.cols - 1) / t.cols;
     std::snprintf(buf, sizeof buf,
-                  "N=%lld K=%lld cols=%d waves=%d k_per_wave=%lld grid=%lld block=%d",
-                  (long long)n, (long long)k, t.cols, t.waves,
+                  "N=%lld K=%lld cols=%d waves=%d unroll=%d k_per_wave=%lld grid=%lld block=%d",
+                  (long long)n, (long long)k, t.cols, t.waves, t.unroll,
                   (long long)(k / t.waves), (long long)groups, 64 * t.waves);
     return buf;
 }

@@ -6,9 +6,12 @@
 // a sweep picked.  Here a tile fixes, for one (N, K):
 //   cols  - weight rows (output columns) one wavefront owns: 16, 32 or 64;
 //   waves - wavefronts of one workgroup, each taking an equal, contiguous
-//           share of K; their partial sums are added in wavefront order.
-// The per-output reduction order is a function of the tile only, and the tile
-// is a function of (N, K) only.
+//           share (slice) of K; their partial sums are added in slice order;
+//   unroll - 128-k blocks a wavefront loads per step of its software
+//           pipeline (1, 2 or 4).
+// Only `waves` enters the arithmetic of an output (how K is sliced); `cols`
+// and `unroll` change the launch, never the bits.  The tile is a function of
+// (N, K) only.
 #pragma once
 #include <cstdint>
 #include <string>
@@ -17,11 +20,12 @@ namespace nvfp4 {
 
 struct Tile {
     int cols = 16;   // 16 * C, C in {1, 2, 4}
-    int waves = 8;   // wavefronts per workgroup (split of K), 1..16
+    int waves = 8;   // wavefronts per workgroup (split of K), 1..8
+    int unroll = 2;  // 128-k blocks per pipeline step: 1, 2 or 4
 };
 
-// Checks a tile against a shape: cols in {16, 32, 64}; waves in 1..16 and
-// dividing K / 128 (whole 128-k blocks per wavefront).
+// Checks a tile against a shape: cols in {16, 32, 64}; waves in 1..8;
+// unroll in {1, 2, 4}; each segment K / waves a whole number of unroll * 128 k.
 bool tile_valid(const Tile& t, int64_t n, int64_t k);
 
 // The tile for (N, K): the override table if one was loaded, else the built-in
@@ -30,7 +34,7 @@ Tile tile_for(int64_t n, int64_t k);
 
 // Loads, once per process, the override table from the file named by the
 // environment variable NVFP4_TILES (if set), so the table is constant for the
-// life of the process.  Lines: "N K cols waves"; '#' starts a comment.
+// life of the process.  Lines: "N K cols waves unroll"; '#' starts a comment.
 // Returns NVFP4_OK or NVFP4_ERR_TILEFILE (the same status on every call).
 int load_tile_override();
 

@@ -188,6 +188,10 @@ def main() -> int:
     ap.add_argument("--extra-m", type=str, default="8", help="row counts timed after the steps, reported only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="also time eager launches")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches instead of graph replays (for counter collection)")
+    ap.add_argument("--copy-only", action="store_true",
+                    help="only run a 1 GiB device copy 5 times (counter calibration) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -200,6 +204,15 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_only:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read_per_dispatch": 1 << 30, "copy_bytes_written_per_dispatch": 1 << 30,
+                          "dispatches": 5}), flush=True)
+        return 0
     nv.init()
     ms_list = [int(v) for v in args.m.split(",") if v]
     extra_m = [int(v) for v in args.extra_m.split(",") if v]
@@ -233,7 +246,10 @@ def main() -> int:
             for m in ms_list:
                 s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 s.record(stream)
-                graphs[m].replay()
+                if args.no_graph:
+                    launches[m].launch_all(stream.cuda_stream)
+                else:
+                    graphs[m].replay()
                 e.record(stream)
                 events[m].append((s, e))
         torch.cuda.synchronize()
@@ -298,6 +314,7 @@ def main() -> int:
     value = total_bytes / wall / 1e9
     out = {
         "metric": "weight-stream HBM GB/s (% of peak) for NVFP4 skinny GEMM at M=1,16,32",
+        "launch": "eager" if args.no_graph else "hip-graph",
         "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",

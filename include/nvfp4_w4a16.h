@@ -21,8 +21,8 @@
  *    prefers an error to a stale output);
  *  - the launch path allocates nothing and never synchronises the device, so
  *    nvfp4_linear can be captured into a HIP graph once nvfp4_init() has run;
- *  - no atomics: a row's output bits do not depend on M or on the other rows
- *    ("10 Kernels", section 10.1).
+ *  - no read-modify-write atomics: a row's output bits do not depend on M or
+ *    on the other rows ("10 Kernels", section 10.1).
  */
 #ifndef NVFP4_W4A16_H
 #define NVFP4_W4A16_H
@@ -98,8 +98,13 @@ int nvfp4_linear_shape_ok(int64_t m, int64_t n, int64_t k);
  * Host.  Checks that the current HIP device is gfx950, loads the kernels'
  * code objects and the (N, K) tile table once per process (the table may be
  * overridden by the file named in the environment variable NVFP4_TILES, read
- * here only).  Call before capturing nvfp4_linear into a HIP graph; the first
- * nvfp4_linear call runs it otherwise.  Safe to call more than once.
+ * here only), and sets up the current device's workspace once per device: 32
+ * MiB of partial sums plus 1 MiB of flag words in uncached device memory, kept
+ * until the process ends (the many-row kernel exchanges segment-group sums
+ * through it).  Call on every device before capturing nvfp4_linear into a HIP
+ * graph; the first nvfp4_linear call on a device runs it otherwise.  Safe to
+ * call more than once.  If the workspace cannot be allocated, nvfp4_linear
+ * still works (with kernels that do not need it) and gives the same bits.
  * Errors: HIP, DEVICE, TILEFILE.
  */
 int nvfp4_init(void);
@@ -116,29 +121,59 @@ int nvfp4_init(void);
  * All buffers belong to the caller and must stay alive until the stream has
  * passed this call.  M == 0 returns NVFP4_OK and launches nothing.  Rows
  * r < M of y are written in full; nothing else is written.  The reduction over
- * K runs in an order fixed by (N, K) alone, so a row's bits are the same for
- * every M and every position of the row in x.  No allocation, no host sync.
+ * K runs in an order fixed by (N, K) alone (see nvfp4_tile_t), so a row's bits
+ * are the same for every M and every position of the row in x.  No
+ * allocation, no host sync.
+ * Shapes whose tile has split > 1 run, for M >= 2, through the device
+ * workspace set up by nvfp4_init: such calls on one device must not overlap in
+ * time (calls on one stream, or on streams ordered by events, never do).  A
+ * workgroup that waits for another's partial sums gives up after about a
+ * second and writes NaN to its outputs instead of hanging.
  * Errors: NULL, SHAPE, ALIGN, DTYPE, HIP, DEVICE, TILEFILE.
  */
 int nvfp4_linear(const void* x_bf16, const uint8_t* w_packed,
                  const uint8_t* scales_e4m3, float tensor_scale, void* y,
                  int64_t m, int64_t n, int64_t k, int y_dtype, void* stream);
 
+/* Kernel choice of nvfp4_linear_tiled (nvfp4_linear always chooses itself). */
+enum {
+    NVFP4_KERNEL_AUTO = 0,       /* as nvfp4_linear: by M, K and the workspace */
+    NVFP4_KERNEL_PERSISTENT = 1, /* x [M, K] whole in LDS; needs M * (K + 8) * 2 + partials <= 64 KB, cols <= 32 */
+    NVFP4_KERNEL_TILE = 2,       /* one workgroup per 16 * C columns, all segments; any shape */
+    NVFP4_KERNEL_SPLIT = 3       /* many-row kernel: one segment group per workgroup, x windows in LDS;
+                                    needs K / waves % 256 == 0, K / split % 512 == 0 and, for
+                                    split > 1, the device workspace */
+};
+
 /*
- * Device, asynchronous: nvfp4_linear with an explicit launch tile instead of
- * the (N, K) table's, for tile sweeps ("10 Kernels", section 10.2: the tables
- * hold the launch settings a sweep picked).  cols: output columns per
- * wavefront (16, 32 or 64); waves: wavefronts per workgroup (1..8), each
- * summing one of `waves` equal K segments, added in segment order; unroll:
- * 128-k blocks per pipeline step (1, 2 or 4), with K a multiple of
- * 128 * unroll * waves.  cols and unroll never change the result's bits;
- * waves does (it is the K segmentation).
- * Errors: those of nvfp4_linear, and TILE for a tile that does not fit.
+ * Launch tile ("10 Kernels", section 10.2: the per-shape tables hold the
+ * launch settings a sweep picked).  The K reduction of every output is: K cut
+ * into `waves` equal segments, each summed as one chain of MFMAs in increasing
+ * k; the segments cut into `split` groups of consecutive segments; a group's
+ * sum adds its chains in segment order, and the output adds the group sums in
+ * group order.  Only waves and split change result bits.
+ */
+typedef struct nvfp4_tile {
+    int cols;   /* output columns per wavefront: 16, 32 or 64 */
+    int waves;  /* K segments, 1..8 (wavefronts per workgroup of the one-group kernels) */
+    int unroll; /* 128-k blocks per pipeline step: 1, 2 or 4; K % (128 * unroll * waves) == 0 */
+    int split;  /* segment groups: 1, 2, 4 or 8, dividing waves */
+    int mwaves; /* wavefronts per workgroup of the many-row kernel: 4 or 8 */
+    int kernel; /* NVFP4_KERNEL_*; ignored by the (N, K) table */
+} nvfp4_tile_t;
+
+/*
+ * Device, asynchronous: nvfp4_linear with an explicit launch tile and kernel
+ * instead of the (N, K) table's, for tile sweeps and for tests that every
+ * kernel gives the same bits for the same waves and split.  `tile` is a host
+ * pointer read during the call only.
+ * Errors: those of nvfp4_linear, NULL for tile == NULL, and TILE for a tile
+ * that does not fit the shape or a kernel that cannot run it.
  */
 int nvfp4_linear_tiled(const void* x_bf16, const uint8_t* w_packed,
                        const uint8_t* scales_e4m3, float tensor_scale, void* y,
-                       int64_t m, int64_t n, int64_t k, int y_dtype, int cols,
-                       int waves, int unroll, void* stream);
+                       int64_t m, int64_t n, int64_t k, int y_dtype,
+                       const nvfp4_tile_t* tile, void* stream);
 
 /*
  * Host.  Writes a one-line text description of the tile nvfp4_linear uses for

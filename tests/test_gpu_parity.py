@@ -133,19 +133,31 @@ def test_bf16_output_is_rounded_fp32_output(inv_weight, inv_x):
 
 
 def test_launch_settings_never_change_bits():
-    # Only the K segmentation (waves) enters the arithmetic: every cols/unroll
-    # choice, persistent or per-tile kernel, gives the default tile's bits.
+    # Only the K segmentation (waves) and its grouping (split) enter the
+    # arithmetic: every cols/unroll/mwaves choice and every kernel that can
+    # run the shape gives the default tile's bits.
     s = workload.INVARIANCE
     w = Weight.from_f32(workload.weights_f32(s.n, s.k, 61))
-    default = nv.tile_info(s.n, s.k)
-    waves = int(default.split("waves=")[1].split()[0])
+    base = nv.table_tile(s.n, s.k)
     for m in (1, 3, 17, 32):
         x = upload_bits(workload.activations_bf16(m, s.k, 62 + m))
         ref = bits(nv.linear(x, w.wp, w.sc, w.t)).clone()
-        for cols in (16, 32, 64):
-            for unroll in (1, 2, 4):
-                if s.k % (128 * unroll * waves):
-                    continue
-                y = nv.linear(x, w.wp, w.sc, w.t, tile=(cols, waves, unroll))
-                torch.cuda.synchronize()
-                assert torch.equal(bits(y), ref), f"M={m} cols={cols} unroll={unroll}"
+        ran = set()
+        for kernel in (nv.KERNEL_PERSISTENT, nv.KERNEL_TILE, nv.KERNEL_SPLIT):
+            for cols in (16, 32, 64):
+                for unroll in (1, 2, 4):
+                    for mwaves in (4, 8):
+                        if s.k % (128 * unroll * base.waves):
+                            continue
+                        tile = base.replace(cols=cols, unroll=unroll, mwaves=mwaves, kernel=kernel)
+                        y = torch.empty((m, s.n), dtype=torch.bfloat16, device=x.device)
+                        st = nv.linear_tiled_raw(x.data_ptr(), w.wp.data_ptr(), w.sc.data_ptr(), w.t,
+                                                 y.data_ptr(), m, s.n, s.k, nv.OUT_BF16, tile,
+                                                 torch.cuda.current_stream().cuda_stream)
+                        if st == nv.ERR_TILE:
+                            continue                  # this kernel cannot run this shape
+                        assert st == nv.OK
+                        torch.cuda.synchronize()
+                        ran.add(kernel)
+                        assert torch.equal(bits(y), ref), f"M={m} {tile}"
+        assert nv.KERNEL_TILE in ran and nv.KERNEL_SPLIT in ran, (m, ran)

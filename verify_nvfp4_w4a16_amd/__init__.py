@@ -21,11 +21,29 @@ ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_NONFINITE = -1, -2, -3, -4, -5
 ERR_BADSCALE, ERR_HIP, ERR_DEVICE, ERR_TILEFILE, ERR_BUFFER = -6, -7, -8, -9, -10
 ERR_TILE = -11
 OUT_BF16, OUT_F32 = 0, 1
+KERNEL_AUTO, KERNEL_PERSISTENT, KERNEL_TILE, KERNEL_SPLIT = 0, 1, 2, 3
 MAX_M = 32
 K_MULTIPLE = 256
 
 EXPORTED = ("nvfp4_pack", "nvfp4_check_scales", "nvfp4_linear_shape_ok", "nvfp4_init",
             "nvfp4_linear", "nvfp4_linear_tiled", "nvfp4_tile_info", "nvfp4_strerror")
+
+
+class Tile(ctypes.Structure):
+    """nvfp4_tile_t: launch tile and kernel choice of nvfp4_linear_tiled."""
+    _fields_ = [("cols", ctypes.c_int), ("waves", ctypes.c_int), ("unroll", ctypes.c_int),
+                ("split", ctypes.c_int), ("mwaves", ctypes.c_int), ("kernel", ctypes.c_int)]
+
+    def __init__(self, cols=16, waves=8, unroll=2, split=1, mwaves=8, kernel=KERNEL_AUTO):
+        super().__init__(cols, waves, unroll, split, mwaves, kernel)
+
+    def replace(self, **kw) -> "Tile":
+        d = {f: getattr(self, f) for f, _ in self._fields_}
+        d.update(kw)
+        return Tile(**d)
+
+    def __repr__(self) -> str:
+        return "Tile(" + ", ".join(f"{f}={getattr(self, f)}" for f, _ in self._fields_) + ")"
 
 
 class Nvfp4Error(RuntimeError):
@@ -46,7 +64,7 @@ def _load() -> ctypes.CDLL:
     lib.nvfp4_init.argtypes = []
     lib.nvfp4_linear.argtypes = [vp, vp, vp, ctypes.c_float, vp, i64, i64, i64, ctypes.c_int, vp]
     lib.nvfp4_linear_tiled.argtypes = [vp, vp, vp, ctypes.c_float, vp, i64, i64, i64, ctypes.c_int,
-                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+                                       ctypes.POINTER(Tile), vp]
     lib.nvfp4_tile_info.argtypes = [i64, i64, ctypes.c_char_p, i64]
     lib.nvfp4_strerror.argtypes = [ctypes.c_int]
     lib.nvfp4_strerror.restype = ctypes.c_char_p
@@ -105,9 +123,15 @@ def init() -> None:
 
 
 def tile_info(n: int, k: int) -> str:
-    buf = ctypes.create_string_buffer(256)
+    buf = ctypes.create_string_buffer(512)
     _check(_lib().nvfp4_tile_info(n, k, buf, len(buf)), "nvfp4_tile_info")
     return buf.value.decode()
+
+
+def table_tile(n: int, k: int) -> Tile:
+    """The tile nvfp4_linear uses for an (N, K) weight (kernel left AUTO)."""
+    fields = dict(kv.split("=") for kv in tile_info(n, k).split())
+    return Tile(*(int(fields[f]) for f in ("cols", "waves", "unroll", "split", "mwaves")))
 
 
 def linear_raw(x_ptr: int, w_ptr: int, s_ptr: int, tensor_scale: float, y_ptr: int,
@@ -118,11 +142,11 @@ def linear_raw(x_ptr: int, w_ptr: int, s_ptr: int, tensor_scale: float, y_ptr: i
 
 
 def linear_tiled_raw(x_ptr: int, w_ptr: int, s_ptr: int, tensor_scale: float, y_ptr: int,
-                     m: int, n: int, k: int, y_dtype: int, cols: int, waves: int, unroll: int,
-                     stream: int) -> int:
+                     m: int, n: int, k: int, y_dtype: int, tile: Tile | None, stream: int) -> int:
     """nvfp4_linear_tiled on raw device addresses; returns the status."""
+    ref = ctypes.byref(tile) if tile is not None else None
     return _lib().nvfp4_linear_tiled(x_ptr, w_ptr, s_ptr, ctypes.c_float(tensor_scale), y_ptr,
-                                     m, n, k, y_dtype, cols, waves, unroll, stream)
+                                     m, n, k, y_dtype, ref, stream)
 
 
 def linear(x, w_packed, scales, tensor_scale: float, out=None, out_dtype=None, stream=None,
@@ -131,7 +155,8 @@ def linear(x, w_packed, scales, tensor_scale: float, out=None, out_dtype=None, s
 
     x: bf16 [M, K]; w_packed: uint8 [N, K/2]; scales: uint8 [N, K/16];
     out: bf16 or float32 [M, N] (allocated when None; dtype from out_dtype,
-    default bf16).  Runs on `stream` (default: torch's current stream)."""
+    default bf16).  Runs on `stream` (default: torch's current stream).  `tile`
+    (a Tile) selects nvfp4_linear_tiled with that launch tile and kernel."""
     import torch
     if x.dtype != torch.bfloat16 or w_packed.dtype != torch.uint8 or scales.dtype != torch.uint8:
         raise TypeError("x must be bfloat16; w_packed and scales uint8")
@@ -157,9 +182,9 @@ def linear(x, w_packed, scales, tensor_scale: float, out=None, out_dtype=None, s
         st = linear_raw(x.data_ptr(), w_packed.data_ptr(), scales.data_ptr(), tensor_scale,
                         out.data_ptr(), m, n, k, y_dtype, stream.cuda_stream)
     else:
-        cols, waves, unroll = tile
+        if not isinstance(tile, Tile):
+            raise TypeError("tile must be a Tile")
         st = linear_tiled_raw(x.data_ptr(), w_packed.data_ptr(), scales.data_ptr(), tensor_scale,
-                              out.data_ptr(), m, n, k, y_dtype, cols, waves, unroll,
-                              stream.cuda_stream)
+                              out.data_ptr(), m, n, k, y_dtype, tile, stream.cuda_stream)
     _check(st, "nvfp4_linear" if tile is None else "nvfp4_linear_tiled")
     return out

@@ -8,6 +8,7 @@
 #include <mutex>
 #include <sstream>
 #include <utility>
+#include <vector>
 
 #include "nvfp4_w4a16.h"
 
@@ -30,8 +31,8 @@ std::map<Key, Tile>& override_table() {
 
 // Default: one 16-column tile per wavefront; K cut into at most 8 segments
 // of whole 128-k blocks (a function of K alone); up to four blocks per
-// pipeline step.
-Tile default_tile(int64_t /*n*/, int64_t k) {
+// pipeline step; segment groups by default_split.
+Tile default_tile(int64_t n, int64_t k) {
     Tile t;
     t.cols = 16;
     int64_t blocks = k / 128;
@@ -40,16 +41,28 @@ Tile default_tile(int64_t /*n*/, int64_t k) {
     t.waves = waves;
     int64_t per = blocks / waves;
     t.unroll = per % 4 == 0 ? 4 : per % 2 == 0 ? 2 : 1;
+    t.split = default_split(n, waves);
+    t.mwaves = 8;
     return t;
 }
 
 }  // namespace
+
+int default_split(int64_t n, int waves) {
+    const int64_t groups = (n + 127) / 128;
+    int split = 1;
+    while (split < waves && groups * split < 512) split *= 2;
+    return split;
+}
 
 bool tile_valid(const Tile& t, int64_t /*n*/, int64_t k) {
     if (t.cols != 16 && t.cols != 32 && t.cols != 64) return false;
     if (t.waves < 1 || t.waves > 8) return false;
     if (t.unroll != 1 && t.unroll != 2 && t.unroll != 4) return false;
     if (k % (int64_t(128) * t.unroll * t.waves) != 0) return false;
+    if (t.split != 1 && t.split != 2 && t.split != 4 && t.split != 8) return false;
+    if (t.split > t.waves || t.waves % t.split != 0) return false;
+    if (t.mwaves != 4 && t.mwaves != 8) return false;
     return true;
 }
 
@@ -75,10 +88,26 @@ static int read_override_file() {
         auto hash = line.find('#');
         if (hash != std::string::npos) line.resize(hash);
         std::istringstream ss(line);
-        int64_t n, k;
+        // N K cols waves unroll [split [mwaves]], integers only
+        std::vector<int64_t> v;
+        std::string tok;
+        while (ss >> tok) {
+            char* endp = nullptr;
+            const long long x = std::strtoll(tok.c_str(), &endp, 10);
+            if (endp == tok.c_str() || *endp != '\0') return NVFP4_ERR_TILEFILE;
+            v.push_back(x);
+        }
+        if (v.empty()) continue;                        // blank line
+        if (v.size() < 5 || v.size() > 7) return NVFP4_ERR_TILEFILE;
+        const int64_t n = v[0], k = v[1];
+        for (size_t i = 2; i < v.size(); ++i)
+            if (v[i] < 0 || v[i] > 64) return NVFP4_ERR_TILEFILE;
         Tile t;
-        if (!(ss >> n)) continue;                       // blank line
-        if (!(ss >> k >> t.cols >> t.waves >> t.unroll)) return NVFP4_ERR_TILEFILE;
+        t.cols = static_cast<int>(v[2]);
+        t.waves = static_cast<int>(v[3]);
+        t.unroll = static_cast<int>(v[4]);
+        t.split = v.size() > 5 ? static_cast<int>(v[5]) : 1;
+        t.mwaves = v.size() > 6 ? static_cast<int>(v[6]) : 8;
         if (nvfp4_linear_shape_ok(1, n, k) != NVFP4_OK || !tile_valid(t, n, k))
             return NVFP4_ERR_TILEFILE;
         table[{n, k}] = t;
@@ -95,11 +124,12 @@ int load_tile_override() {
 }
 
 std::string tile_text(int64_t n, int64_t k, const Tile& t) {
-    char buf[256];
+    char buf[320];
     int64_t groups = (n + t.cols - 1) / t.cols;
     std::snprintf(buf, sizeof buf,
-                  "N=%lld K=%lld cols=%d waves=%d unroll=%d k_per_wave=%lld grid=%lld block=%d",
-                  (long long)n, (long long)k, t.cols, t.waves, t.unroll,
+                  "N=%lld K=%lld cols=%d waves=%d unroll=%d split=%d mwaves=%d k_per_wave=%lld "
+                  "grid=%lld block=%d",
+                  (long long)n, (long long)k, t.cols, t.waves, t.unroll, t.split, t.mwaves,
                   (long long)(k / t.waves), (long long)groups, 64 * t.waves);
     return buf;
 }

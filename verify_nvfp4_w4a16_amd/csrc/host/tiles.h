@@ -8,10 +8,15 @@
 //   waves - wavefronts of one workgroup, each taking an equal, contiguous
 //           share (slice) of K; their partial sums are added in slice order;
 //   unroll - 128-k blocks a wavefront loads per step of its software
-//           pipeline (1, 2 or 4).
-// Only `waves` enters the arithmetic of an output (how K is sliced); `cols`
-// and `unroll` change the launch, never the bits.  The tile is a function of
-// (N, K) only.
+//           pipeline (1, 2 or 4);
+//   split  - groups of consecutive segments (1, 2, 4 or 8, dividing waves):
+//           an output is the sum, in group order, of its group sums, each
+//           the sum of the group's segment chains in segment order;
+//   mwaves - wavefronts per workgroup of the many-row kernel (4 or 8), which
+//           runs one segment group per workgroup.
+// Only `waves` and `split` enter the arithmetic of an output (how K is cut
+// and in which order the pieces are added); `cols`, `unroll` and `mwaves`
+// change the launch, never the bits.  The tile is a function of (N, K) only.
 #pragma once
 #include <cstdint>
 #include <string>
@@ -20,13 +25,21 @@ namespace nvfp4 {
 
 struct Tile {
     int cols = 16;   // 16 * C, C in {1, 2, 4}
-    int waves = 8;   // wavefronts per workgroup (split of K), 1..8
+    int waves = 8;   // K segments (wavefronts per workgroup of the one-group kernels), 1..8
     int unroll = 2;  // 128-k blocks per pipeline step: 1, 2 or 4
+    int split = 1;   // segment groups: 1, 2, 4 or 8, dividing waves
+    int mwaves = 8;  // wavefronts per workgroup of the many-row kernel: 4 or 8
 };
 
 // Checks a tile against a shape: cols in {16, 32, 64}; waves in 1..8;
-// unroll in {1, 2, 4}; each segment K / waves a whole number of unroll * 128 k.
+// unroll in {1, 2, 4}; each segment K / waves a whole number of unroll * 128 k;
+// split in {1, 2, 4, 8} dividing waves; mwaves in {4, 8}.
 bool tile_valid(const Tile& t, int64_t n, int64_t k);
+
+// Segment groups the default rule picks for N output columns: enough
+// workgroups of 128 columns x one group each to give every one of 256 CUs
+// two of them, at most `waves` groups.
+int default_split(int64_t n, int waves);
 
 // The tile for (N, K): the override table if one was loaded, else the built-in
 // table, else the default rule.  Never depends on M.
@@ -34,7 +47,8 @@ Tile tile_for(int64_t n, int64_t k);
 
 // Loads, once per process, the override table from the file named by the
 // environment variable NVFP4_TILES (if set), so the table is constant for the
-// life of the process.  Lines: "N K cols waves unroll"; '#' starts a comment.
+// life of the process.  Lines: "N K cols waves unroll [split [mwaves]]"; '#'
+// starts a comment; a missing split is 1 and a missing mwaves 8.
 // Returns NVFP4_OK or NVFP4_ERR_TILEFILE (the same status on every call).
 int load_tile_override();
 

@@ -34,6 +34,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <atomic>
 #include <mutex>
 #include <string>
 
@@ -59,8 +60,26 @@ struct Args {
     void* y;               // [M, N] bf16 or fp32
     float t;
     int m, n, k;
-    int k_per_wave;
+    int k_per_wave;        // segment length
+    int group;             // segments per segment group
 };
+
+// Folds segment sum `v` of segment `w` (w >= 1) into the running sums of the
+// two-level order: `grp` is the sum of the current group so far, `tot` the
+// sum of the finished groups (valid once w >= group).
+__device__ __forceinline__ void fold_segment(f32x4& grp, f32x4& tot, f32x4 v, int w, int group) {
+    // branch-free (selects), so the caller's control flow stays simple
+    const bool starts = w % group == 0;
+    const f32x4 closed = w == group ? grp : tot + grp;
+    tot = starts ? closed : tot;
+    grp = starts ? v : grp + v;
+}
+
+// Keeps the machine scheduler from moving instructions across this point.
+// Placed after the loads of the next pipeline chunk, it makes them go out
+// before the waits for the current chunk, so two chunks are in flight while
+// one waits (left alone, the scheduler sinks those loads below the waits).
+__device__ __forceinline__ void issue_point() { __builtin_amdgcn_sched_barrier(0); }
 
 __device__ __forceinline__ u32x4 load16(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
@@ -124,12 +143,15 @@ __device__ __forceinline__ int lds_pitch(int k) { return k + 8; }
 //
 // One workgroup owns 16*C output columns; its `waves` wavefronts cut K into
 // `waves` equal segments.  Wavefront w sums segment w as one chain of MFMAs in
-// increasing k, and the segment sums are added in segment order.  C and U
-// change neither the chains nor the final sum: only the segment count enters
-// the arithmetic, and it is fixed by the (N, K) tile.
+// increasing k, and the segment sums are added in the two-level order of the
+// tile (consecutive segments form `waves / group` groups; each group's chains
+// are added in segment order, then the group sums in group order).  C and U
+// change neither the chains nor the final sum: only the segment count and
+// grouping enter the arithmetic, and both are fixed by the (N, K) tile.
 //
-// XLDS: x [M, K] is first copied into LDS (rows >= M are never read: their A
-// operand is zero), so the weight pipeline holds only weights in registers.
+// XLDS: x [M, K] is first copied into LDS (A rows >= M repeat row M-1; their
+// outputs are never stored), so the weight pipeline holds only weights in
+// registers.
 // Otherwise (x too large for LDS) each chunk also fetches its A operands.
 template <int C, int MT, int U, bool XLDS, bool OUT_F32>
 __global__ void __launch_bounds__(512)
@@ -262,15 +284,18 @@ nvfp4_skinny(Args a) {
     int i = 0;
     for (; i + 2 <= nchunks; i += 2) {
         load(B, k0 + (i + 1) * kBlockK * U);
+        issue_point();
         compute(A, k0 + i * kBlockK * U);
         if (i + 2 < nchunks) load(A, k0 + (i + 2) * kBlockK * U);
+        issue_point();
         compute(B, k0 + (i + 1) * kBlockK * U);
     }
     if (i < nchunks) compute(A, k0 + i * kBlockK * U);
 
-    // Segment partials, added in segment order: wavefront 0 keeps its own sum
-    // in registers and adds those of wavefronts 1, 2, ... in turn.  The LDS
-    // that held x is reused once every wavefront is done with it.
+    // Segment sums, added in the two-level order: wavefront 0 keeps its own
+    // sum in registers and folds in those of wavefronts 1, 2, ... in turn
+    // (group sums in segment order, then the group sums in group order).  The
+    // LDS that held x is reused once every wavefront is done with it.
     if (waves > 1) {
         float* partials = reinterpret_cast<float*>(lds);
         __syncthreads();
@@ -285,14 +310,22 @@ nvfp4_skinny(Args a) {
         }
         __syncthreads();
         if (wave != 0) return;
+        f32x4 tot[C][MT] = {};
         for (int w2 = 1; w2 < waves; ++w2) {
 #pragma unroll
             for (int c = 0; c < C; ++c)
 #pragma unroll
                 for (int t = 0; t < MT; ++t)
+                {
+                    const float* p = partials + ((w2 * C + c) * MT + t) * 4 * kWave + lane;
+                    fold_segment(acc[c][t], tot[c][t], f32x4{p[0], p[kWave], p[2 * kWave], p[3 * kWave]}, w2, a.group);
+                }
+        }
+        if (a.group < waves) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[c][t][j] += partials[((w2 * C + c) * MT + t) * 4 * kWave + j * kWave + lane];
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+                for (int t = 0; t < MT; ++t) acc[c][t] = tot[c][t] + acc[c][t];
         }
     }
 #pragma unroll
@@ -427,8 +460,8 @@ nvfp4_skinny_persistent(Args a) {
     };
 
     // After the last chunk of a tile: segment partials through LDS (two
-    // buffers, so one barrier per tile), wavefront 0 adds them in segment
-    // order, scales, rounds and stores.
+    // buffers, so one barrier per tile), wavefront 0 adds them in the
+    // two-level order, scales, rounds and stores.
     int parity = 0;
     auto finish_tile = [&](int j) {
         const int tile = (int)blockIdx.x + (j / nch) * (int)gridDim.x;
@@ -447,14 +480,23 @@ nvfp4_skinny_persistent(Args a) {
             __syncthreads();
         }
         if (wave == 0) {
+            f32x4 tot[C][MT] = {};
             for (int w2 = 1; w2 < waves; ++w2) {
 #pragma unroll
                 for (int c = 0; c < C; ++c)
 #pragma unroll
                     for (int t = 0; t < MT; ++t)
+                    {
+                        const float* p = buf + ((w2 * C + c) * MT + t) * 4 * kWave + lane;
+                        fold_segment(acc[c][t], tot[c][t], f32x4{p[0], p[kWave], p[2 * kWave], p[3 * kWave]}, w2,
+                                     a.group);
+                    }
+            }
+            if (a.group < waves) {
 #pragma unroll
-                        for (int jj = 0; jj < 4; ++jj)
-                            acc[c][t][jj] += buf[((w2 * C + c) * MT + t) * 4 * kWave + jj * kWave + lane];
+                for (int c = 0; c < C; ++c)
+#pragma unroll
+                    for (int t = 0; t < MT; ++t) acc[c][t] = tot[c][t] + acc[c][t];
             }
 #pragma unroll
             for (int c = 0; c < C; ++c) {
@@ -480,20 +522,284 @@ nvfp4_skinny_persistent(Args a) {
             for (int t = 0; t < MT; ++t) acc[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     };
 
-    // One pipeline over all (tile, chunk) of this wavefront; the loads past
-    // the end repeat the last chunk (never computed), keeping them unconditional.
-    for (int j = 0; j < total; j += 2) {
-        load(B, min(j + 1, total - 1));
+    // One pipeline over all (tile, chunk) of this wavefront; a load past the
+    // end repeats the last chunk (never computed), keeping loads
+    // unconditional.  The loop has a single exit at the bottom: an exit
+    // between the two halves would give the header a path on which chunk B
+    // is still in flight, and the compiler would then drain every load there.
+    int j = 0;
+    for (; j + 1 < total; j += 2) {
+        load(B, j + 1);
+        issue_point();
         compute(A, j);
         if (j % nch == nch - 1) finish_tile(j);
-        if (j + 1 >= total) break;
         load(A, min(j + 2, total - 1));
+        issue_point();
         compute(B, j + 1);
         if ((j + 1) % nch == nch - 1) finish_tile(j + 1);
+    }
+    if (j < total) {
+        compute(A, j);
+        if (j % nch == nch - 1) finish_tile(j);
+    }
+}
+
+// Many-row kernel (x too large to sit whole in one workgroup's LDS).  A
+// workgroup owns 16*C*W output columns (W wavefronts with C column tiles
+// each) and one segment group: K range [part * K/split, (part+1) * K/split),
+// i.e. `group` consecutive segments.  x comes into LDS in windows of 512 k
+// (two pipeline chunks), double-buffered, and every window is read by all W
+// wavefronts, so x is fetched once per 16*C*W columns instead of once per
+// 16*C.  A wavefront runs the chains of the group's segments one after the
+// other and keeps the group sum (chains added in segment order).
+//
+// With split == 1 that sum is the output.  Otherwise the column group's
+// `split` workgroups are blockIdx = part * groups + column_group: those of
+// parts 0..split-2 store their group sums in `work` (uncached device memory,
+// so a store that has completed is visible to every CU) and then write the
+// call's epoch (a nonzero number that differs between consecutive calls) to
+// their flag word; the workgroup of the last part waits for the flags to hold
+// the epoch (bounded: past the limit it writes NaN instead of hanging), adds
+// the group sums in group order with its own last, stores y and clears the
+// flags, so a replayed graph (same epoch) starts from clear flags too.  A flag
+// left behind by a call that timed out holds an old epoch and is ignored.
+// Workgroups are dispatched in index order, so each part's producers are
+// resident or done before its consumer waits, and producers never wait.  No
+// read-modify-write atomics are used.
+struct SplitArgs {
+    Args a;               // a.k_per_wave: segment length; a.group: segments per group
+    float* work;          // [groups][split-1][W][C][MT][4][64] fp32 group sums
+    uint32_t* flags;      // [groups][split]: `epoch` once a group sum is in `work`
+    uint32_t epoch;
+    int split;
+    int groups;           // column groups of 16*C*W
+};
+
+constexpr uint32_t kSpinLimit = 1u << 20;   // polls of a flag before giving up (~1 s)
+
+template <int C, int MT, int W, bool OUT_F32>
+__global__ void __launch_bounds__(64 * W)
+nvfp4_skinny_split(SplitArgs sa) {
+    constexpr int U = 2;
+    constexpr int kChunk = kBlockK * U;                 // k per pipeline chunk
+    constexpr int kWin = 2 * kChunk;                    // k per x window
+    constexpr int kPitch = kWin + 8;                    // LDS row pitch (bf16 elements)
+    constexpr int kVecRow = kWin / 8;                   // 16-byte vectors per window row
+    constexpr int kThreads = 64 * W;
+    constexpr int kStage = (16 * MT * kVecRow + kThreads - 1) / kThreads;
+    extern __shared__ __align__(16) uint16_t lds[];    // two windows [M][kPitch]
+    const Args& a = sa.a;
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    const int col_lane = lane % 16;
+    const int kq = lane / 16;
+    const int cgroup = (int)blockIdx.x % sa.groups;
+    const int part = (int)blockIdx.x / sa.groups;
+    const int krange = a.k / sa.split;
+    const int kbase = part * krange;
+    const int nwin = krange / kWin;
+    const int seg_chunks = a.k_per_wave / kChunk;
+    const int slice = a.m * kPitch;
+    const int col_base = (cgroup * W + wave) * 16 * C;
+    const uint32_t row_bytes = static_cast<uint32_t>(a.k) / 2;
+    const uint32_t scale_bytes = static_cast<uint32_t>(a.k) / 16;
+
+    const uint8_t* wrow[C];
+    const uint8_t* srow[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const uint32_t n = static_cast<uint32_t>(min(col_base + 16 * c + col_lane, a.n - 1));
+        wrow[c] = a.wp + static_cast<uint64_t>(n) * row_bytes + kbase / 2 + 16 * kq;
+        srow[c] = a.sc + static_cast<uint64_t>(n) * scale_bytes + kbase / 16;
+    }
+    int xr[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) xr[t] = min(16 * t + col_lane, a.m - 1);
+
+    // chunk i of the range: k = kbase + i * kChunk
+    auto load = [&](Chunk<C, MT, U, true>& ch, int i) {
+        const uint32_t kb = static_cast<uint32_t>(i * kChunk);
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                ch.w[c][u] = load16_stream(wrow[c] + (kb + kBlockK * u) / 2);
+                ch.s[c][u] = load8_stream(srow[c] + (kb + kBlockK * u) / 16);
+            }
+    };
+    // x window `win` of the range: loads into registers, then stores to LDS.
+    // Indices past the last row are clamped (a repeated store of one value).
+    const int xtotal = a.m * kVecRow;
+    u32x4 xs[kStage];
+    auto stage_issue = [&](int win) {
+        const uint16_t* src = a.x + kbase + win * kWin;
+#pragma unroll
+        for (int r = 0; r < kStage; ++r) {
+            const int v = min(r * kThreads + (int)threadIdx.x, xtotal - 1);
+            xs[r] = load16(src + (int64_t)(v / kVecRow) * a.k + (v % kVecRow) * 8);
+        }
+    };
+    auto stage_commit = [&](int buf) {
+#pragma unroll
+        for (int r = 0; r < kStage; ++r) {
+            const int v = min(r * kThreads + (int)threadIdx.x, xtotal - 1);
+            *reinterpret_cast<u32x4*>(lds + buf * slice + (v / kVecRow) * kPitch + (v % kVecRow) * 8) = xs[r];
+        }
+    };
+
+    f32x4 acc[C][MT], grp[C][MT];
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[c][t] = grp[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // chunk i (its window's buffer `buf`, half i % 2 of the window)
+    auto compute = [&](const Chunk<C, MT, U, true>& ch, int i, int buf) {
+        const uint16_t* xb = lds + buf * slice + (i % 2) * kChunk;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            u32x4 xa[MT][4];
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    xa[t][s] = *reinterpret_cast<const u32x4*>(xb + xr[t] * kPitch + kBlockK * u + 32 * kq + 8 * s);
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                const uint32_t d = static_cast<uint32_t>(ch.s[c][u] >> (16 * kq));
+                const float g0 = __builtin_amdgcn_cvt_f32_fp8(d, 0);
+                const float g1 = __builtin_amdgcn_cvt_f32_fp8(d, 1);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    bf16x8 b = decode8(ch.w[c][u][s], s < 2 ? g0 : g1);
+#pragma unroll
+                    for (int t = 0; t < MT; ++t)
+                        acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[t][s]), b,
+                                                                           acc[c][t], 0, 0, 0);
+                }
+            }
+        }
+        // end of a segment: its chain joins the group sum (the first chain
+        // is taken as it is, so a -0 sum keeps its sign)
+        if ((i + 1) % seg_chunks == 0) {
+            const bool first = i + 1 == seg_chunks;
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+                for (int t = 0; t < MT; ++t) {
+                    grp[c][t] = first ? acc[c][t] : grp[c][t] + acc[c][t];
+                    acc[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+        }
+    };
+
+    // Pipeline: while chunk i is multiplied, chunk i + 1 is in flight; the
+    // next window's x loads go out right after the weights of the window's
+    // second chunk and are stored to the other buffer after both chunks.
+    Chunk<C, MT, U, true> A, B;
+    stage_issue(0);
+    load(A, 0);
+    stage_commit(0);
+    __syncthreads();
+    int win = 0;
+    for (; win + 1 < nwin; ++win) {
+        const int buf = win & 1;
+        load(B, 2 * win + 1);
+        stage_issue(win + 1);
+        issue_point();
+        compute(A, 2 * win, buf);
+        load(A, 2 * win + 2);
+        issue_point();
+        compute(B, 2 * win + 1, buf);
+        stage_commit(buf ^ 1);
+        __syncthreads();
+    }
+    load(B, 2 * win + 1);
+    issue_point();
+    compute(A, 2 * win, win & 1);
+    compute(B, 2 * win + 1, win & 1);
+
+    if (sa.split > 1) {
+        constexpr int kSlot = W * C * MT * 4 * kWave;   // floats of one workgroup's group sums
+        const int P = sa.split;
+        float* work = sa.work + (size_t)cgroup * (P - 1) * kSlot;
+        uint32_t* flags = sa.flags + (size_t)cgroup * P;
+        const int base = wave * C * MT * 4 * kWave + lane;
+        if (part < P - 1) {
+            float* slot = work + (size_t)part * kSlot + base;
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) slot[((c * MT + t) * 4 + j) * kWave] = grp[c][t][j];
+            // every store of the workgroup has completed before the flag is set
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (threadIdx.x == 0) __hip_atomic_store(flags + part, sa.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        __shared__ uint32_t timed_out;
+        if (threadIdx.x == 0) timed_out = 0;
+        __syncthreads();
+        if ((int)threadIdx.x < P - 1) {
+            uint32_t spins = 0;
+            while (__hip_atomic_load(flags + threadIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != sa.epoch) {
+                if (++spins >= kSpinLimit) {
+                    timed_out = 1;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(8);
+            }
+        }
+        __syncthreads();
+        f32x4 tot[C][MT] = {};
+        for (int q = 0; q < P - 1; ++q) {
+            const float* slot = work + (size_t)q * kSlot + base;
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float v = __hip_atomic_load(slot + ((c * MT + t) * 4 + j) * kWave,
+                                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        tot[c][t][j] = q == 0 ? v : tot[c][t][j] + v;
+                    }
+        }
+        const bool bad = timed_out != 0;
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    grp[c][t][j] = bad ? __builtin_nanf("") : tot[c][t][j] + grp[c][t][j];
+        if ((int)threadIdx.x < P - 1)
+            __hip_atomic_store(flags + threadIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int n = col_base + 16 * c + col_lane;
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int m = 16 * t + 4 * kq + j;
+                if (m < a.m && n < a.n) {
+                    float r = grp[c][t][j] * a.t;
+                    if (OUT_F32)
+                        static_cast<float*>(a.y)[(int64_t)m * a.n + n] = r;
+                    else
+                        static_cast<uint16_t*>(a.y)[(int64_t)m * a.n + n] = f32_to_bf16_rne(r);
+                }
+            }
     }
 }
 
 using KernelFn = void (*)(Args);
+using SplitFn = void (*)(SplitArgs);
 
 template <int C, int MT, int U>
 KernelFn pick_out(bool xlds, int y_dtype) {
@@ -544,64 +850,104 @@ KernelFn pick_persistent(int mt, int cols, int unroll, int y_dtype) {
     return cols == 16 ? pick_p_u<1, 2>(unroll, y_dtype) : pick_p_u<2, 2>(unroll, y_dtype);
 }
 
-// Multiprocessor count per device, filled by nvfp4_init.
+template <int C, int MT, int W>
+SplitFn pick_s_out(int y_dtype) {
+    return y_dtype == NVFP4_OUT_F32 ? nvfp4_skinny_split<C, MT, W, true> : nvfp4_skinny_split<C, MT, W, false>;
+}
+
+template <int MT>
+SplitFn pick_s_w(int c, int w, int y_dtype) {
+    if (c == 1) return w == 4 ? pick_s_out<1, MT, 4>(y_dtype) : pick_s_out<1, MT, 8>(y_dtype);
+    return w == 4 ? pick_s_out<2, MT, 4>(y_dtype) : pick_s_out<2, MT, 8>(y_dtype);
+}
+
+// c: column tiles per wavefront (1 or 2), w: wavefronts per workgroup (4 or 8)
+SplitFn pick_split(int mt, int c, int w, int y_dtype) {
+    return mt == 1 ? pick_s_w<1>(c, w, y_dtype) : pick_s_w<2>(c, w, y_dtype);
+}
+
+// Per-device state, set up once per device by nvfp4_init (or the first call
+// on that device).
 constexpr int kMaxDevices = 64;
-int g_cu_count[kMaxDevices] = {};
+constexpr size_t kWorkBytes = size_t(32) << 20;      // group sums of the many-row kernel
+constexpr size_t kFlagWords = size_t(1) << 18;       // 1 MiB of flag words
+struct DeviceState {
+    std::once_flag once;
+    int status = NVFP4_OK;
+    int cus = 0;
+    float* work = nullptr;          // uncached, never freed
+    uint32_t* flags = nullptr;      // uncached, zero between calls, never freed
+    std::atomic<uint32_t> epoch{0};
+};
+DeviceState g_dev[kMaxDevices];
+
+template <typename Fn>
+bool allow_full_lds(Fn fn) {
+    const void* f = reinterpret_cast<const void*>(fn);
+    hipFuncAttributes attr;
+    if (hipFuncGetAttributes(&attr, f) != hipSuccess) return false;
+    // the static LDS of the kernel counts against the same 160 KB
+    const int dyn = kMaxLdsBytes - static_cast<int>(attr.sharedSizeBytes);
+    return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) == hipSuccess;
+}
+
+int init_device(int dev) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return NVFP4_ERR_HIP;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return NVFP4_ERR_DEVICE;
+    DeviceState& d = g_dev[dev];
+    d.cus = prop.multiProcessorCount;
+    // Touch every kernel so its code object is loaded before any graph
+    // capture, and let each use the whole LDS.
+    const int cols[3] = {16, 32, 64};
+    for (int mt = 1; mt <= 2; ++mt)
+        for (int od = 0; od <= 1; ++od) {
+            for (int ci = 0; ci < 3; ++ci)
+                for (int un = 1; un <= 4; un *= 2)
+                    for (int xl = 0; xl <= 1; ++xl)
+                        if (!allow_full_lds(pick_kernel(mt, cols[ci], un, xl != 0, od))) return NVFP4_ERR_HIP;
+            for (int cc = 16; cc <= 32; cc += 16)
+                for (int un = 1; un <= 4; un *= 2)
+                    if (!allow_full_lds(pick_persistent(mt, cc, un, od))) return NVFP4_ERR_HIP;
+            for (int c = 1; c <= 2; ++c)
+                for (int w = 4; w <= 8; w += 4)
+                    if (!allow_full_lds(pick_split(mt, c, w, od))) return NVFP4_ERR_HIP;
+        }
+    // Workspace of the many-row kernel.  Without it that kernel runs only
+    // where the tile has split == 1 (the other kernels give the same bits).
+    void* work = nullptr;
+    void* flags = nullptr;
+    if (hipExtMallocWithFlags(&work, kWorkBytes, hipDeviceMallocUncached) == hipSuccess &&
+        hipExtMallocWithFlags(&flags, kFlagWords * sizeof(uint32_t), hipDeviceMallocUncached) == hipSuccess &&
+        hipMemset(flags, 0, kFlagWords * sizeof(uint32_t)) == hipSuccess && hipDeviceSynchronize() == hipSuccess) {
+        d.work = static_cast<float*>(work);
+        d.flags = static_cast<uint32_t*>(flags);
+    } else {
+        (void)hipGetLastError();   // clear the failure; the memory (if any) stays unused
+    }
+    return NVFP4_OK;
+}
 
 std::once_flag g_init_once;
 int g_init_status = NVFP4_OK;
 
-void do_init() {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) { g_init_status = NVFP4_ERR_HIP; return; }
-    hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) { g_init_status = NVFP4_ERR_HIP; return; }
-    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) { g_init_status = NVFP4_ERR_DEVICE; return; }
-    int st = nvfp4::load_tile_override();
-    if (st != NVFP4_OK) { g_init_status = st; return; }
-    int ndev = 0;
-    if (hipGetDeviceCount(&ndev) != hipSuccess) { g_init_status = NVFP4_ERR_HIP; return; }
-    for (int d = 0; d < ndev && d < kMaxDevices; ++d) {
-        hipDeviceProp_t p;
-        if (hipGetDeviceProperties(&p, d) != hipSuccess) { g_init_status = NVFP4_ERR_HIP; return; }
-        g_cu_count[d] = p.multiProcessorCount;
-    }
-    // Touch every kernel so its code object is loaded before any graph capture.
-    const int cols[3] = {16, 32, 64};
-    for (int mt = 1; mt <= 2; ++mt)
-        for (int ci = 0; ci < 3; ++ci)
-            for (int un = 1; un <= 4; un *= 2)
-                for (int xl = 0; xl <= 1; ++xl)
-                for (int od = 0; od <= 1; ++od) {
-                    const void* fn = reinterpret_cast<const void*>(pick_kernel(mt, cols[ci], un, xl != 0, od));
-                    hipFuncAttributes attr;
-                    if (hipFuncGetAttributes(&attr, fn) != hipSuccess ||
-                        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                            kMaxLdsBytes) != hipSuccess) {
-                        g_init_status = NVFP4_ERR_HIP;
-                        return;
-                    }
-                }
-    for (int mt = 1; mt <= 2; ++mt)
-        for (int cc = 16; cc <= 32; cc += 16)
-            for (int un = 1; un <= 4; un *= 2)
-                for (int od = 0; od <= 1; ++od) {
-                    const void* fn = reinterpret_cast<const void*>(pick_persistent(mt, cc, un, od));
-                    hipFuncAttributes attr;
-                    if (hipFuncGetAttributes(&attr, fn) != hipSuccess ||
-                        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                            kMaxLdsBytes) != hipSuccess) {
-                        g_init_status = NVFP4_ERR_HIP;
-                        return;
-                    }
-                }
+int current_device(int* dev) {
+    if (hipGetDevice(dev) != hipSuccess) return NVFP4_ERR_HIP;
+    if (*dev < 0 || *dev >= kMaxDevices) return NVFP4_ERR_DEVICE;
+    return NVFP4_OK;
 }
 
 }  // namespace
 
 extern "C" int nvfp4_init(void) {
-    std::call_once(g_init_once, do_init);
-    return g_init_status;
+    std::call_once(g_init_once, [] { g_init_status = nvfp4::load_tile_override(); });
+    if (g_init_status != NVFP4_OK) return g_init_status;
+    int dev = 0;
+    int st = current_device(&dev);
+    if (st != NVFP4_OK) return st;
+    DeviceState& d = g_dev[dev];
+    std::call_once(d.once, [&] { d.status = init_device(dev); });
+    return d.status;
 }
 
 extern "C" int nvfp4_tile_info(int64_t n, int64_t k, char* buf, int64_t buflen) {
@@ -616,8 +962,34 @@ extern "C" int nvfp4_tile_info(int64_t n, int64_t k, char* buf, int64_t buflen) 
 
 namespace {
 
+// Launch plan of the many-row kernel; false if it cannot run this call.
+struct SplitPlan {
+    int c = 1, w = 8;
+    int64_t groups = 0;
+    size_t lds = 0;
+};
+
+bool plan_split(const nvfp4::Tile& tile, int64_t m, int64_t n, int64_t k, const DeviceState& d, SplitPlan* p) {
+    const int64_t seg = k / tile.waves;
+    if (seg % 256 != 0 || (k / tile.split) % 512 != 0) return false;
+    p->c = tile.cols == 16 ? 1 : 2;
+    p->w = tile.mwaves;
+    const int64_t cols = int64_t(16) * p->c * p->w;
+    p->groups = (n + cols - 1) / cols;
+    p->lds = 2 * size_t(m) * (512 + 8) * sizeof(uint16_t);
+    if (tile.split > 1) {
+        const int mt = m <= 16 ? 1 : 2;
+        const size_t slot = size_t(p->w) * p->c * mt * 4 * kWave * sizeof(float);
+        if (!d.work || !d.flags) return false;
+        if (size_t(p->groups) * (tile.split - 1) * slot > kWorkBytes) return false;
+        if (size_t(p->groups) * tile.split > kFlagWords) return false;
+    }
+    return p->groups * tile.split <= int64_t(0x7fffffff);
+}
+
 int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4m3, float tensor_scale,
-           void* y, int64_t m, int64_t n, int64_t k, int y_dtype, void* stream, const nvfp4::Tile& tile) {
+           void* y, int64_t m, int64_t n, int64_t k, int y_dtype, void* stream, const nvfp4::Tile& tile,
+           int kernel) {
     int st = nvfp4_linear_shape_ok(m, n, k);
     if (st != NVFP4_OK) return st;
     if (y_dtype != NVFP4_OUT_BF16 && y_dtype != NVFP4_OUT_F32) return NVFP4_ERR_DTYPE;
@@ -629,6 +1001,10 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
         return NVFP4_ERR_ALIGN;
     st = nvfp4_init();
     if (st != NVFP4_OK) return st;
+    int dev = 0;
+    st = current_device(&dev);
+    if (st != NVFP4_OK) return st;
+    const DeviceState& d = g_dev[dev];
 
     const int mt = m <= 16 ? 1 : 2;
     Args a;
@@ -641,36 +1017,58 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
     a.n = static_cast<int>(n);
     a.k = static_cast<int>(k);
     a.k_per_wave = static_cast<int>(k / tile.waves);
+    a.group = tile.waves / tile.split;
     const int c = tile.cols / 16;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+
     // x [M, K] small enough to share the LDS of one workgroup with two
     // buffers of segment partials, in at most 64 KB so a CU holds two such
     // workgroups: the persistent kernel.
     const size_t x_bytes = size_t(m) * (k + 8) * sizeof(uint16_t);
     const size_t pers_bytes = x_bytes + 2 * size_t(tile.waves) * c * mt * 4 * kWave * sizeof(float);
-    if (tile.cols <= 32 && pers_bytes <= size_t(64 * 1024)) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess) return NVFP4_ERR_HIP;
-        const int cus = dev < kMaxDevices && g_cu_count[dev] > 0 ? g_cu_count[dev] : 256;
+    const bool pers_ok = tile.cols <= 32 && pers_bytes <= size_t(64 * 1024);
+    SplitPlan plan;
+    const bool split_ok = plan_split(tile, m, n, k, d, &plan);
+    if (kernel == NVFP4_KERNEL_AUTO)
+        kernel = pers_ok ? NVFP4_KERNEL_PERSISTENT : split_ok ? NVFP4_KERNEL_SPLIT : NVFP4_KERNEL_TILE;
+    if ((kernel == NVFP4_KERNEL_PERSISTENT && !pers_ok) || (kernel == NVFP4_KERNEL_SPLIT && !split_ok))
+        return NVFP4_ERR_TILE;
+
+    if (kernel == NVFP4_KERNEL_PERSISTENT) {
+        const int cus = d.cus > 0 ? d.cus : 256;
         const int64_t tiles = (n + tile.cols - 1) / tile.cols;
         const int per_cu = tile.waves >= 8 ? 2 : 4;
         const int64_t grid_p = tiles < int64_t(per_cu) * cus ? tiles : int64_t(per_cu) * cus;
         hipLaunchKernelGGL(pick_persistent(mt, tile.cols, tile.unroll, y_dtype),
                            dim3(static_cast<unsigned>(grid_p)), dim3(static_cast<unsigned>(kWave * tile.waves)),
-                           pers_bytes, static_cast<hipStream_t>(stream), a);
-        if (hipGetLastError() != hipSuccess) return NVFP4_ERR_HIP;
-        return NVFP4_OK;
+                           pers_bytes, hs, a);
+    } else if (kernel == NVFP4_KERNEL_SPLIT) {
+        SplitArgs sa;
+        sa.a = a;
+        sa.work = d.work;
+        sa.flags = d.flags;
+        sa.split = tile.split;
+        sa.groups = static_cast<int>(plan.groups);
+        DeviceState& dm = g_dev[dev];
+        uint32_t e = dm.epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+        if (e == 0) e = dm.epoch.fetch_add(1, std::memory_order_relaxed) + 1;   // 0 means clear
+        sa.epoch = e;
+        hipLaunchKernelGGL(pick_split(mt, plan.c, plan.w, y_dtype),
+                           dim3(static_cast<unsigned>(plan.groups * tile.split)),
+                           dim3(static_cast<unsigned>(kWave * plan.w)), plan.lds, hs, sa);
+    } else {
+        // The per-tile kernel; x goes through LDS when it fits in 64 KB.
+        // With x fetched per chunk, one 128-k block per step keeps the A
+        // operands of two row tiles in registers (the pipeline depth never
+        // changes bits).
+        const bool xlds = x_bytes <= size_t(64 * 1024);
+        const size_t part_bytes = tile.waves > 1 ? size_t(tile.waves) * c * mt * 4 * kWave * sizeof(float) : 0;
+        const size_t lds = xlds && x_bytes > part_bytes ? x_bytes : part_bytes;
+        const dim3 grid(static_cast<unsigned>((n + tile.cols - 1) / tile.cols));
+        const dim3 block(static_cast<unsigned>(kWave * tile.waves));
+        const int unroll = xlds ? tile.unroll : 1;
+        hipLaunchKernelGGL(pick_kernel(mt, tile.cols, unroll, xlds, y_dtype), grid, block, lds, hs, a);
     }
-    // Otherwise the per-tile kernel; x goes through LDS when it fits in 64 KB.
-    // With x fetched per chunk, one 128-k block per step keeps the A operands
-    // of two row tiles in registers (the pipeline depth never changes bits).
-    const bool xlds = x_bytes <= size_t(64 * 1024);
-    const size_t part_bytes = tile.waves > 1 ? size_t(tile.waves) * c * mt * 4 * kWave * sizeof(float) : 0;
-    const size_t lds = xlds && x_bytes > part_bytes ? x_bytes : part_bytes;
-    const dim3 grid(static_cast<unsigned>((n + tile.cols - 1) / tile.cols));
-    const dim3 block(static_cast<unsigned>(kWave * tile.waves));
-    const int unroll = xlds ? tile.unroll : 1;
-    hipLaunchKernelGGL(pick_kernel(mt, tile.cols, unroll, xlds, y_dtype), grid, block, lds,
-                       static_cast<hipStream_t>(stream), a);
     if (hipGetLastError() != hipSuccess) return NVFP4_ERR_HIP;
     return NVFP4_OK;
 }
@@ -684,18 +1082,22 @@ extern "C" int nvfp4_linear(const void* x_bf16, const uint8_t* w_packed, const u
     if (st != NVFP4_OK) return st;
     if (nvfp4::load_tile_override() != NVFP4_OK) return NVFP4_ERR_TILEFILE;
     return launch(x_bf16, w_packed, scales_e4m3, tensor_scale, y, m, n, k, y_dtype, stream,
-                  nvfp4::tile_for(n, k));
+                  nvfp4::tile_for(n, k), NVFP4_KERNEL_AUTO);
 }
 
 extern "C" int nvfp4_linear_tiled(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4m3,
                                   float tensor_scale, void* y, int64_t m, int64_t n, int64_t k, int y_dtype,
-                                  int cols, int waves, int unroll, void* stream) {
+                                  const nvfp4_tile_t* t, void* stream) {
     int st = nvfp4_linear_shape_ok(m, n, k);
     if (st != NVFP4_OK) return st;
+    if (!t) return NVFP4_ERR_NULL;
     nvfp4::Tile tile;
-    tile.cols = cols;
-    tile.waves = waves;
-    tile.unroll = unroll;
+    tile.cols = t->cols;
+    tile.waves = t->waves;
+    tile.unroll = t->unroll;
+    tile.split = t->split;
+    tile.mwaves = t->mwaves;
     if (!nvfp4::tile_valid(tile, n, k)) return NVFP4_ERR_TILE;
-    return launch(x_bf16, w_packed, scales_e4m3, tensor_scale, y, m, n, k, y_dtype, stream, tile);
+    if (t->kernel < NVFP4_KERNEL_AUTO || t->kernel > NVFP4_KERNEL_SPLIT) return NVFP4_ERR_TILE;
+    return launch(x_bf16, w_packed, scales_e4m3, tensor_scale, y, m, n, k, y_dtype, stream, tile, t->kernel);
 }

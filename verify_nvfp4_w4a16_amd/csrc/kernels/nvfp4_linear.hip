@@ -34,6 +34,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <string>
@@ -347,19 +348,142 @@ nvfp4_skinny(Args a) {
     }
 }
 
-// Persistent variant for x small enough to sit in LDS whole (the M = 1 GEMV
+// ---- Weight chunks staged in LDS ---------------------------------------
+// The two fast kernels stream weights through LDS.  A chunk is 512 k of the
+// 16 weight rows of one column tile: 256 bytes of nibbles and 32 scale bytes
+// per row.  Direct-to-LDS loads (global_load_lds) bring it in, each load
+// instruction reading 4 rows x 256 contiguous bytes; loading the MFMA operand
+// layout straight into registers instead touches 16 rows x 64 bytes per
+// instruction (half of each 128-byte line), which streams at roughly half the
+// HBM bandwidth.  The operands are then read from LDS in the MFMA layout.
+//
+// Layout of one column tile's chunk: 4 groups of 4 rows (1024 bytes + 64 of
+// padding per group); row r of a group at 256 r, its 16-byte piece p at
+// 16 (p ^ r).  The load lane l = 16 r + j fetches piece j ^ r of row r and
+// lands at 16 l, so each instruction reads whole 256-byte runs, and the 16
+// rows of one operand read fall into 16 different 16-byte bank groups.  Then
+// 16 rows x 32 scale bytes, row-major.
+constexpr int kChunkK = 512;                      // k per chunk
+constexpr int kGrpBytes = 4 * 256 + 64;
+constexpr int kWBytes = 4 * kGrpBytes;
+constexpr int kSBytes = 16 * 32;
+constexpr int kTileBytes = kWBytes + kSBytes;     // one column tile's chunk in LDS
+constexpr int kDmaPerTile = 6;                    // load instructions per column tile's chunk
+
+// Waits until at most N vector memory operations of this wavefront are
+// outstanding (the direct-to-LDS loads count there), and keeps both the
+// compiler and the scheduler from moving LDS reads above the wait.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Workgroup barrier for LDS traffic: waits for this wavefront's LDS
+// operations only (__syncthreads would also drain every outstanding global
+// load, emptying the weight pipeline at each barrier), then synchronises.
+// Direct-to-LDS loads that others must see are waited for with wait_vm first.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0); vmcnt and expcnt not waited for
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Stores v to LDS at p through an instruction the compiler does not track:
+// a plain LDS store issued while direct-to-LDS loads are in flight makes the
+// compiler wait for every outstanding load first (it may alias their
+// destinations), which would empty the weight pipeline.  Callers order it
+// with lds_barrier, which waits for all LDS operations of the wavefront.
+__device__ __forceinline__ void lds_store_f32(float* p, float v) {
+    const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+    asm volatile("ds_write_b32 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+
+// Issues the loads of the chunk at byte `kb` of each row (k = 2 kb) of weight
+// rows row0 .. row0 + 15 (rows past nmax read row nmax, never used) into dst.
+__device__ __forceinline__ void issue_tile_chunk(uint8_t* dst, const uint8_t* wp, const uint8_t* sc, int row0,
+                                                 int nmax, uint32_t row_bytes, uint32_t scale_bytes, uint32_t kb,
+                                                 int lane) {
+    const int r = lane / 16, j = lane % 16;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const uint32_t row = static_cast<uint32_t>(min(row0 + 4 * u + r, nmax));
+        __builtin_amdgcn_global_load_lds(wp + static_cast<uint64_t>(row) * row_bytes + kb + 16 * (j ^ r),
+                                         dst + u * kGrpBytes, 16, 0, 0);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t row = static_cast<uint32_t>(min(row0 + 8 * h + lane / 8, nmax));
+        __builtin_amdgcn_global_load_lds(sc + static_cast<uint64_t>(row) * scale_bytes + kb / 8 + 4 * (lane % 8),
+                                         dst + kWBytes + h * 256, 4, 0, 0);
+    }
+}
+
+// 16-byte piece p (32 k) of row n of a staged chunk: the B operand of lane
+// (n, kq) for 128-k block b is piece 4 b + kq.
+__device__ __forceinline__ u32x4 chunk_piece(const uint8_t* src, int n, int p) {
+    return *reinterpret_cast<const u32x4*>(src + (n / 4) * kGrpBytes + 256 * (n % 4) + 16 * (p ^ (n % 4)));
+}
+
+// The 8 scale bytes of 128-k block b of row n of a staged chunk.
+__device__ __forceinline__ uint64_t chunk_scales(const uint8_t* src, int n, int b) {
+    return *reinterpret_cast<const uint64_t*>(src + kWBytes + 32 * n + 8 * b);
+}
+
+// Multiplies one staged chunk into acc: C column tiles (chunks at
+// wsrc + c * kTileBytes), MT row tiles of A read from LDS at xsrc (row pitch
+// `pitch` elements, k of the chunk's first element at 0).  Per 128-k block and
+// 32-k slice the MFMA sequence is the one of every kernel here.
+template <int C, int MT>
+__device__ __forceinline__ void mma_chunk(f32x4 (&acc)[C][MT], const uint8_t* wsrc, const uint16_t* xsrc,
+                                          int pitch, const int (&xr)[MT], int col_lane, int kq) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        u32x4 xa[MT][4];
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                xa[t][s] = *reinterpret_cast<const u32x4*>(xsrc + xr[t] * pitch + kBlockK * b + 32 * kq + 8 * s);
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const uint8_t* src = wsrc + c * kTileBytes;
+            const uint32_t d = static_cast<uint32_t>(chunk_scales(src, col_lane, b) >> (16 * kq));
+            const float g0 = __builtin_amdgcn_cvt_f32_fp8(d, 0);
+            const float g1 = __builtin_amdgcn_cvt_f32_fp8(d, 1);
+            const u32x4 w = chunk_piece(src, col_lane, 4 * b + kq);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                bf16x8 bv = decode8(w[s], s < 2 ? g0 : g1);
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+                    acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[t][s]), bv, acc[c][t], 0, 0, 0);
+            }
+        }
+    }
+}
+
+// Persistent kernel for x small enough to sit in LDS whole (the M = 1 GEMV
 // regime and small M).  A few workgroups per CU walk the column tiles
-// t = blockIdx.x, blockIdx.x + gridDim.x, ...; each tile is 16*C columns and
-// its `waves` wavefronts take the same K segments as the non-persistent
-// kernel, so every output has the same chain and the same segment order (the
-// two variants give identical bits).  The weight stream of one wavefront is a
-// single pipeline over (tile, chunk): the loads of the next chunk -- in the
-// next tile at a tile boundary -- are in flight while the current chunk is
-// decoded, and x is staged once per workgroup instead of once per tile.
-template <int C, int MT, int U, bool OUT_F32>
+// t = blockIdx.x, blockIdx.x + gridDim.x, ...; a tile is 16*C columns and its
+// `waves` wavefronts take the K segments of the tile (same chains and the
+// same two-level order as every other kernel).  Each wavefront streams its
+// (tile, chunk) sequence through two LDS chunk buffers of its own: the next
+// chunk's loads are in flight while the current one is multiplied, across
+// tile boundaries too.  x is staged once per workgroup.  With NB = 3 chunk
+// buffers per wavefront two chunks are in flight while one is multiplied
+// (NB = 2: one), which is what keeps enough bytes in flight per CU when a
+// single workgroup fits a CU's LDS.
+//
+// LDS: x [M][K + 8] bf16 | 2 x segment partials | per wavefront NB chunk buffers.
+template <int C, int MT, int NB, bool OUT_F32>
 __global__ void __launch_bounds__(512)
 nvfp4_skinny_persistent(Args a) {
-    extern __shared__ __align__(16) uint16_t lds[];   // x rows, then 2 x partial buffers
+    extern __shared__ __align__(16) uint16_t lds[];
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
     const int waves = blockDim.x / kWave;
@@ -370,11 +494,12 @@ nvfp4_skinny_persistent(Args a) {
     const int pitch = lds_pitch(a.k);
     float* partials = reinterpret_cast<float*>(lds + a.m * pitch);   // [2][waves][C][MT][4][64]
     const int part_stride = waves * C * MT * 4 * kWave;
+    uint8_t* wbuf = reinterpret_cast<uint8_t*>(partials + 2 * part_stride) + wave * NB * C * kTileBytes;
 
     const int tiles = (a.n + 16 * C - 1) / (16 * C);
     const int my_tiles = tiles > (int)blockIdx.x ? (tiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 0;
     const int k0 = wave * a.k_per_wave;
-    const int nch = a.k_per_wave / (kBlockK * U);     // chunks per tile per wavefront
+    const int nch = a.k_per_wave / kChunkK;           // chunks per tile per wavefront
     const int total = my_tiles * nch;
     if (total == 0) return;                           // uniform over the workgroup
 
@@ -382,47 +507,41 @@ nvfp4_skinny_persistent(Args a) {
 #pragma unroll
     for (int t = 0; t < MT; ++t) xr[t] = min(16 * t + col_lane, a.m - 1);
 
-    // chunk j -> tile blockIdx.x + (j / nch) * gridDim.x, k = k0 + (j % nch) * 128U
-    auto load = [&](Chunk<C, MT, U, true>& ch, int j) {
+    // chunk j -> tile blockIdx.x + (j / nch) * gridDim.x, k = k0 + (j % nch) * 512
+    auto issue = [&](int j) {
         const int tile = (int)blockIdx.x + (j / nch) * (int)gridDim.x;
-        const uint32_t kb = static_cast<uint32_t>(k0 + (j % nch) * kBlockK * U);
+        const uint32_t kb = static_cast<uint32_t>(k0 + (j % nch) * kChunkK) / 2;
+        uint8_t* dst = wbuf + (j % NB) * C * kTileBytes;
 #pragma unroll
-        for (int c = 0; c < C; ++c) {
-            const uint32_t n = static_cast<uint32_t>(min(tile * 16 * C + 16 * c + col_lane, a.n - 1));
-            const uint8_t* wr = a.wp + static_cast<uint64_t>(n) * row_bytes + kb / 2 + 16 * kq;
-            const uint8_t* sr = a.sc + static_cast<uint64_t>(n) * scale_bytes + kb / 16;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                ch.w[c][u] = load16_stream(wr + (kBlockK / 2) * u);
-                ch.s[c][u] = load8_stream(sr + (kBlockK / 16) * u);
-            }
-        }
+        for (int c = 0; c < C; ++c)
+            issue_tile_chunk(dst + c * kTileBytes, a.wp, a.sc, tile * 16 * C + 16 * c, a.n - 1, row_bytes,
+                             scale_bytes, kb, lane);
     };
 
-    Chunk<C, MT, U, true> A, B;
-    // Stage x first (all loads issued before the first weights), then the
-    // first chunk's weights, then the LDS stores of x.
+    // Stage x with direct-to-LDS loads, then the first chunks' loads.  (An
+    // LDS store issued while direct-to-LDS loads are in flight makes the
+    // compiler wait for all of them first, as it may alias their
+    // destinations, so this kernel stores nothing to LDS on that path.)  Row r
+    // of x is ceil(K / 512) loads of up to 1 KB; load i is issued by
+    // wavefront i % waves.
     {
-        constexpr int kStage = 4;
-        const int vec_per_row = a.k / 8;
-        const int xtotal = a.m * vec_per_row;
-        const int per_round = kStage * (int)blockDim.x;
-        auto stage_round = [&](int base, bool first) {
-            u32x4 d[kStage];
-            int v[kStage];
-#pragma unroll
-            for (int r = 0; r < kStage; ++r) {
-                v[r] = min(base + r * (int)blockDim.x + (int)threadIdx.x, xtotal - 1);
-                d[r] = load16(a.x + (int64_t)(v[r] / vec_per_row) * a.k + (v[r] % vec_per_row) * 8);
-            }
-            if (first) load(A, 0);
-#pragma unroll
-            for (int r = 0; r < kStage; ++r)
-                *reinterpret_cast<u32x4*>(lds + (v[r] / vec_per_row) * pitch + (v[r] % vec_per_row) * 8) = d[r];
-        };
-        stage_round(0, true);
-        for (int base = per_round; base < xtotal; base += per_round) stage_round(base, false);
-        __syncthreads();
+        const int per_row = (a.k + kChunkK - 1) / kChunkK;
+        const int xloads = a.m * per_row;
+        for (int i = wave; i < xloads; i += waves) {
+            const int r = i / per_row, p = i % per_row;
+            const int valid = min(kWave, (a.k - p * kChunkK) / 8);    // 16-byte pieces in this load
+            if (lane < valid)
+                __builtin_amdgcn_global_load_lds(a.x + (int64_t)r * a.k + p * kChunkK + 8 * lane,
+                                                 lds + r * pitch + p * kChunkK, 16, 0, 0);
+        }
+        issue(0);
+        if (NB > 2 && total > 1) {
+            issue(1);
+            wait_vm<2 * kDmaPerTile * C>();           // this wavefront's x loads have landed
+        } else {
+            wait_vm<kDmaPerTile * C>();
+        }
+        lds_barrier();                                // ... and everyone's
     }
 
     f32x4 acc[C][MT];
@@ -431,32 +550,9 @@ nvfp4_skinny_persistent(Args a) {
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const Chunk<C, MT, U, true>& ch, int j) {
-        const int kb = k0 + (j % nch) * kBlockK * U;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int k = kb + kBlockK * u;
-            u32x4 xa[MT][4];
-#pragma unroll
-            for (int t = 0; t < MT; ++t)
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    xa[t][s] = *reinterpret_cast<const u32x4*>(lds + xr[t] * pitch + k + 32 * kq + 8 * s);
-#pragma unroll
-            for (int c = 0; c < C; ++c) {
-                const uint32_t d = static_cast<uint32_t>(ch.s[c][u] >> (16 * kq));
-                const float g0 = __builtin_amdgcn_cvt_f32_fp8(d, 0);
-                const float g1 = __builtin_amdgcn_cvt_f32_fp8(d, 1);
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    bf16x8 b = decode8(ch.w[c][u][s], s < 2 ? g0 : g1);
-#pragma unroll
-                    for (int t = 0; t < MT; ++t)
-                        acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[t][s]), b,
-                                                                           acc[c][t], 0, 0, 0);
-                }
-            }
-        }
+    auto compute = [&](int j) {
+        mma_chunk<C, MT>(acc, wbuf + (j % NB) * C * kTileBytes, lds + k0 + (j % nch) * kChunkK, pitch, xr,
+                         col_lane, kq);
     };
 
     // After the last chunk of a tile: segment partials through LDS (two
@@ -475,9 +571,10 @@ nvfp4_skinny_persistent(Args a) {
                     for (int t = 0; t < MT; ++t)
 #pragma unroll
                         for (int jj = 0; jj < 4; ++jj)
-                            buf[((wave * C + c) * MT + t) * 4 * kWave + jj * kWave + lane] = acc[c][t][jj];
+                            lds_store_f32(buf + ((wave * C + c) * MT + t) * 4 * kWave + jj * kWave + lane,
+                                          acc[c][t][jj]);
             }
-            __syncthreads();
+            lds_barrier();
         }
         if (wave == 0) {
             f32x4 tot[C][MT] = {};
@@ -485,8 +582,7 @@ nvfp4_skinny_persistent(Args a) {
 #pragma unroll
                 for (int c = 0; c < C; ++c)
 #pragma unroll
-                    for (int t = 0; t < MT; ++t)
-                    {
+                    for (int t = 0; t < MT; ++t) {
                         const float* p = buf + ((w2 * C + c) * MT + t) * 4 * kWave + lane;
                         fold_segment(acc[c][t], tot[c][t], f32x4{p[0], p[kWave], p[2 * kWave], p[3 * kWave]}, w2,
                                      a.group);
@@ -522,36 +618,43 @@ nvfp4_skinny_persistent(Args a) {
             for (int t = 0; t < MT; ++t) acc[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     };
 
-    // One pipeline over all (tile, chunk) of this wavefront; a load past the
-    // end repeats the last chunk (never computed), keeping loads
-    // unconditional.  The loop has a single exit at the bottom: an exit
-    // between the two halves would give the header a path on which chunk B
-    // is still in flight, and the compiler would then drain every load there.
+    // One pipeline over all (tile, chunk) of this wavefront, NB - 1 chunks
+    // ahead, with its single exit at the bottom; the last chunks are peeled,
+    // so no load is repeated.
+    constexpr int kAhead = NB - 1;
     int j = 0;
-    for (; j + 1 < total; j += 2) {
-        load(B, j + 1);
-        issue_point();
-        compute(A, j);
-        if (j % nch == nch - 1) finish_tile(j);
-        load(A, min(j + 2, total - 1));
-        issue_point();
-        compute(B, j + 1);
-        if ((j + 1) % nch == nch - 1) finish_tile(j + 1);
-    }
-    if (j < total) {
-        compute(A, j);
+    for (; j + kAhead < total; ++j) {
+        issue(j + kAhead);
+        wait_vm<kAhead * kDmaPerTile * C>();          // chunk j has landed
+        compute(j);
         if (j % nch == nch - 1) finish_tile(j);
     }
+    if (NB > 2 && j + 1 < total) {
+        wait_vm<kDmaPerTile * C>();
+        compute(j);
+        if (j % nch == nch - 1) finish_tile(j);
+        ++j;
+    }
+    wait_vm<0>();
+    compute(j);
+    finish_tile(j);                                   // the last chunk ends a tile
+}
+
+// LDS bytes of the persistent kernel with nb chunk buffers per wavefront.
+size_t persistent_lds_bytes(int64_t m, int64_t k, int waves, int c, int mt, int nb) {
+    return size_t(m) * (k + 8) * sizeof(uint16_t) + 2 * size_t(waves) * c * mt * 4 * kWave * sizeof(float) +
+           size_t(waves) * nb * c * kTileBytes;
 }
 
 // Many-row kernel (x too large to sit whole in one workgroup's LDS).  A
 // workgroup owns 16*C*W output columns (W wavefronts with C column tiles
 // each) and one segment group: K range [part * K/split, (part+1) * K/split),
 // i.e. `group` consecutive segments.  x comes into LDS in windows of 512 k
-// (two pipeline chunks), double-buffered, and every window is read by all W
-// wavefronts, so x is fetched once per 16*C*W columns instead of once per
-// 16*C.  A wavefront runs the chains of the group's segments one after the
-// other and keeps the group sum (chains added in segment order).
+// (one chunk), double-buffered, each row of a window one direct-to-LDS load;
+// every window is read by all W wavefronts, so x is fetched once per 16*C*W
+// columns instead of once per 16*C.  Each wavefront streams its weight chunks
+// through two LDS buffers of its own, runs the chains of the group's segments
+// one after the other and keeps the group sum (chains added in segment order).
 //
 // With split == 1 that sum is the output.  Otherwise the column group's
 // `split` workgroups are blockIdx = part * groups + column_group: those of
@@ -576,18 +679,13 @@ struct SplitArgs {
 };
 
 constexpr uint32_t kSpinLimit = 1u << 20;   // polls of a flag before giving up (~1 s)
+constexpr int kXPitch = kChunkK + 8;        // LDS row pitch of an x window (bf16 elements)
 
 template <int C, int MT, int W, bool OUT_F32>
 __global__ void __launch_bounds__(64 * W)
 nvfp4_skinny_split(SplitArgs sa) {
-    constexpr int U = 2;
-    constexpr int kChunk = kBlockK * U;                 // k per pipeline chunk
-    constexpr int kWin = 2 * kChunk;                    // k per x window
-    constexpr int kPitch = kWin + 8;                    // LDS row pitch (bf16 elements)
-    constexpr int kVecRow = kWin / 8;                   // 16-byte vectors per window row
-    constexpr int kThreads = 64 * W;
-    constexpr int kStage = (16 * MT * kVecRow + kThreads - 1) / kThreads;
-    extern __shared__ __align__(16) uint16_t lds[];    // two windows [M][kPitch]
+    constexpr int kXLoads = (16 * MT + W - 1) / W;      // x rows one wavefront loads per window
+    extern __shared__ __align__(16) uint16_t lds[];    // x windows [2][M][kXPitch] | chunk buffers
     const Args& a = sa.a;
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
@@ -597,54 +695,36 @@ nvfp4_skinny_split(SplitArgs sa) {
     const int part = (int)blockIdx.x / sa.groups;
     const int krange = a.k / sa.split;
     const int kbase = part * krange;
-    const int nwin = krange / kWin;
-    const int seg_chunks = a.k_per_wave / kChunk;
-    const int slice = a.m * kPitch;
+    const int nwin = krange / kChunkK;
+    const int seg_chunks = a.k_per_wave / kChunkK;
+    const int slice = a.m * kXPitch;
     const int col_base = (cgroup * W + wave) * 16 * C;
     const uint32_t row_bytes = static_cast<uint32_t>(a.k) / 2;
     const uint32_t scale_bytes = static_cast<uint32_t>(a.k) / 16;
+    uint8_t* wbuf = reinterpret_cast<uint8_t*>(lds + 2 * slice) + wave * 2 * C * kTileBytes;
 
-    const uint8_t* wrow[C];
-    const uint8_t* srow[C];
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-        const uint32_t n = static_cast<uint32_t>(min(col_base + 16 * c + col_lane, a.n - 1));
-        wrow[c] = a.wp + static_cast<uint64_t>(n) * row_bytes + kbase / 2 + 16 * kq;
-        srow[c] = a.sc + static_cast<uint64_t>(n) * scale_bytes + kbase / 16;
-    }
     int xr[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) xr[t] = min(16 * t + col_lane, a.m - 1);
 
-    // chunk i of the range: k = kbase + i * kChunk
-    auto load = [&](Chunk<C, MT, U, true>& ch, int i) {
-        const uint32_t kb = static_cast<uint32_t>(i * kChunk);
+    // x window `win`: rows wave, wave + W, ... (clamped to M-1: a repeated
+    // load of identical data), each 1 KB landing at its LDS row.
+    auto issue_x = [&](int win) {
+        uint16_t* dst = lds + (win & 1) * slice;
+#pragma unroll
+        for (int i = 0; i < kXLoads; ++i) {
+            const int r = min(wave + i * W, a.m - 1);
+            __builtin_amdgcn_global_load_lds(a.x + (int64_t)r * a.k + kbase + win * kChunkK + 8 * lane,
+                                             dst + r * kXPitch, 16, 0, 0);
+        }
+    };
+    auto issue_w = [&](int win) {
+        const uint32_t kb = static_cast<uint32_t>(kbase + win * kChunkK) / 2;
+        uint8_t* dst = wbuf + (win & 1) * C * kTileBytes;
 #pragma unroll
         for (int c = 0; c < C; ++c)
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                ch.w[c][u] = load16_stream(wrow[c] + (kb + kBlockK * u) / 2);
-                ch.s[c][u] = load8_stream(srow[c] + (kb + kBlockK * u) / 16);
-            }
-    };
-    // x window `win` of the range: loads into registers, then stores to LDS.
-    // Indices past the last row are clamped (a repeated store of one value).
-    const int xtotal = a.m * kVecRow;
-    u32x4 xs[kStage];
-    auto stage_issue = [&](int win) {
-        const uint16_t* src = a.x + kbase + win * kWin;
-#pragma unroll
-        for (int r = 0; r < kStage; ++r) {
-            const int v = min(r * kThreads + (int)threadIdx.x, xtotal - 1);
-            xs[r] = load16(src + (int64_t)(v / kVecRow) * a.k + (v % kVecRow) * 8);
-        }
-    };
-    auto stage_commit = [&](int buf) {
-#pragma unroll
-        for (int r = 0; r < kStage; ++r) {
-            const int v = min(r * kThreads + (int)threadIdx.x, xtotal - 1);
-            *reinterpret_cast<u32x4*>(lds + buf * slice + (v / kVecRow) * kPitch + (v % kVecRow) * 8) = xs[r];
-        }
+            issue_tile_chunk(dst + c * kTileBytes, a.wp, a.sc, col_base + 16 * c, a.n - 1, row_bytes, scale_bytes,
+                             kb, lane);
     };
 
     f32x4 acc[C][MT], grp[C][MT];
@@ -653,36 +733,13 @@ nvfp4_skinny_split(SplitArgs sa) {
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[c][t] = grp[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // chunk i (its window's buffer `buf`, half i % 2 of the window)
-    auto compute = [&](const Chunk<C, MT, U, true>& ch, int i, int buf) {
-        const uint16_t* xb = lds + buf * slice + (i % 2) * kChunk;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            u32x4 xa[MT][4];
-#pragma unroll
-            for (int t = 0; t < MT; ++t)
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    xa[t][s] = *reinterpret_cast<const u32x4*>(xb + xr[t] * kPitch + kBlockK * u + 32 * kq + 8 * s);
-#pragma unroll
-            for (int c = 0; c < C; ++c) {
-                const uint32_t d = static_cast<uint32_t>(ch.s[c][u] >> (16 * kq));
-                const float g0 = __builtin_amdgcn_cvt_f32_fp8(d, 0);
-                const float g1 = __builtin_amdgcn_cvt_f32_fp8(d, 1);
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    bf16x8 b = decode8(ch.w[c][u][s], s < 2 ? g0 : g1);
-#pragma unroll
-                    for (int t = 0; t < MT; ++t)
-                        acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[t][s]), b,
-                                                                           acc[c][t], 0, 0, 0);
-                }
-            }
-        }
+    auto compute = [&](int win) {
+        mma_chunk<C, MT>(acc, wbuf + (win & 1) * C * kTileBytes, lds + (win & 1) * slice, kXPitch, xr, col_lane,
+                         kq);
         // end of a segment: its chain joins the group sum (the first chain
         // is taken as it is, so a -0 sum keeps its sign)
-        if ((i + 1) % seg_chunks == 0) {
-            const bool first = i + 1 == seg_chunks;
+        if ((win + 1) % seg_chunks == 0) {
+            const bool first = win + 1 == seg_chunks;
 #pragma unroll
             for (int c = 0; c < C; ++c)
 #pragma unroll
@@ -693,31 +750,22 @@ nvfp4_skinny_split(SplitArgs sa) {
         }
     };
 
-    // Pipeline: while chunk i is multiplied, chunk i + 1 is in flight; the
-    // next window's x loads go out right after the weights of the window's
-    // second chunk and are stored to the other buffer after both chunks.
-    Chunk<C, MT, U, true> A, B;
-    stage_issue(0);
-    load(A, 0);
-    stage_commit(0);
-    __syncthreads();
+    // Window w is multiplied while window w + 1 (x and weights) is in flight.
+    issue_x(0);
+    issue_w(0);
+    wait_vm<0>();
+    lds_barrier();
     int win = 0;
     for (; win + 1 < nwin; ++win) {
-        const int buf = win & 1;
-        load(B, 2 * win + 1);
-        stage_issue(win + 1);
-        issue_point();
-        compute(A, 2 * win, buf);
-        load(A, 2 * win + 2);
-        issue_point();
-        compute(B, 2 * win + 1, buf);
-        stage_commit(buf ^ 1);
-        __syncthreads();
+        issue_x(win + 1);
+        issue_w(win + 1);
+        wait_vm<kXLoads + kDmaPerTile * C>();       // window win's weights have landed
+        compute(win);
+        wait_vm<kDmaPerTile * C>();                 // this wavefront's x rows of win + 1 have landed
+        lds_barrier();                              // ... and everyone's; buffer win & 1 is free
     }
-    load(B, 2 * win + 1);
-    issue_point();
-    compute(A, 2 * win, win & 1);
-    compute(B, 2 * win + 1, win & 1);
+    wait_vm<0>();
+    compute(win);
 
     if (sa.split > 1) {
         constexpr int kSlot = W * C * MT * 4 * kWave;   // floats of one workgroup's group sums
@@ -798,6 +846,11 @@ nvfp4_skinny_split(SplitArgs sa) {
     }
 }
 
+// LDS bytes of the many-row kernel (dynamic part).
+size_t split_lds_bytes(int64_t m, int w, int c) {
+    return 2 * size_t(m) * kXPitch * sizeof(uint16_t) + size_t(w) * 2 * c * kTileBytes;
+}
+
 using KernelFn = void (*)(Args);
 using SplitFn = void (*)(SplitArgs);
 
@@ -830,24 +883,21 @@ KernelFn pick_kernel(int mt, int cols, int unroll, bool xlds, int y_dtype) {
     return mt == 1 ? pick_c<1>(cols, unroll, xlds, y_dtype) : pick_c<2>(cols, unroll, xlds, y_dtype);
 }
 
-template <int C, int MT, int U>
+template <int C, int MT, int NB>
 KernelFn pick_p_out(int y_dtype) {
-    return y_dtype == NVFP4_OUT_F32 ? nvfp4_skinny_persistent<C, MT, U, true>
-                                    : nvfp4_skinny_persistent<C, MT, U, false>;
+    return y_dtype == NVFP4_OUT_F32 ? nvfp4_skinny_persistent<C, MT, NB, true>
+                                    : nvfp4_skinny_persistent<C, MT, NB, false>;
 }
 
-template <int C, int MT>
-KernelFn pick_p_u(int unroll, int y_dtype) {
-    switch (unroll) {
-        case 1: return pick_p_out<C, MT, 1>(y_dtype);
-        case 2: return pick_p_out<C, MT, 2>(y_dtype);
-        default: return pick_p_out<C, MT, 4>(y_dtype);
-    }
+template <int NB>
+KernelFn pick_p_c(int mt, int c, int y_dtype) {
+    if (mt == 1) return c == 1 ? pick_p_out<1, 1, NB>(y_dtype) : pick_p_out<2, 1, NB>(y_dtype);
+    return c == 1 ? pick_p_out<1, 2, NB>(y_dtype) : pick_p_out<2, 2, NB>(y_dtype);
 }
 
-KernelFn pick_persistent(int mt, int cols, int unroll, int y_dtype) {
-    if (mt == 1) return cols == 16 ? pick_p_u<1, 1>(unroll, y_dtype) : pick_p_u<2, 1>(unroll, y_dtype);
-    return cols == 16 ? pick_p_u<1, 2>(unroll, y_dtype) : pick_p_u<2, 2>(unroll, y_dtype);
+// c: column tiles per wavefront (1 or 2); nb: chunk buffers per wavefront (2 or 3)
+KernelFn pick_persistent(int mt, int c, int nb, int y_dtype) {
+    return nb == 3 ? pick_p_c<3>(mt, c, y_dtype) : pick_p_c<2>(mt, c, y_dtype);
 }
 
 template <int C, int MT, int W>
@@ -906,9 +956,9 @@ int init_device(int dev) {
                 for (int un = 1; un <= 4; un *= 2)
                     for (int xl = 0; xl <= 1; ++xl)
                         if (!allow_full_lds(pick_kernel(mt, cols[ci], un, xl != 0, od))) return NVFP4_ERR_HIP;
-            for (int cc = 16; cc <= 32; cc += 16)
-                for (int un = 1; un <= 4; un *= 2)
-                    if (!allow_full_lds(pick_persistent(mt, cc, un, od))) return NVFP4_ERR_HIP;
+            for (int c = 1; c <= 2; ++c)
+                for (int nb = 2; nb <= 3; ++nb)
+                    if (!allow_full_lds(pick_persistent(mt, c, nb, od))) return NVFP4_ERR_HIP;
             for (int c = 1; c <= 2; ++c)
                 for (int w = 4; w <= 8; w += 4)
                     if (!allow_full_lds(pick_split(mt, c, w, od))) return NVFP4_ERR_HIP;
@@ -971,12 +1021,13 @@ struct SplitPlan {
 
 bool plan_split(const nvfp4::Tile& tile, int64_t m, int64_t n, int64_t k, const DeviceState& d, SplitPlan* p) {
     const int64_t seg = k / tile.waves;
-    if (seg % 256 != 0 || (k / tile.split) % 512 != 0) return false;
+    if (seg % kChunkK != 0) return false;
     p->c = tile.cols == 16 ? 1 : 2;
     p->w = tile.mwaves;
     const int64_t cols = int64_t(16) * p->c * p->w;
     p->groups = (n + cols - 1) / cols;
-    p->lds = 2 * size_t(m) * (512 + 8) * sizeof(uint16_t);
+    p->lds = split_lds_bytes(m, p->w, p->c);
+    if (p->lds + 256 > size_t(kMaxLdsBytes)) return false;
     if (tile.split > 1) {
         const int mt = m <= 16 ? 1 : 2;
         const size_t slot = size_t(p->w) * p->c * mt * 4 * kWave * sizeof(float);
@@ -1021,12 +1072,16 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
     const int c = tile.cols / 16;
     const hipStream_t hs = static_cast<hipStream_t>(stream);
 
-    // x [M, K] small enough to share the LDS of one workgroup with two
-    // buffers of segment partials, in at most 64 KB so a CU holds two such
-    // workgroups: the persistent kernel.
+    // The persistent kernel when x [M, K], two buffers of segment partials
+    // and the wavefronts' chunk buffers fit one workgroup's LDS and the
+    // segments are whole chunks; two workgroups per CU when two fit.
     const size_t x_bytes = size_t(m) * (k + 8) * sizeof(uint16_t);
-    const size_t pers_bytes = x_bytes + 2 * size_t(tile.waves) * c * mt * 4 * kWave * sizeof(float);
-    const bool pers_ok = tile.cols <= 32 && pers_bytes <= size_t(64 * 1024);
+    // Three chunk buffers per wavefront when they fit, else two.
+    const int pc = tile.cols == 16 ? 1 : 2;
+    const int pnb = persistent_lds_bytes(m, k, tile.waves, pc, mt, 3) + 256 <= size_t(kMaxLdsBytes) ? 3 : 2;
+    const size_t pers_bytes = persistent_lds_bytes(m, k, tile.waves, pc, mt, pnb);
+    const bool pers_ok = tile.cols <= 32 && (k / tile.waves) % kChunkK == 0 &&
+                         pers_bytes + 256 <= size_t(kMaxLdsBytes) && x_bytes <= size_t(64 * 1024);
     SplitPlan plan;
     const bool split_ok = plan_split(tile, m, n, k, d, &plan);
     if (kernel == NVFP4_KERNEL_AUTO)
@@ -1037,9 +1092,9 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
     if (kernel == NVFP4_KERNEL_PERSISTENT) {
         const int cus = d.cus > 0 ? d.cus : 256;
         const int64_t tiles = (n + tile.cols - 1) / tile.cols;
-        const int per_cu = tile.waves >= 8 ? 2 : 4;
+        const int per_cu = std::max(1, std::min(64 / tile.waves, int(kMaxLdsBytes / (pers_bytes + 256))));
         const int64_t grid_p = tiles < int64_t(per_cu) * cus ? tiles : int64_t(per_cu) * cus;
-        hipLaunchKernelGGL(pick_persistent(mt, tile.cols, tile.unroll, y_dtype),
+        hipLaunchKernelGGL(pick_persistent(mt, pc, pnb, y_dtype),
                            dim3(static_cast<unsigned>(grid_p)), dim3(static_cast<unsigned>(kWave * tile.waves)),
                            pers_bytes, hs, a);
     } else if (kernel == NVFP4_KERNEL_SPLIT) {

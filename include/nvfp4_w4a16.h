@@ -135,14 +135,17 @@ int nvfp4_linear(const void* x_bf16, const uint8_t* w_packed,
                  const uint8_t* scales_e4m3, float tensor_scale, void* y,
                  int64_t m, int64_t n, int64_t k, int y_dtype, void* stream);
 
-/* Kernel choice of nvfp4_linear_tiled (nvfp4_linear always chooses itself). */
+/* Kernel choice of nvfp4_linear_tiled (nvfp4_linear always chooses itself).
+ * Every kernel computes the same bits for the same tile waves and split. */
 enum {
     NVFP4_KERNEL_AUTO = 0,       /* as nvfp4_linear: by M, K and the workspace */
-    NVFP4_KERNEL_PERSISTENT = 1, /* x [M, K] whole in LDS; needs M * (K + 8) * 2 + partials <= 64 KB, cols <= 32 */
-    NVFP4_KERNEL_TILE = 2,       /* one workgroup per 16 * C columns, all segments; any shape */
-    NVFP4_KERNEL_SPLIT = 3       /* many-row kernel: one segment group per workgroup, x windows in LDS;
-                                    needs K / waves % 256 == 0, K / split % 512 == 0 and, for
-                                    split > 1, the device workspace */
+    NVFP4_KERNEL_PERSISTENT = 1, /* workgroups walk the column tiles with x [M, K] whole in LDS; needs
+                                    K / waves % 512 == 0, M * (K + 8) * 2 <= 64 KB, cols <= 32 */
+    NVFP4_KERNEL_TILE = 2,       /* one workgroup per column tile, each wavefront streaming its K segment
+                                    through LDS; needs K / waves % 512 == 0, cols <= 32 and small M */
+    NVFP4_KERNEL_SPLIT = 3,      /* many-row kernel: one segment group per workgroup, x windows in LDS;
+                                    needs K / waves % 512 == 0 and, for split > 1, the device workspace */
+    NVFP4_KERNEL_GENERIC = 4     /* one workgroup per column tile, register loads; any shape */
 };
 
 /*
@@ -158,7 +161,7 @@ typedef struct nvfp4_tile {
     int waves;  /* K segments, 1..8 (wavefronts per workgroup of the one-group kernels) */
     int unroll; /* 128-k blocks per pipeline step: 1, 2 or 4; K % (128 * unroll * waves) == 0 */
     int split;  /* segment groups: 1, 2, 4 or 8, dividing waves */
-    int mwaves; /* wavefronts per workgroup of the many-row kernel: 4 or 8 */
+    int mwaves; /* wavefronts per workgroup of the many-row kernel: 4 or 8; 0 = by M (4 up to 16 rows) */
     int kernel; /* NVFP4_KERNEL_*; ignored by the (N, K) table */
 } nvfp4_tile_t;
 

@@ -158,7 +158,7 @@ def test_tiled_entry_validates_the_tile():
     lib = nv._lib()
     buf = (ctypes.c_uint8 * 64)()
     a16 = (ctypes.addressof(buf) + 15) & ~15
-    def call(cols, waves, unroll, k=1024, m=1, split=1, mwaves=8, kernel=nv.KERNEL_AUTO):
+    def call(cols, waves, unroll, k=1024, m=1, split=1, mwaves=0, kernel=nv.KERNEL_AUTO):
         t = nv.Tile(cols, waves, unroll, split, mwaves, kernel)
         return lib.nvfp4_linear_tiled(a16, a16, a16, 1.0, a16, m, 16, k, 0, ctypes.byref(t), None)
     assert call(48, 2, 2) == nv.ERR_TILE
@@ -169,7 +169,7 @@ def test_tiled_entry_validates_the_tile():
     assert call(16, 4, 2, split=3) == nv.ERR_TILE    # split not a power of two
     assert call(16, 2, 2, split=4) == nv.ERR_TILE    # more groups than segments
     assert call(16, 4, 2, mwaves=2) == nv.ERR_TILE   # many-row workgroups are 4 or 8 wavefronts
-    assert call(16, 4, 2, kernel=4) == nv.ERR_TILE   # no such kernel
+    assert call(16, 4, 2, kernel=5) == nv.ERR_TILE   # no such kernel
     assert call(16, 4, 2, kernel=-1) == nv.ERR_TILE
     assert call(16, 2, 2, k=100) == nv.ERR_SHAPE
     assert call(16, 2, 2, m=0) == nv.OK              # M == 0: nothing launched
@@ -183,7 +183,7 @@ def test_tile_struct_matches_the_header():
     body = re.search(r"typedef struct nvfp4_tile \{(.*?)\} nvfp4_tile_t;", header, re.S).group(1)
     names = re.findall(r"int (\w+);", body)
     assert names == [f for f, _ in nv.Tile._fields_]
-    for name in ("KERNEL_AUTO", "KERNEL_PERSISTENT", "KERNEL_TILE", "KERNEL_SPLIT"):
+    for name in ("KERNEL_AUTO", "KERNEL_PERSISTENT", "KERNEL_TILE", "KERNEL_SPLIT", "KERNEL_GENERIC"):
         value = int(re.search(r"NVFP4_%s = (\d+)" % name, header).group(1))
         assert getattr(nv, name) == value
 
@@ -204,7 +204,7 @@ def test_tile_info_depends_on_shape_only():
         assert f"N={n} K={k}" in info
         assert info == nv.tile_info(n, k)
         t = nv.table_tile(n, k)
-        assert t.waves % t.split == 0 and t.mwaves in (4, 8)
+        assert t.waves % t.split == 0 and t.mwaves in (0, 4, 8)
     with pytest.raises(nv.Nvfp4Error):
         nv.tile_info(16, 100)
     buf = ctypes.create_string_buffer(8)
@@ -212,13 +212,19 @@ def test_tile_info_depends_on_shape_only():
 
 
 def test_default_split_fills_the_chip():
-    # Segment groups: enough 128-column workgroups for two per CU of 256, at
-    # most one group per segment; a function of N (and K through waves) only.
-    for n, k, split in [(4096, 4096, 8), (8192, 4096, 8), (24576, 4096, 4), (12288, 4096, 8),
-                        (151552, 4096, 1), (65536, 4096, 1), (32768, 4096, 2), (4096, 256, 2),
-                        (16, 1024, 8)]:
+    # Segment groups: enough 128-column workgroups for every one of 256 CUs,
+    # at most one group per segment; a function of N (and K through waves).
+    for n, k, split in [(4096, 4096, 8), (12288, 4096, 4), (32768, 4096, 1), (16384, 4096, 2),
+                        (65536, 4096, 1), (151552, 4096, 1), (4096, 256, 2), (16, 1024, 8)]:
         t = nv.table_tile(n, k)
         assert t.split == min(split, t.waves), (n, k, t)
+
+
+def test_builtin_table_entries():
+    # Sweep-picked splits of the decode round's products; all else default.
+    for n, k, split in [(8192, 4096, 4), (4096, 8192, 4), (24576, 4096, 1), (4096, 12288, 8)]:
+        t = nv.table_tile(n, k)
+        assert (t.cols, t.waves, t.split, t.mwaves) == (16, 8, split, 0), (n, k, t)
 
 
 def _tile_info_in_fresh_process(env_value, n=1024, k=1024):
@@ -240,9 +246,9 @@ def test_tile_override_file(tmp_path):
     # The table is read once per process, so each case runs in its own process.
     f = tmp_path / "tiles.txt"
     f.write_text("# N K cols waves unroll\n1024 1024 32 4 2\n")
-    assert "cols=32 waves=4 unroll=2 split=1 mwaves=8" in _tile_info_in_fresh_process(str(f))
+    assert "cols=32 waves=4 unroll=2 split=1 mwaves=0" in _tile_info_in_fresh_process(str(f))
     f.write_text("1024 1024 32 4 2 2\n")
-    assert "cols=32 waves=4 unroll=2 split=2 mwaves=8" in _tile_info_in_fresh_process(str(f))
+    assert "cols=32 waves=4 unroll=2 split=2 mwaves=0" in _tile_info_in_fresh_process(str(f))
     f.write_text("1024 1024 32 4 2 4 4  # comment\n")
     assert "cols=32 waves=4 unroll=2 split=4 mwaves=4" in _tile_info_in_fresh_process(str(f))
     for bad in ("1024 1024 32 4 2 8\n",          # more groups than segments

@@ -143,7 +143,7 @@ def test_launch_settings_never_change_bits():
         x = upload_bits(workload.activations_bf16(m, s.k, 62 + m))
         ref = bits(nv.linear(x, w.wp, w.sc, w.t)).clone()
         ran = set()
-        for kernel in (nv.KERNEL_PERSISTENT, nv.KERNEL_TILE, nv.KERNEL_SPLIT):
+        for kernel in (nv.KERNEL_PERSISTENT, nv.KERNEL_TILE, nv.KERNEL_SPLIT, nv.KERNEL_GENERIC):
             for cols in (16, 32, 64):
                 for unroll in (1, 2, 4):
                     for mwaves in (4, 8):
@@ -160,4 +160,6 @@ def test_launch_settings_never_change_bits():
                         torch.cuda.synchronize()
                         ran.add(kernel)
                         assert torch.equal(bits(y), ref), f"M={m} {tile}"
-        assert nv.KERNEL_TILE in ran and nv.KERNEL_SPLIT in ran, (m, ran)
+        assert nv.KERNEL_GENERIC in ran and nv.KERNEL_SPLIT in ran, (m, ran)
+        if m <= 3:
+            assert nv.KERNEL_TILE in ran and nv.KERNEL_PERSISTENT in ran, (m, ran)

@@ -21,7 +21,7 @@ ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_NONFINITE = -1, -2, -3, -4, -5
 ERR_BADSCALE, ERR_HIP, ERR_DEVICE, ERR_TILEFILE, ERR_BUFFER = -6, -7, -8, -9, -10
 ERR_TILE = -11
 OUT_BF16, OUT_F32 = 0, 1
-KERNEL_AUTO, KERNEL_PERSISTENT, KERNEL_TILE, KERNEL_SPLIT = 0, 1, 2, 3
+KERNEL_AUTO, KERNEL_PERSISTENT, KERNEL_TILE, KERNEL_SPLIT, KERNEL_GENERIC = 0, 1, 2, 3, 4
 MAX_M = 32
 K_MULTIPLE = 256
 
@@ -34,7 +34,7 @@ class Tile(ctypes.Structure):
     _fields_ = [("cols", ctypes.c_int), ("waves", ctypes.c_int), ("unroll", ctypes.c_int),
                 ("split", ctypes.c_int), ("mwaves", ctypes.c_int), ("kernel", ctypes.c_int)]
 
-    def __init__(self, cols=16, waves=8, unroll=2, split=1, mwaves=8, kernel=KERNEL_AUTO):
+    def __init__(self, cols=16, waves=8, unroll=2, split=1, mwaves=0, kernel=KERNEL_AUTO):
         super().__init__(cols, waves, unroll, split, mwaves, kernel)
 
     def replace(self, **kw) -> "Tile":

@@ -17,10 +17,26 @@ namespace {
 
 using Key = std::pair<int64_t, int64_t>;
 
-// Built-in entries chosen by sweeping launch settings on MI355X, keeping only
-// settings whose output bits equal the default's at every row count 1..32.
+Tile default_tile(int64_t n, int64_t k);
+
+// Built-in entries chosen by sweeping launch settings on MI355X (every
+// kernel at M = 1, 2, 8, 16, 32 over cold weights; the split that gave the
+// lowest times over those row counts).  Every entry's bits are the same at
+// every row count; entries differ from the default rule only in split.
 const std::map<Key, Tile>& builtin_table() {
-    static const std::map<Key, Tile> table = {};
+    static const std::map<Key, Tile> table = [] {
+        std::map<Key, Tile> t;
+        auto add = [&](int64_t n, int64_t k, int split) {
+            Tile x = default_tile(n, k);
+            x.split = split;
+            t[{n, k}] = x;
+        };
+        add(8192, 4096, 4);     // q/o-sized products of the decode round
+        add(4096, 8192, 4);
+        add(24576, 4096, 1);    // gate/up
+        add(4096, 12288, 8);    // down
+        return t;
+    }();
     return table;
 }
 
@@ -42,7 +58,7 @@ Tile default_tile(int64_t n, int64_t k) {
     int64_t per = blocks / waves;
     t.unroll = per % 4 == 0 ? 4 : per % 2 == 0 ? 2 : 1;
     t.split = default_split(n, waves);
-    t.mwaves = 8;
+    t.mwaves = 0;
     return t;
 }
 
@@ -51,7 +67,7 @@ Tile default_tile(int64_t n, int64_t k) {
 int default_split(int64_t n, int waves) {
     const int64_t groups = (n + 127) / 128;
     int split = 1;
-    while (split < waves && groups * split < 512) split *= 2;
+    while (split < waves && groups * split < 256) split *= 2;
     return split;
 }
 
@@ -62,7 +78,7 @@ bool tile_valid(const Tile& t, int64_t /*n*/, int64_t k) {
     if (k % (int64_t(128) * t.unroll * t.waves) != 0) return false;
     if (t.split != 1 && t.split != 2 && t.split != 4 && t.split != 8) return false;
     if (t.split > t.waves || t.waves % t.split != 0) return false;
-    if (t.mwaves != 4 && t.mwaves != 8) return false;
+    if (t.mwaves != 0 && t.mwaves != 4 && t.mwaves != 8) return false;
     return true;
 }
 
@@ -107,7 +123,7 @@ static int read_override_file() {
         t.waves = static_cast<int>(v[3]);
         t.unroll = static_cast<int>(v[4]);
         t.split = v.size() > 5 ? static_cast<int>(v[5]) : 1;
-        t.mwaves = v.size() > 6 ? static_cast<int>(v[6]) : 8;
+        t.mwaves = v.size() > 6 ? static_cast<int>(v[6]) : 0;
         if (nvfp4_linear_shape_ok(1, n, k) != NVFP4_OK || !tile_valid(t, n, k))
             return NVFP4_ERR_TILEFILE;
         table[{n, k}] = t;

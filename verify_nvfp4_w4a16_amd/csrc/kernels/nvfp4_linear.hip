@@ -646,6 +646,138 @@ size_t persistent_lds_bytes(int64_t m, int64_t k, int waves, int c, int mt, int 
            size_t(waves) * nb * c * kTileBytes;
 }
 
+// Per-tile kernel: one workgroup per column tile of 16*C columns, its
+// `waves` wavefronts one K segment each.  Every wavefront stages its own
+// slice of x (M rows x k_per_wave) and streams its segment's chunks through
+// NB LDS buffers of its own, all by direct-to-LDS loads, so no wavefront
+// waits for another until the segment sums are added: each writes its sum
+// into its first chunk buffer, and after one barrier wavefront 0 adds them in
+// the two-level order, scales, rounds and stores.  With workgroups short and
+// small, several share a CU and one's reduction overlaps the others' loads.
+//
+// LDS per wavefront: x slice [M][k_per_wave + 8] bf16 | NB chunk buffers.
+template <int C, int MT, int NB, bool OUT_F32>
+__global__ void __launch_bounds__(512)
+nvfp4_skinny_tile(Args a) {
+    extern __shared__ __align__(16) uint8_t ldsb[];
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    const int waves = blockDim.x / kWave;
+    const int col_lane = lane % 16;
+    const int kq = lane / 16;
+    const int ks = a.k_per_wave;
+    const int nch = ks / kChunkK;
+    const int xpitch = ks + 8;
+    const uint32_t row_bytes = static_cast<uint32_t>(a.k) / 2;
+    const uint32_t scale_bytes = static_cast<uint32_t>(a.k) / 16;
+    const int wave_bytes = a.m * xpitch * 2 + NB * C * kTileBytes;
+    uint16_t* xs = reinterpret_cast<uint16_t*>(ldsb + wave * wave_bytes);
+    uint8_t* wbuf = ldsb + wave * wave_bytes + a.m * xpitch * 2;
+    const int col0 = (int)blockIdx.x * 16 * C;
+    const int k0 = wave * ks;
+
+    int xr[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) xr[t] = min(16 * t + col_lane, a.m - 1);
+
+    // this wavefront's x slice: M x nch loads of 1 KB
+    for (int i = 0; i < a.m * nch; ++i) {
+        const int r = i / nch, p = i % nch;
+        __builtin_amdgcn_global_load_lds(a.x + (int64_t)r * a.k + k0 + p * kChunkK + 8 * lane,
+                                         xs + r * xpitch + p * kChunkK, 16, 0, 0);
+    }
+    auto issue = [&](int j) {
+        const uint32_t kb = static_cast<uint32_t>(k0 + j * kChunkK) / 2;
+        uint8_t* dst = wbuf + (j % NB) * C * kTileBytes;
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+            issue_tile_chunk(dst + c * kTileBytes, a.wp, a.sc, col0 + 16 * c, a.n - 1, row_bytes, scale_bytes, kb,
+                             lane);
+    };
+
+    f32x4 acc[C][MT];
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](int j) {
+        mma_chunk<C, MT>(acc, wbuf + (j % NB) * C * kTileBytes, xs + j * kChunkK, xpitch, xr, col_lane, kq);
+    };
+
+    // NB - 1 chunks ahead; the last ones peeled so no load is repeated.
+    constexpr int kAhead = NB - 1;
+    for (int q = 0; q < kAhead && q < nch; ++q) issue(q);
+    int j = 0;
+    for (; j + kAhead < nch; ++j) {
+        issue(j + kAhead);
+        wait_vm<kAhead * kDmaPerTile * C>();          // x and chunk j have landed
+        compute(j);
+    }
+    if (NB > 2 && j + 1 < nch) {
+        wait_vm<kDmaPerTile * C>();
+        compute(j);
+        ++j;
+    }
+    if (j < nch) {
+        wait_vm<0>();
+        compute(j);
+    }
+
+    // segment sums: each wavefront's into its first chunk buffer, then
+    // wavefront 0 adds them in the two-level order
+    float* mine = reinterpret_cast<float*>(wbuf);
+    if (wave != 0) {
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    lds_store_f32(mine + ((c * MT + t) * 4 + jj) * kWave + lane, acc[c][t][jj]);
+    }
+    lds_barrier();
+    if (wave != 0) return;
+    f32x4 tot[C][MT] = {};
+    for (int w2 = 1; w2 < waves; ++w2) {
+        const float* other = reinterpret_cast<const float*>(ldsb + w2 * wave_bytes + a.m * xpitch * 2);
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const float* p = other + (c * MT + t) * 4 * kWave + lane;
+                fold_segment(acc[c][t], tot[c][t], f32x4{p[0], p[kWave], p[2 * kWave], p[3 * kWave]}, w2, a.group);
+            }
+    }
+    if (a.group < waves) {
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int t = 0; t < MT; ++t) acc[c][t] = tot[c][t] + acc[c][t];
+    }
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int n = col0 + 16 * c + col_lane;
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int m = 16 * t + 4 * kq + jj;
+                if (m < a.m && n < a.n) {
+                    float r = acc[c][t][jj] * a.t;
+                    if (OUT_F32)
+                        static_cast<float*>(a.y)[(int64_t)m * a.n + n] = r;
+                    else
+                        static_cast<uint16_t*>(a.y)[(int64_t)m * a.n + n] = f32_to_bf16_rne(r);
+                }
+            }
+    }
+}
+
+// LDS bytes of the per-tile kernel.
+size_t tile_lds_bytes(int64_t m, int64_t ks, int waves, int c, int nb) {
+    return size_t(waves) * (size_t(m) * (ks + 8) * 2 + size_t(nb) * c * kTileBytes);
+}
+
 // Many-row kernel (x too large to sit whole in one workgroup's LDS).  A
 // workgroup owns 16*C*W output columns (W wavefronts with C column tiles
 // each) and one segment group: K range [part * K/split, (part+1) * K/split),
@@ -900,6 +1032,22 @@ KernelFn pick_persistent(int mt, int c, int nb, int y_dtype) {
     return nb == 3 ? pick_p_c<3>(mt, c, y_dtype) : pick_p_c<2>(mt, c, y_dtype);
 }
 
+template <int C, int MT, int NB>
+KernelFn pick_t_out(int y_dtype) {
+    return y_dtype == NVFP4_OUT_F32 ? nvfp4_skinny_tile<C, MT, NB, true> : nvfp4_skinny_tile<C, MT, NB, false>;
+}
+
+template <int NB>
+KernelFn pick_t_c(int mt, int c, int y_dtype) {
+    if (mt == 1) return c == 1 ? pick_t_out<1, 1, NB>(y_dtype) : pick_t_out<2, 1, NB>(y_dtype);
+    return c == 1 ? pick_t_out<1, 2, NB>(y_dtype) : pick_t_out<2, 2, NB>(y_dtype);
+}
+
+// per-tile kernel; c: column tiles per wavefront (1 or 2); nb: chunk buffers (1..3)
+KernelFn pick_tile(int mt, int c, int nb, int y_dtype) {
+    return nb == 3 ? pick_t_c<3>(mt, c, y_dtype) : nb == 2 ? pick_t_c<2>(mt, c, y_dtype) : pick_t_c<1>(mt, c, y_dtype);
+}
+
 template <int C, int MT, int W>
 SplitFn pick_s_out(int y_dtype) {
     return y_dtype == NVFP4_OUT_F32 ? nvfp4_skinny_split<C, MT, W, true> : nvfp4_skinny_split<C, MT, W, false>;
@@ -959,6 +1107,9 @@ int init_device(int dev) {
             for (int c = 1; c <= 2; ++c)
                 for (int nb = 2; nb <= 3; ++nb)
                     if (!allow_full_lds(pick_persistent(mt, c, nb, od))) return NVFP4_ERR_HIP;
+            for (int c = 1; c <= 2; ++c)
+                for (int nb = 1; nb <= 3; ++nb)
+                    if (!allow_full_lds(pick_tile(mt, c, nb, od))) return NVFP4_ERR_HIP;
             for (int c = 1; c <= 2; ++c)
                 for (int w = 4; w <= 8; w += 4)
                     if (!allow_full_lds(pick_split(mt, c, w, od))) return NVFP4_ERR_HIP;
@@ -1023,7 +1174,9 @@ bool plan_split(const nvfp4::Tile& tile, int64_t m, int64_t n, int64_t k, const 
     const int64_t seg = k / tile.waves;
     if (seg % kChunkK != 0) return false;
     p->c = tile.cols == 16 ? 1 : 2;
-    p->w = tile.mwaves;
+    // mwaves 0: four wavefronts per workgroup up to 16 rows, eight above
+    // (measured on MI355X; never changes bits)
+    p->w = tile.mwaves != 0 ? tile.mwaves : m <= 16 ? 4 : 8;
     const int64_t cols = int64_t(16) * p->c * p->w;
     p->groups = (n + cols - 1) / cols;
     p->lds = split_lds_bytes(m, p->w, p->c);
@@ -1084,9 +1237,25 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
                          pers_bytes + 256 <= size_t(kMaxLdsBytes) && x_bytes <= size_t(64 * 1024);
     SplitPlan plan;
     const bool split_ok = plan_split(tile, m, n, k, d, &plan);
+    // The per-tile kernel: each wavefront's x slice and chunk buffers (up to
+    // three, at most one per chunk of its segment) within the LDS.
+    // The most chunk buffers (up to three, at most one per chunk of the
+    // segment) that fit.
+    const int64_t ks = k / tile.waves;
+    int tnb = int(std::min<int64_t>(3, std::max<int64_t>(1, ks / kChunkK)));
+    while (tnb > 1 && tile_lds_bytes(m, ks, tile.waves, pc, tnb) + 256 > size_t(kMaxLdsBytes)) --tnb;
+    const size_t tile_bytes = tile_lds_bytes(m, ks, tile.waves, pc, tnb);
+    const bool tile_ok = tile.cols <= 32 && ks % kChunkK == 0 && tile_bytes + 256 <= size_t(kMaxLdsBytes);
+    // Measured on MI355X: the per-tile kernel leads up to four rows (its
+    // workgroups are short and several share a CU), then the persistent one
+    // while x fits, then the many-row kernel.
     if (kernel == NVFP4_KERNEL_AUTO)
-        kernel = pers_ok ? NVFP4_KERNEL_PERSISTENT : split_ok ? NVFP4_KERNEL_SPLIT : NVFP4_KERNEL_TILE;
-    if ((kernel == NVFP4_KERNEL_PERSISTENT && !pers_ok) || (kernel == NVFP4_KERNEL_SPLIT && !split_ok))
+        kernel = tile_ok && m <= 4 ? NVFP4_KERNEL_TILE
+                 : pers_ok         ? NVFP4_KERNEL_PERSISTENT
+                 : split_ok        ? NVFP4_KERNEL_SPLIT
+                                   : NVFP4_KERNEL_GENERIC;
+    if ((kernel == NVFP4_KERNEL_PERSISTENT && !pers_ok) || (kernel == NVFP4_KERNEL_SPLIT && !split_ok) ||
+        (kernel == NVFP4_KERNEL_TILE && !tile_ok))
         return NVFP4_ERR_TILE;
 
     if (kernel == NVFP4_KERNEL_PERSISTENT) {
@@ -1111,11 +1280,14 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
         hipLaunchKernelGGL(pick_split(mt, plan.c, plan.w, y_dtype),
                            dim3(static_cast<unsigned>(plan.groups * tile.split)),
                            dim3(static_cast<unsigned>(kWave * plan.w)), plan.lds, hs, sa);
+    } else if (kernel == NVFP4_KERNEL_TILE) {
+        hipLaunchKernelGGL(pick_tile(mt, pc, tnb, y_dtype), dim3(static_cast<unsigned>((n + 16 * pc - 1) / (16 * pc))),
+                           dim3(static_cast<unsigned>(kWave * tile.waves)), tile_bytes, hs, a);
     } else {
-        // The per-tile kernel; x goes through LDS when it fits in 64 KB.
-        // With x fetched per chunk, one 128-k block per step keeps the A
-        // operands of two row tiles in registers (the pipeline depth never
-        // changes bits).
+        // The generic per-tile kernel (register loads, any shape); x goes
+        // through LDS when it fits in 64 KB.  With x fetched per chunk, one
+        // 128-k block per step keeps the A operands of two row tiles in
+        // registers (the pipeline depth never changes bits).
         const bool xlds = x_bytes <= size_t(64 * 1024);
         const size_t part_bytes = tile.waves > 1 ? size_t(tile.waves) * c * mt * 4 * kWave * sizeof(float) : 0;
         const size_t lds = xlds && x_bytes > part_bytes ? x_bytes : part_bytes;
@@ -1153,6 +1325,6 @@ extern "C" int nvfp4_linear_tiled(const void* x_bf16, const uint8_t* w_packed, c
     tile.split = t->split;
     tile.mwaves = t->mwaves;
     if (!nvfp4::tile_valid(tile, n, k)) return NVFP4_ERR_TILE;
-    if (t->kernel < NVFP4_KERNEL_AUTO || t->kernel > NVFP4_KERNEL_SPLIT) return NVFP4_ERR_TILE;
+    if (t->kernel < NVFP4_KERNEL_AUTO || t->kernel > NVFP4_KERNEL_GENERIC) return NVFP4_ERR_TILE;
     return launch(x_bf16, w_packed, scales_e4m3, tensor_scale, y, m, n, k, y_dtype, stream, tile, t->kernel);
 }

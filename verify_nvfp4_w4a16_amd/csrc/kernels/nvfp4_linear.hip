@@ -810,7 +810,7 @@ struct SplitArgs {
     int groups;           // column groups of 16*C*W
 };
 
-constexpr uint32_t kSpinLimit = 1u << 20;   // polls of a flag before giving up (~1 s)
+constexpr uint32_t kSpinLimit = 1u << 20;   // polls of a flag before giving up (about a second)
 constexpr int kXPitch = kChunkK + 8;        // LDS row pitch of an x window (bf16 elements)
 
 template <int C, int MT, int W, bool OUT_F32>
@@ -883,6 +883,8 @@ nvfp4_skinny_split(SplitArgs sa) {
     };
 
     // Window w is multiplied while window w + 1 (x and weights) is in flight.
+    // (Requesting windows 0 and 1 together measured slower: the second
+    // window's loads delay the first's.)
     issue_x(0);
     issue_w(0);
     wait_vm<0>();
@@ -929,7 +931,7 @@ nvfp4_skinny_split(SplitArgs sa) {
                     timed_out = 1;
                     break;
                 }
-                __builtin_amdgcn_s_sleep(8);
+                __builtin_amdgcn_s_sleep(1);
             }
         }
         __syncthreads();

@@ -163,3 +163,39 @@ def test_launch_settings_never_change_bits():
         assert nv.KERNEL_GENERIC in ran and nv.KERNEL_SPLIT in ran, (m, ran)
         if m <= 3:
             assert nv.KERNEL_TILE in ran and nv.KERNEL_PERSISTENT in ran, (m, ran)
+
+
+def _run_tiled(xd, w, m, tile, out_dtype=torch.bfloat16):
+    y = torch.empty((m, w.n), dtype=out_dtype, device=DEV)
+    st = nv.linear_tiled_raw(xd.data_ptr(), w.wp.data_ptr(), w.sc.data_ptr(), w.t, y.data_ptr(), m, w.n, w.k,
+                             nv.OUT_F32 if out_dtype == torch.float32 else nv.OUT_BF16, tile,
+                             torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return st, y
+
+
+def test_ragged_columns_every_kernel_and_split():
+    # N = 4136: the last column group of every kernel is partly past N (its
+    # loads repeat row N-1, its stores are skipped).  For each segment
+    # grouping (split 1, 2, 8; 8 crosses workgroups in the many-row kernel)
+    # every kernel that can run the shape gives the same bits, within the
+    # oracle's tolerance.
+    n, k = 4136, 4096
+    w = Weight.from_f32(workload.weights_f32(n, k, 91))
+    for split in (1, 2, 8):
+        base = nv.table_tile(n, k).replace(split=split)
+        for m in (1, 3, 17, 32):
+            x = workload.activations_bf16(m, k, 92 + m)
+            xd = upload_bits(x)
+            outs = {}
+            for kernel in (nv.KERNEL_TILE, nv.KERNEL_PERSISTENT, nv.KERNEL_SPLIT, nv.KERNEL_GENERIC):
+                st, y = _run_tiled(xd, w, m, base.replace(kernel=kernel))
+                if st == nv.ERR_TILE:
+                    continue
+                assert st == nv.OK
+                outs[kernel] = y
+            assert nv.KERNEL_SPLIT in outs and nv.KERNEL_GENERIC in outs
+            first = next(iter(outs.values()))
+            for kernel, y in outs.items():
+                assert torch.equal(bits(y), bits(first)), f"split={split} M={m} kernel {kernel}"
+            check_parity(first, x, w, label=f"ragged 4136x4096 split={split}")

@@ -165,6 +165,16 @@ def cpu_baseline(torch, dev, rnd: Round, graphs: dict, launches: dict, ms_list) 
             "seconds": total_s, "parity_max_err_over_tol": worst}
 
 
+def kernel_name(m: int) -> str:
+    """The kernel nvfp4_linear runs for the decode round's products at M rows
+    (the dispatch rule of the library: per-tile kernel up to 4 rows, else the
+    many-row kernel for these shapes, whose x does not fit one LDS)."""
+    if m <= 4:
+        return f"nvfp4_skinny_tile<1, 1, NB, bf16> (per-tile kernel, M={m} round)"
+    mt, w = (1, 4) if m <= 16 else (2, 8)
+    return f"nvfp4_skinny_split<1, {mt}, {w}, bf16> (many-row kernel, M={m} round)"
+
+
 def traffic_from_profile(per_launch_alg: float):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source."""
@@ -303,7 +313,7 @@ def main() -> int:
     traffic = traffic_from_profile(alg_per_launch)
     roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
-                "kernel": f"nvfp4_skinny (M={dom} round, {'2' if dom > 16 else '1'} A tile(s))",
+                "kernel": kernel_name(dom),
                 "alg_bytes_per_launch": alg_per_launch, "avg_launch_us": avg_launch_s * 1e6}
 
     base = None

@@ -221,10 +221,10 @@ def test_default_split_fills_the_chip():
 
 
 def test_builtin_table_entries():
-    # Sweep-picked splits of the decode round's products; all else default.
-    for n, k, split in [(8192, 4096, 4), (4096, 8192, 4), (24576, 4096, 1), (4096, 12288, 8)]:
+    # Sweep-picked segment counts and groupings of the decode round's products.
+    for n, k, waves, split in [(8192, 4096, 8, 4), (4096, 8192, 8, 4), (24576, 4096, 4, 1), (4096, 12288, 8, 8)]:
         t = nv.table_tile(n, k)
-        assert (t.cols, t.waves, t.split, t.mwaves) == (16, 8, split, 0), (n, k, t)
+        assert (t.cols, t.waves, t.split, t.mwaves) == (16, waves, split, 0), (n, k, t)
 
 
 def _tile_info_in_fresh_process(env_value, n=1024, k=1024):

@@ -20,21 +20,23 @@ using Key = std::pair<int64_t, int64_t>;
 Tile default_tile(int64_t n, int64_t k);
 
 // Built-in entries chosen by sweeping launch settings on MI355X (every
-// kernel at M = 1, 2, 8, 16, 32 over cold weights; the split that gave the
-// lowest times over those row counts).  Every entry's bits are the same at
-// every row count; entries differ from the default rule only in split.
+// kernel at M = 1, 2, 8, 16, 32 over cold weights; the segment count and
+// grouping that gave the lowest times over those row counts).  Every entry's
+// bits are the same at every row count; entries differ from the default rule
+// only in waves and split.
 const std::map<Key, Tile>& builtin_table() {
     static const std::map<Key, Tile> table = [] {
         std::map<Key, Tile> t;
-        auto add = [&](int64_t n, int64_t k, int split) {
+        auto add = [&](int64_t n, int64_t k, int waves, int split) {
             Tile x = default_tile(n, k);
+            x.waves = waves;
             x.split = split;
             t[{n, k}] = x;
         };
-        add(8192, 4096, 4);     // q/o-sized products of the decode round
-        add(4096, 8192, 4);
-        add(24576, 4096, 1);    // gate/up
-        add(4096, 12288, 8);    // down
+        add(8192, 4096, 8, 4);      // q/o-sized products of the decode round
+        add(4096, 8192, 8, 4);
+        add(24576, 4096, 4, 1);     // gate/up
+        add(4096, 12288, 8, 8);     // down
         return t;
     }();
     return table;

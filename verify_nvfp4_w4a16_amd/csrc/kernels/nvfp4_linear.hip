@@ -942,19 +942,34 @@ nvfp4_skinny_split(SplitArgs sa) {
             }
         }
         __syncthreads();
+        // The group sums are read in batches of parts, all loads of a batch
+        // in flight together (one round trip per batch, not per part); a
+        // batch past the last part re-reads that part (unused), so the loads
+        // need no branches.
+        constexpr int kVals = C * MT * 4;
+        constexpr int kBatch = 32 / kVals;
         f32x4 tot[C][MT] = {};
-        for (int q = 0; q < P - 1; ++q) {
-            const float* slot = work + (size_t)q * kSlot + base;
+        for (int q0 = 0; q0 < P - 1; q0 += kBatch) {
+            float v[kBatch][kVals];
 #pragma unroll
-            for (int c = 0; c < C; ++c)
+            for (int b = 0; b < kBatch; ++b) {
+                const float* slot = work + (size_t)min(q0 + b, P - 2) * kSlot + base;
 #pragma unroll
-                for (int t = 0; t < MT; ++t)
+                for (int i = 0; i < kVals; ++i)
+                    v[b][i] = __hip_atomic_load(slot + i * kWave, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float v = __hip_atomic_load(slot + ((c * MT + t) * 4 + j) * kWave,
-                                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        tot[c][t][j] = q == 0 ? v : tot[c][t][j] + v;
-                    }
+            for (int b = 0; b < kBatch; ++b)
+                if (q0 + b < P - 1)
+#pragma unroll
+                    for (int c = 0; c < C; ++c)
+#pragma unroll
+                        for (int t = 0; t < MT; ++t)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                const float g = v[b][(c * MT + t) * 4 + j];
+                                tot[c][t][j] = q0 + b == 0 ? g : tot[c][t][j] + g;
+                            }
         }
         const bool bad = timed_out != 0;
 #pragma unroll

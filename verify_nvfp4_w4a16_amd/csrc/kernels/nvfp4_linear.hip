@@ -403,6 +403,47 @@ __device__ __forceinline__ void lds_store_f32(float* p, float v) {
     asm volatile("ds_write_b32 %0, %1" : : "v"(addr), "v"(v) : "memory");
 }
 
+// 16-byte version of lds_store_f32 (p 16-byte aligned).
+__device__ __forceinline__ void lds_store_f32x4(float* p, f32x4 v) {
+    const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+    asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+
+// Folds the segment sums of wavefronts 1 .. waves-1 into wavefront 0's acc in
+// the two-level order.  Wavefront w's vector (c, t) of lane l is at
+// part(w) + 4 * ((c * MT + t) * 64 + l) (one 16-byte read); the reads of a
+// batch of wavefronts are issued together, then folded in wavefront order.
+template <int C, int MT, typename PartFn>
+__device__ __forceinline__ void fold_waves(f32x4 (&acc)[C][MT], PartFn part, int waves, int group, int lane) {
+    constexpr int kB = C * MT == 1 ? 7 : C * MT == 2 ? 4 : 2;
+    f32x4 tot[C][MT] = {};
+    for (int w0 = 1; w0 < waves; w0 += kB) {
+        f32x4 v[kB][C][MT];
+#pragma unroll
+        for (int i = 0; i < kB; ++i) {
+            const float* p = part(min(w0 + i, waves - 1));   // past the last: re-read, unused
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+                    v[i][c][t] = *reinterpret_cast<const f32x4*>(p + 4 * ((c * MT + t) * kWave + lane));
+        }
+#pragma unroll
+        for (int i = 0; i < kB; ++i)
+            if (w0 + i < waves)
+#pragma unroll
+                for (int c = 0; c < C; ++c)
+#pragma unroll
+                    for (int t = 0; t < MT; ++t) fold_segment(acc[c][t], tot[c][t], v[i][c][t], w0 + i, group);
+    }
+    if (group < waves) {
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int t = 0; t < MT; ++t) acc[c][t] = tot[c][t] + acc[c][t];
+    }
+}
+
 // Issues the loads of the chunk at byte `kb` of each row (k = 2 kb) of weight
 // rows row0 .. row0 + 15 (rows past nmax read row nmax, never used) into dst.
 __device__ __forceinline__ void issue_tile_chunk(uint8_t* dst, const uint8_t* wp, const uint8_t* sc, int row0,
@@ -569,31 +610,12 @@ nvfp4_skinny_persistent(Args a) {
                 for (int c = 0; c < C; ++c)
 #pragma unroll
                     for (int t = 0; t < MT; ++t)
-#pragma unroll
-                        for (int jj = 0; jj < 4; ++jj)
-                            lds_store_f32(buf + ((wave * C + c) * MT + t) * 4 * kWave + jj * kWave + lane,
-                                          acc[c][t][jj]);
+                        lds_store_f32x4(buf + 4 * (((wave * C + c) * MT + t) * kWave + lane), acc[c][t]);
             }
             lds_barrier();
         }
         if (wave == 0) {
-            f32x4 tot[C][MT] = {};
-            for (int w2 = 1; w2 < waves; ++w2) {
-#pragma unroll
-                for (int c = 0; c < C; ++c)
-#pragma unroll
-                    for (int t = 0; t < MT; ++t) {
-                        const float* p = buf + ((w2 * C + c) * MT + t) * 4 * kWave + lane;
-                        fold_segment(acc[c][t], tot[c][t], f32x4{p[0], p[kWave], p[2 * kWave], p[3 * kWave]}, w2,
-                                     a.group);
-                    }
-            }
-            if (a.group < waves) {
-#pragma unroll
-                for (int c = 0; c < C; ++c)
-#pragma unroll
-                    for (int t = 0; t < MT; ++t) acc[c][t] = tot[c][t] + acc[c][t];
-            }
+            fold_waves<C, MT>(acc, [&](int w2) { return buf + 4 * w2 * C * MT * kWave; }, waves, a.group, lane);
 #pragma unroll
             for (int c = 0; c < C; ++c) {
                 const int n = tile * 16 * C + 16 * c + col_lane;
@@ -730,30 +752,13 @@ nvfp4_skinny_tile(Args a) {
 #pragma unroll
         for (int c = 0; c < C; ++c)
 #pragma unroll
-            for (int t = 0; t < MT; ++t)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-                    lds_store_f32(mine + ((c * MT + t) * 4 + jj) * kWave + lane, acc[c][t][jj]);
+            for (int t = 0; t < MT; ++t) lds_store_f32x4(mine + 4 * ((c * MT + t) * kWave + lane), acc[c][t]);
     }
     lds_barrier();
     if (wave != 0) return;
-    f32x4 tot[C][MT] = {};
-    for (int w2 = 1; w2 < waves; ++w2) {
-        const float* other = reinterpret_cast<const float*>(ldsb + w2 * wave_bytes + a.m * xpitch * 2);
-#pragma unroll
-        for (int c = 0; c < C; ++c)
-#pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                const float* p = other + (c * MT + t) * 4 * kWave + lane;
-                fold_segment(acc[c][t], tot[c][t], f32x4{p[0], p[kWave], p[2 * kWave], p[3 * kWave]}, w2, a.group);
-            }
-    }
-    if (a.group < waves) {
-#pragma unroll
-        for (int c = 0; c < C; ++c)
-#pragma unroll
-            for (int t = 0; t < MT; ++t) acc[c][t] = tot[c][t] + acc[c][t];
-    }
+    fold_waves<C, MT>(
+        acc, [&](int w2) { return reinterpret_cast<const float*>(ldsb + w2 * wave_bytes + a.m * xpitch * 2); },
+        waves, a.group, lane);
 #pragma unroll
     for (int c = 0; c < C; ++c) {
         const int n = col0 + 16 * c + col_lane;

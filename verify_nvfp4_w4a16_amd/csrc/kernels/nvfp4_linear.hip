@@ -417,6 +417,7 @@ template <int C, int MT, typename PartFn>
 __device__ __forceinline__ void fold_waves(f32x4 (&acc)[C][MT], PartFn part, int waves, int group, int lane) {
     constexpr int kB = C * MT == 1 ? 7 : C * MT == 2 ? 4 : 2;
     f32x4 tot[C][MT] = {};
+    int pos = group == 1 ? 0 : 1;        // position of segment w0 in its group
     for (int w0 = 1; w0 < waves; w0 += kB) {
         f32x4 v[kB][C][MT];
 #pragma unroll
@@ -428,13 +429,35 @@ __device__ __forceinline__ void fold_waves(f32x4 (&acc)[C][MT], PartFn part, int
                 for (int t = 0; t < MT; ++t)
                     v[i][c][t] = *reinterpret_cast<const f32x4*>(p + 4 * ((c * MT + t) * kWave + lane));
         }
+        // The fold decisions are wavefront-uniform: scalar branches and a
+        // running position in the group keep this serial tail short.
 #pragma unroll
-        for (int i = 0; i < kB; ++i)
-            if (w0 + i < waves)
+        for (int i = 0; i < kB; ++i) {
+            if (w0 + i >= waves) break;
+            if (pos == 0) {                                   // segment w0 + i starts a group
+                if (w0 + i == group) {
+#pragma unroll
+                    for (int c = 0; c < C; ++c)
+#pragma unroll
+                        for (int t = 0; t < MT; ++t) tot[c][t] = acc[c][t];
+                } else {
+#pragma unroll
+                    for (int c = 0; c < C; ++c)
+#pragma unroll
+                        for (int t = 0; t < MT; ++t) tot[c][t] = tot[c][t] + acc[c][t];
+                }
 #pragma unroll
                 for (int c = 0; c < C; ++c)
 #pragma unroll
-                    for (int t = 0; t < MT; ++t) fold_segment(acc[c][t], tot[c][t], v[i][c][t], w0 + i, group);
+                    for (int t = 0; t < MT; ++t) acc[c][t] = v[i][c][t];
+            } else {
+#pragma unroll
+                for (int c = 0; c < C; ++c)
+#pragma unroll
+                    for (int t = 0; t < MT; ++t) acc[c][t] = acc[c][t] + v[i][c][t];
+            }
+            pos = pos + 1 == group ? 0 : pos + 1;
+        }
     }
     if (group < waves) {
 #pragma unroll

@@ -172,7 +172,8 @@ def kernel_name(m: int) -> str:
     if m <= 4:
         return f"nvfp4_skinny_tile<1, 1, NB, bf16> (per-tile kernel, M={m} round)"
     mt, w = (1, 4) if m <= 16 else (2, 8)
-    return f"nvfp4_skinny_split<1, {mt}, {w}, bf16> (many-row kernel, M={m} round)"
+    return (f"nvfp4_skinny_split<1, {mt}, W, bf16> (many-row kernel, M={m} round; "
+            f"W = 6 for the 24576-column product, {w} for the others)")
 
 
 def traffic_from_profile(per_launch_alg: float):

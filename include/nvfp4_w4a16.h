@@ -161,7 +161,7 @@ typedef struct nvfp4_tile {
     int waves;  /* K segments, 1..8 (wavefronts per workgroup of the one-group kernels) */
     int unroll; /* 128-k blocks per pipeline step: 1, 2 or 4; K % (128 * unroll * waves) == 0 */
     int split;  /* segment groups: 1, 2, 4 or 8, dividing waves */
-    int mwaves; /* wavefronts per workgroup of the many-row kernel: 4 or 8; 0 = by M (4 up to 16 rows) */
+    int mwaves; /* wavefronts per workgroup of the many-row kernel: 4, 6 or 8; 0 = by M (4 up to 16 rows) */
     int kernel; /* NVFP4_KERNEL_*; ignored by the (N, K) table */
 } nvfp4_tile_t;
 

@@ -168,7 +168,7 @@ def test_tiled_entry_validates_the_tile():
     assert call(16, 16, 1, k=8192) == nv.ERR_TILE    # more than 8 wavefronts
     assert call(16, 4, 2, split=3) == nv.ERR_TILE    # split not a power of two
     assert call(16, 2, 2, split=4) == nv.ERR_TILE    # more groups than segments
-    assert call(16, 4, 2, mwaves=2) == nv.ERR_TILE   # many-row workgroups are 4 or 8 wavefronts
+    assert call(16, 4, 2, mwaves=2) == nv.ERR_TILE   # many-row workgroups are 4, 6 or 8 wavefronts
     assert call(16, 4, 2, kernel=5) == nv.ERR_TILE   # no such kernel
     assert call(16, 4, 2, kernel=-1) == nv.ERR_TILE
     assert call(16, 2, 2, k=100) == nv.ERR_SHAPE
@@ -204,7 +204,7 @@ def test_tile_info_depends_on_shape_only():
         assert f"N={n} K={k}" in info
         assert info == nv.tile_info(n, k)
         t = nv.table_tile(n, k)
-        assert t.waves % t.split == 0 and t.mwaves in (0, 4, 8)
+        assert t.waves % t.split == 0 and t.mwaves in (0, 4, 6, 8)
     with pytest.raises(nv.Nvfp4Error):
         nv.tile_info(16, 100)
     buf = ctypes.create_string_buffer(8)
@@ -222,9 +222,10 @@ def test_default_split_fills_the_chip():
 
 def test_builtin_table_entries():
     # Sweep-picked segment counts and groupings of the decode round's products.
-    for n, k, waves, split in [(8192, 4096, 8, 4), (4096, 8192, 8, 4), (24576, 4096, 4, 1), (4096, 12288, 8, 8)]:
+    for n, k, waves, split, mwaves in [(8192, 4096, 8, 4, 0), (4096, 8192, 8, 4, 0), (24576, 4096, 4, 1, 6),
+                                       (4096, 12288, 8, 8, 0)]:
         t = nv.table_tile(n, k)
-        assert (t.cols, t.waves, t.split, t.mwaves) == (16, waves, split, 0), (n, k, t)
+        assert (t.cols, t.waves, t.split, t.mwaves) == (16, waves, split, mwaves), (n, k, t)
 
 
 def _tile_info_in_fresh_process(env_value, n=1024, k=1024):
@@ -252,7 +253,7 @@ def test_tile_override_file(tmp_path):
     f.write_text("1024 1024 32 4 2 4 4  # comment\n")
     assert "cols=32 waves=4 unroll=2 split=4 mwaves=4" in _tile_info_in_fresh_process(str(f))
     for bad in ("1024 1024 32 4 2 8\n",          # more groups than segments
-                "1024 1024 32 4 2 2 6\n",        # mwaves not 4 or 8
+                "1024 1024 32 4 2 2 5\n",        # mwaves not 4, 6 or 8
                 "1024 1024 32 4 2 2 8 1\n",      # too many fields
                 "1024 1024 32 4\n",              # too few
                 "1024 1024 32 4 2x\n",           # not an integer

@@ -146,7 +146,7 @@ def test_launch_settings_never_change_bits():
         for kernel in (nv.KERNEL_PERSISTENT, nv.KERNEL_TILE, nv.KERNEL_SPLIT, nv.KERNEL_GENERIC):
             for cols in (16, 32, 64):
                 for unroll in (1, 2, 4):
-                    for mwaves in (4, 8):
+                    for mwaves in (4, 6, 8):
                         if s.k % (128 * unroll * base.waves):
                             continue
                         tile = base.replace(cols=cols, unroll=unroll, mwaves=mwaves, kernel=kernel)

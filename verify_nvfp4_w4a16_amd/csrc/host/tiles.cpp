@@ -23,20 +23,21 @@ Tile default_tile(int64_t n, int64_t k);
 // kernel at M = 1, 2, 8, 16, 32 over cold weights; the segment count and
 // grouping that gave the lowest times over those row counts).  Every entry's
 // bits are the same at every row count; entries differ from the default rule
-// only in waves and split.
+// only in waves and split (which set the bits) and mwaves (which does not).
 const std::map<Key, Tile>& builtin_table() {
     static const std::map<Key, Tile> table = [] {
         std::map<Key, Tile> t;
-        auto add = [&](int64_t n, int64_t k, int waves, int split) {
+        auto add = [&](int64_t n, int64_t k, int waves, int split, int mwaves) {
             Tile x = default_tile(n, k);
             x.waves = waves;
             x.split = split;
+            x.mwaves = mwaves;
             t[{n, k}] = x;
         };
-        add(8192, 4096, 8, 4);      // q/o-sized products of the decode round
-        add(4096, 8192, 8, 4);
-        add(24576, 4096, 4, 1);     // gate/up
-        add(4096, 12288, 8, 8);     // down
+        add(8192, 4096, 8, 4, 0);      // q/o-sized products of the decode round
+        add(4096, 8192, 8, 4, 0);
+        add(24576, 4096, 4, 1, 6);     // gate/up: 96 columns per many-row workgroup, one per CU
+        add(4096, 12288, 8, 8, 0);     // down
         return t;
     }();
     return table;
@@ -80,7 +81,7 @@ bool tile_valid(const Tile& t, int64_t /*n*/, int64_t k) {
     if (k % (int64_t(128) * t.unroll * t.waves) != 0) return false;
     if (t.split != 1 && t.split != 2 && t.split != 4 && t.split != 8) return false;
     if (t.split > t.waves || t.waves % t.split != 0) return false;
-    if (t.mwaves != 0 && t.mwaves != 4 && t.mwaves != 8) return false;
+    if (t.mwaves != 0 && t.mwaves != 4 && t.mwaves != 6 && t.mwaves != 8) return false;
     return true;
 }
 

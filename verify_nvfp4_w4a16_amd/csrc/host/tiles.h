@@ -12,7 +12,7 @@
 //   split  - groups of consecutive segments (1, 2, 4 or 8, dividing waves):
 //           an output is the sum, in group order, of its group sums, each
 //           the sum of the group's segment chains in segment order;
-//   mwaves - wavefronts per workgroup of the many-row kernel (4 or 8, or 0:
+//   mwaves - wavefronts per workgroup of the many-row kernel (4, 6 or 8, or 0:
 //           chosen by the row count), which runs one segment group per
 //           workgroup.
 // Only `waves` and `split` enter the arithmetic of an output (how K is cut
@@ -29,12 +29,12 @@ struct Tile {
     int waves = 8;   // K segments (wavefronts per workgroup of the one-group kernels), 1..8
     int unroll = 2;  // 128-k blocks per pipeline step: 1, 2 or 4
     int split = 1;   // segment groups: 1, 2, 4 or 8, dividing waves
-    int mwaves = 0;  // wavefronts per workgroup of the many-row kernel: 4, 8 or 0 (by row count)
+    int mwaves = 0;  // wavefronts per workgroup of the many-row kernel: 4, 6, 8 or 0 (by row count)
 };
 
 // Checks a tile against a shape: cols in {16, 32, 64}; waves in 1..8;
 // unroll in {1, 2, 4}; each segment K / waves a whole number of unroll * 128 k;
-// split in {1, 2, 4, 8} dividing waves; mwaves in {0, 4, 8}.
+// split in {1, 2, 4, 8} dividing waves; mwaves in {0, 4, 6, 8}.
 bool tile_valid(const Tile& t, int64_t n, int64_t k);
 
 // Segment groups the default rule picks for N output columns: enough

@@ -1107,11 +1107,12 @@ SplitFn pick_s_out(int y_dtype) {
 
 template <int MT>
 SplitFn pick_s_w(int c, int w, int y_dtype) {
-    if (c == 1) return w == 4 ? pick_s_out<1, MT, 4>(y_dtype) : pick_s_out<1, MT, 8>(y_dtype);
-    return w == 4 ? pick_s_out<2, MT, 4>(y_dtype) : pick_s_out<2, MT, 8>(y_dtype);
+    if (c == 1)
+        return w == 4 ? pick_s_out<1, MT, 4>(y_dtype) : w == 6 ? pick_s_out<1, MT, 6>(y_dtype) : pick_s_out<1, MT, 8>(y_dtype);
+    return w == 4 ? pick_s_out<2, MT, 4>(y_dtype) : w == 6 ? pick_s_out<2, MT, 6>(y_dtype) : pick_s_out<2, MT, 8>(y_dtype);
 }
 
-// c: column tiles per wavefront (1 or 2), w: wavefronts per workgroup (4 or 8)
+// c: column tiles per wavefront (1 or 2), w: wavefronts per workgroup (4, 6 or 8)
 SplitFn pick_split(int mt, int c, int w, int y_dtype) {
     return mt == 1 ? pick_s_w<1>(c, w, y_dtype) : pick_s_w<2>(c, w, y_dtype);
 }
@@ -1163,7 +1164,7 @@ int init_device(int dev) {
                 for (int nb = 1; nb <= 3; ++nb)
                     if (!allow_full_lds(pick_tile(mt, c, nb, od))) return NVFP4_ERR_HIP;
             for (int c = 1; c <= 2; ++c)
-                for (int w = 4; w <= 8; w += 4)
+                for (int w = 4; w <= 8; w += 2)
                     if (!allow_full_lds(pick_split(mt, c, w, od))) return NVFP4_ERR_HIP;
         }
     // Workspace of the many-row kernel.  Without it that kernel runs only
@@ -1227,7 +1228,7 @@ bool plan_split(const nvfp4::Tile& tile, int64_t m, int64_t n, int64_t k, const 
     if (seg % kChunkK != 0) return false;
     p->c = tile.cols == 16 ? 1 : 2;
     // mwaves 0: four wavefronts per workgroup up to 16 rows, eight above
-    // (measured on MI355X; never changes bits)
+    // (measured on MI355X; never changes bits; six suits N = 96 * 256)
     p->w = tile.mwaves != 0 ? tile.mwaves : m <= 16 ? 4 : 8;
     const int64_t cols = int64_t(16) * p->c * p->w;
     p->groups = (n + cols - 1) / cols;

@@ -171,9 +171,11 @@ def kernel_name(m: int) -> str:
     many-row kernel for these shapes, whose x does not fit one LDS)."""
     if m <= 4:
         return f"nvfp4_skinny_tile<1, 1, NB, bf16> (per-tile kernel, M={m} round)"
-    mt, w = (1, 4) if m <= 16 else (2, 8)
-    return (f"nvfp4_skinny_split<1, {mt}, W, bf16> (many-row kernel, M={m} round; "
-            f"W = 6 for the 24576-column product, {w} for the others)")
+    if m <= 16:
+        return (f"nvfp4_skinny_split<1, 1, W, bf16> (many-row kernel, M={m} round; "
+                f"W = 6 for the 24576-column product, 4 for the others)")
+    return (f"nvfp4_skinny_split<1, 2, W, bf16> (many-row kernel, M={m} round; "
+            f"W = 6 for the 24576-column product, 4 for the 4096x8192 one, 8 for the others)")
 
 
 def traffic_from_profile(per_launch_alg: float):

@@ -11,9 +11,11 @@
 // converter):
 //  * Weights are the B operand of v_mfma_f32_16x16x32_bf16: lane l owns weight
 //    row (output column) l % 16 and, per instruction, 8 consecutive k of it.
-//    One 16-byte load per lane brings 32 k of one row (4 instructions' worth);
-//    the 4 lanes that share a row read 64 contiguous bytes.  Weights never
-//    pass through LDS.
+//    A lane's 16-byte operand piece holds 32 k of one row (4 instructions'
+//    worth).  The streaming kernels bring weights into LDS with direct-to-LDS
+//    loads that read 4 rows x 256 contiguous bytes each (an XOR swizzle keeps
+//    the 16 rows of one operand read in different bank groups); the generic
+//    kernel loads the pieces straight into registers.
 //  * Decode is in registers: v_cvt_scalef32_pk_f32_fp4 turns one packed byte
 //    into two fp32 e2m1 values (its scale operand contributes only an
 //    exponent, so it is given 1.0), a multiply by the group's e4m3 scale
@@ -22,12 +24,16 @@
 //    operand.  e2m1 times e4m3 has at most 6 significant bits, so the bf16
 //    weight is exact ("10 Kernels", 10.2, makes the same point for fp16).
 //  * Activations are the A operand: 16 rows per instruction, one 16-row tile
-//    for M <= 16 and two for 17..32; rows >= M are zero.
+//    for M <= 16 and two for 17..32; rows >= M repeat row M - 1 and are never
+//    stored.
 //  * Every M, including M = 1, runs the same instruction sequence on each
-//    output element: the K order is fixed by the (N, K) tile, wavefront
-//    partials are added in wavefront order through LDS, and nothing uses
-//    atomics ("10 Kernels", 10.1).  The M = 1 entry is a GEMV-shaped
-//    instantiation (one A tile, x fetched straight into registers).
+//    output element: the K order is fixed by the (N, K) tile (segments, each
+//    one MFMA chain in increasing k, added in a fixed two-level order), and
+//    nothing uses atomics ("10 Kernels", 10.1).  The kernels differ only in
+//    how work and data are laid over the machine: one workgroup per column
+//    tile (few rows), persistent workgroups walking the tiles, many-row
+//    workgroups sharing x windows (their segment groups meet through device
+//    memory), and a generic register-load kernel for any shape.
 //  * Epilogue: fp32 sum times t, one round-to-nearest-even to bf16, or fp32.
 #include <hip/hip_runtime.h>
 

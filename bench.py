@@ -46,8 +46,12 @@ def cpu_budget() -> int:
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """SHA-256 prefix of the kernel source with its comment lines and blank
+    lines removed, so a counter profile stays attached to the code it
+    measured across comment-only edits."""
+    with open(KERNEL_SOURCE, encoding="utf-8") as f:
+        code = [ln.rstrip() for ln in f if ln.strip() and not ln.lstrip().startswith("//")]
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
 class Round:

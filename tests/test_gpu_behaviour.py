@@ -84,3 +84,45 @@ def test_binding_rejects_bad_arguments(weight):
         nv.linear(x[:2].float(), weight.wp, weight.sc, weight.t)
     with pytest.raises(ValueError):
         nv.linear(x[:2], weight.wp[:, :-16], weight.sc, weight.t)
+
+
+def test_subnormal_inputs_and_products_recorded():
+    # bf16 subnormal activations and fp32-subnormal products: measured on
+    # MI355X, the bf16 MFMA keeps both exactly (no flush to zero); this pins
+    # that, and that every kernel and every row count give the same bits.
+    n, k = 16, 4096
+    packed = np.zeros((n, k // 2), dtype=np.uint8)
+    scales = np.full((n, k // 16), 0x38, dtype=np.uint8)
+    packed[3, 5 // 2] = 0x7 << 4            # (n=3, k=5): code 7 = 6.0, high nibble (odd k)
+    scales[3, 0] = 0x7E                      # 448: Wd[3, 5] = 2688
+    packed[4, 7 // 2] = 0x1 << 4             # (n=4, k=7): code 1 = 0.5
+    scales[4, 0] = 0x01                      # 2^-9: Wd[4, 7] = 2^-10
+    w = Weight(packed, scales, 1.0)
+    x = np.zeros((2, k), dtype=np.uint16)
+    x[0, 5] = 0x0008                         # 2^-130, a bf16 subnormal
+    x[0, 7] = 0x0080                         # 2^-126, the smallest normal bf16
+    x[1, 5] = 0x0080
+    x[1, 7] = 0x3F80                         # 1.0
+    y = run(x, w, torch.float32).cpu().numpy().astype(np.float64)
+    assert y[1, 3] == 2688.0 * 2.0 ** -126 and y[1, 4] == 2.0 ** -10
+    sub_x, sub_p = y[0, 3], y[0, 4]
+    assert sub_x in (0.0, 2688.0 * 2.0 ** -130), sub_x
+    assert sub_p in (0.0, 2.0 ** -136), sub_p
+    print(f"[subnormal] bf16 subnormal x: {'kept' if sub_x else 'flushed'}; "
+          f"fp32-subnormal product: {'kept' if sub_p else 'flushed'}", flush=True)
+    assert sub_x and sub_p
+    assert not np.delete(y, [3, 4], axis=1).any()
+    # same bits for one row alone and through every kernel
+    ref = bits(run(x, w, torch.float32)).clone()
+    assert torch.equal(bits(run(x[:1], w, torch.float32)), ref[:1])
+    xt = upload_bits(x)
+    for kernel in (nv.KERNEL_PERSISTENT, nv.KERNEL_TILE, nv.KERNEL_SPLIT, nv.KERNEL_GENERIC):
+        yk = torch.empty((2, n), dtype=torch.float32, device=DEV)
+        st = nv.linear_tiled_raw(xt.data_ptr(), w.wp.data_ptr(), w.sc.data_ptr(), w.t, yk.data_ptr(), 2, n, k,
+                                 nv.OUT_F32, nv.table_tile(n, k).replace(kernel=kernel),
+                                 torch.cuda.current_stream().cuda_stream)
+        if st == nv.ERR_TILE:
+            continue
+        assert st == nv.OK
+        torch.cuda.synchronize()
+        assert torch.equal(bits(yk), ref), kernel

@@ -179,7 +179,7 @@ def kernel_name(m: int) -> str:
         return (f"nvfp4_skinny_split<1, 1, W, bf16> (many-row kernel, M={m} round; "
                 f"W = 6 for the 24576-column product, 4 for the others)")
     return (f"nvfp4_skinny_split<1, 2, W, bf16> (many-row kernel, M={m} round; "
-            f"W = 6 for the 24576-column product, 4 for the 4096x8192 one, 8 for the others)")
+            f"W = 6 for the 24576-column product, 8 for the others)")
 
 
 def traffic_from_profile(per_launch_alg: float):

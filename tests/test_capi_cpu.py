@@ -222,7 +222,7 @@ def test_default_split_fills_the_chip():
 
 def test_builtin_table_entries():
     # Sweep-picked segment counts and groupings of the decode round's products.
-    for n, k, waves, split, mwaves in [(8192, 4096, 8, 4, 0), (4096, 8192, 8, 4, 4), (24576, 4096, 4, 1, 6),
+    for n, k, waves, split, mwaves in [(8192, 4096, 8, 4, 0), (4096, 8192, 8, 8, 0), (24576, 4096, 4, 1, 6),
                                        (4096, 12288, 8, 8, 0)]:
         t = nv.table_tile(n, k)
         assert (t.cols, t.waves, t.split, t.mwaves) == (16, waves, split, mwaves), (n, k, t)

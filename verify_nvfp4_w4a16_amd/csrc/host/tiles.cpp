@@ -35,7 +35,7 @@ const std::map<Key, Tile>& builtin_table() {
             t[{n, k}] = x;
         };
         add(8192, 4096, 8, 4, 0);      // q/o-sized products of the decode round
-        add(4096, 8192, 8, 4, 4);      // four-wavefront many-row workgroups: 256 of them at any M
+        add(4096, 8192, 8, 8, 0);
         add(24576, 4096, 4, 1, 6);     // gate/up: 96 columns per many-row workgroup, one per CU
         add(4096, 12288, 8, 8, 0);     // down
         return t;

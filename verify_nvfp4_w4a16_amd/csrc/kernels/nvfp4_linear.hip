@@ -399,17 +399,12 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// Stores v to LDS at p through an instruction the compiler does not track:
-// a plain LDS store issued while direct-to-LDS loads are in flight makes the
-// compiler wait for every outstanding load first (it may alias their
-// destinations), which would empty the weight pipeline.  Callers order it
-// with lds_barrier, which waits for all LDS operations of the wavefront.
-__device__ __forceinline__ void lds_store_f32(float* p, float v) {
-    const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
-    asm volatile("ds_write_b32 %0, %1" : : "v"(addr), "v"(v) : "memory");
-}
-
-// 16-byte version of lds_store_f32 (p 16-byte aligned).
+// Stores v to LDS at p (16-byte aligned) through an instruction the compiler
+// does not track: a plain LDS store issued while direct-to-LDS loads are in
+// flight makes the compiler wait for every outstanding load first (it may
+// alias their destinations), which would empty the weight pipeline.  Callers
+// order it with lds_barrier, which waits for all LDS operations of the
+// wavefront.
 __device__ __forceinline__ void lds_store_f32x4(float* p, f32x4 v) {
     const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
     asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(v) : "memory");

@@ -105,6 +105,9 @@ int nvfp4_linear_shape_ok(int64_t m, int64_t n, int64_t k);
  * graph; the first nvfp4_linear call on a device runs it otherwise.  Safe to
  * call more than once.  If the workspace cannot be allocated, nvfp4_linear
  * still works (with kernels that do not need it) and gives the same bits.
+ * Test hook, read here once per process: NVFP4_TEST_SPLIT_TIMEOUT=1 makes the
+ * many-row kernel's producer workgroups skip their flags and its consumers
+ * give up after a few polls, so tests can check that a time-out writes NaN.
  * Errors: HIP, DEVICE, TILEFILE.
  */
 int nvfp4_init(void);

@@ -126,3 +126,39 @@ def test_subnormal_inputs_and_products_recorded():
         assert st == nv.OK
         torch.cuda.synchronize()
         assert torch.equal(bits(yk), ref), kernel
+
+
+_TIMEOUT_CHILD = r"""
+import numpy as np, torch
+import verify_nvfp4_w4a16_amd as nv
+import workload
+n, k = 4096, 8192                          # split > 1: the many-row kernel's parts meet through flags
+w = workload.weights_f32(n, k, 5)
+packed, scales, t = nv.pack(w)
+dev = torch.device("cuda:0")
+wp, sc = torch.from_numpy(packed).to(dev), torch.from_numpy(scales).to(dev)
+assert nv.table_tile(n, k).split > 1
+for m, expect_nan in ((17, True), (32, True), (1, False)):
+    xb = workload.activations_bf16(m, k, 6 + m)
+    x = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
+    y = nv.linear(x, wp, sc, t, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    nan = torch.isnan(y)
+    assert bool(nan.all()) if expect_nan else not bool(nan.any()), (m, int(nan.sum()))
+print("timeout path ok", flush=True)
+"""
+
+
+def test_many_row_time_out_writes_nan():
+    # NVFP4_TEST_SPLIT_TIMEOUT=1 (read once per process): the producers of the
+    # many-row kernel set no flags and the consumers give up after a few
+    # polls; every output of the product must then be NaN rather than a
+    # hang or a partial sum.  The per-tile kernel (M = 1) has no exchange.
+    import os, subprocess, sys
+    env = dict(os.environ, NVFP4_TEST_SPLIT_TIMEOUT="1")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env["PYTHONPATH"] = root + os.pathsep + os.path.join(root, "tests") + os.pathsep + env.get("PYTHONPATH", "")
+    r = subprocess.run([sys.executable, "-c", _TIMEOUT_CHILD], env=env, cwd=root, capture_output=True, text=True,
+                       timeout=300)
+    print(r.stdout[-2000:], r.stderr[-2000:], flush=True)
+    assert r.returncode == 0 and "timeout path ok" in r.stdout

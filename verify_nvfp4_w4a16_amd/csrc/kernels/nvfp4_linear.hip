@@ -39,6 +39,7 @@
 
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <algorithm>
 #include <atomic>
@@ -837,9 +838,12 @@ struct SplitArgs {
     uint32_t epoch;
     int split;
     int groups;           // column groups of 16*C*W
+    uint32_t spin_limit;  // polls of a flag before giving up
+    int drop_flags;       // test hook: producers set no flag, so the consumer times out
 };
 
 constexpr uint32_t kSpinLimit = 1u << 20;   // polls of a flag before giving up (about a second)
+constexpr uint32_t kTestSpinLimit = 64;     // with the NVFP4_TEST_SPLIT_TIMEOUT hook
 constexpr int kXPitch = kChunkK + 8;        // LDS row pitch of an x window (bf16 elements)
 
 template <int C, int MT, int W, bool OUT_F32>
@@ -947,7 +951,8 @@ nvfp4_skinny_split(SplitArgs sa) {
             // every store of the workgroup has completed before the flag is set
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            if (threadIdx.x == 0) __hip_atomic_store(flags + part, sa.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (threadIdx.x == 0 && !sa.drop_flags)
+                __hip_atomic_store(flags + part, sa.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             return;
         }
         __shared__ uint32_t timed_out;
@@ -962,7 +967,7 @@ nvfp4_skinny_split(SplitArgs sa) {
             for (uint32_t spins = 0;; ++spins) {
                 const uint32_t next = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 if (prev == sa.epoch) break;
-                if (spins >= kSpinLimit) {
+                if (spins >= sa.spin_limit) {
                     timed_out = 1;
                     break;
                 }
@@ -1185,6 +1190,11 @@ int init_device(int dev) {
 
 std::once_flag g_init_once;
 int g_init_status = NVFP4_OK;
+// Test hook, read once per process: with NVFP4_TEST_SPLIT_TIMEOUT=1 the
+// many-row kernel's producers set no flags and its consumers give up after a
+// few polls, so a test can see the time-out path write NaN (every kernel
+// still exits normally).
+bool g_test_split_timeout = false;
 
 int current_device(int* dev) {
     if (hipGetDevice(dev) != hipSuccess) return NVFP4_ERR_HIP;
@@ -1195,7 +1205,11 @@ int current_device(int* dev) {
 }  // namespace
 
 extern "C" int nvfp4_init(void) {
-    std::call_once(g_init_once, [] { g_init_status = nvfp4::load_tile_override(); });
+    std::call_once(g_init_once, [] {
+        const char* hook = std::getenv("NVFP4_TEST_SPLIT_TIMEOUT");
+        g_test_split_timeout = hook && std::strcmp(hook, "1") == 0;
+        g_init_status = nvfp4::load_tile_override();
+    });
     if (g_init_status != NVFP4_OK) return g_init_status;
     int dev = 0;
     int st = current_device(&dev);
@@ -1326,6 +1340,8 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
         sa.work = d.work;
         sa.flags = d.flags;
         sa.split = tile.split;
+        sa.spin_limit = g_test_split_timeout ? kTestSpinLimit : kSpinLimit;
+        sa.drop_flags = g_test_split_timeout ? 1 : 0;
         sa.groups = static_cast<int>(plan.groups);
         DeviceState& dm = g_dev[dev];
         uint32_t e = dm.epoch.fetch_add(1, std::memory_order_relaxed) + 1;

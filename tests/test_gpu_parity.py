@@ -199,3 +199,42 @@ def test_ragged_columns_every_kernel_and_split():
             for kernel, y in outs.items():
                 assert torch.equal(bits(y), bits(first)), f"split={split} M={m} kernel {kernel}"
             check_parity(first, x, w, label=f"ragged 4136x4096 split={split}")
+
+
+def test_exhaustive_decode_every_code_and_scale_byte():
+    # One-hot activations pick single weights, so y[m, n] = E2M1[m] * E4M3[n]
+    # exactly (t = 1, fp32 output): all 16 e2m1 codes against all 256 scale
+    # bytes (negative ones decoded literally, 0x7F/0xFF give NaN), through
+    # every kernel that can run the shape.  Zeros compare as values (a -0
+    # product lands in a +0 accumulator).
+    from oracle.formats import E2M1, E4M3
+    n, k = 256, 4096
+    packed = np.zeros((n, k // 2), dtype=np.uint8)
+    for j in range(8):
+        packed[:, j] = (2 * j) | ((2 * j + 1) << 4)      # k = 0..15 hold codes 0..15
+    scales = np.zeros((n, k // 16), dtype=np.uint8)
+    scales[:, 0] = np.arange(256, dtype=np.uint8)
+    w = Weight(packed, scales, 1.0)
+    x = np.zeros((16, k), dtype=np.uint16)
+    x[np.arange(16), np.arange(16)] = 0x3F80             # x[m, m] = 1.0
+    expect = (E2M1[:, None] * E4M3[None, :]).astype(np.float32)
+    xt = upload_bits(x)
+    ran = 0
+    for kernel in (nv.KERNEL_AUTO, nv.KERNEL_PERSISTENT, nv.KERNEL_TILE, nv.KERNEL_SPLIT, nv.KERNEL_GENERIC):
+        for m in (1, 16):
+            y = torch.empty((m, n), dtype=torch.float32, device=DEV)
+            st = nv.linear_tiled_raw(xt.data_ptr(), w.wp.data_ptr(), w.sc.data_ptr(), w.t, y.data_ptr(), m, n, k,
+                                     nv.OUT_F32, nv.table_tile(n, k).replace(kernel=kernel),
+                                     torch.cuda.current_stream().cuda_stream)
+            if st == nv.ERR_TILE:
+                continue
+            assert st == nv.OK
+            torch.cuda.synchronize()
+            got = y.cpu().numpy()
+            want = expect[:m]
+            nan = np.isnan(want)
+            assert np.array_equal(np.isnan(got), nan), (kernel, m)
+            assert np.array_equal(got[~nan], want[~nan]), (kernel, m)
+            ran += 1
+    print(f"[decode] 16 codes x 256 scale bytes exact through {ran} kernel/row-count runs", flush=True)
+    assert ran >= 6

@@ -495,41 +495,70 @@ __device__ __forceinline__ u32x4 chunk_piece(const uint8_t* src, int n, int p) {
     return *reinterpret_cast<const u32x4*>(src + (n / 4) * kGrpBytes + 256 * (n % 4) + 16 * (p ^ (n % 4)));
 }
 
-// The 8 scale bytes of 128-k block b of row n of a staged chunk.
-__device__ __forceinline__ uint64_t chunk_scales(const uint8_t* src, int n, int b) {
-    return *reinterpret_cast<const uint64_t*>(src + kWBytes + 32 * n + 8 * b);
+// The two scale bytes of row n that lane quarter kq needs in 128-k block b
+// of a staged chunk (groups 8b + 2kq and 8b + 2kq + 1), in the low 16 bits.
+__device__ __forceinline__ uint32_t chunk_scale_pair(const uint8_t* src, int n, int b, int kq) {
+    return *reinterpret_cast<const uint16_t*>(src + kWBytes + 32 * n + 8 * b + 2 * kq);
 }
+
+// LDS operands of one 128-k block: A pieces of every row tile, and per
+// column tile the packed nibbles and the two scale bytes.
+template <int C, int MT>
+struct BlockOps {
+    u32x4 xa[MT][4];
+    u32x4 w[C];
+    uint32_t d[C];
+};
 
 // Multiplies one staged chunk into acc: C column tiles (chunks at
 // wsrc + c * kTileBytes), MT row tiles of A read from LDS at xsrc (row pitch
 // `pitch` elements, k of the chunk's first element at 0).  Per 128-k block and
 // 32-k slice the MFMA sequence is the one of every kernel here.
+//
+// The LDS reads of block b + 1 are issued before block b is decoded and
+// multiplied (a scheduling barrier keeps them there), so their latency is
+// covered by block b's work instead of stalling each MFMA.
 template <int C, int MT>
 __device__ __forceinline__ void mma_chunk(f32x4 (&acc)[C][MT], const uint8_t* wsrc, const uint16_t* xsrc,
                                           int pitch, const int (&xr)[MT], int col_lane, int kq) {
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        u32x4 xa[MT][4];
+    BlockOps<C, MT> ops[2];
+    auto fetch = [&](BlockOps<C, MT>& o, int b) {
 #pragma unroll
         for (int t = 0; t < MT; ++t)
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-                xa[t][s] = *reinterpret_cast<const u32x4*>(xsrc + xr[t] * pitch + kBlockK * b + 32 * kq + 8 * s);
+                o.xa[t][s] = *reinterpret_cast<const u32x4*>(xsrc + xr[t] * pitch + kBlockK * b + 32 * kq + 8 * s);
 #pragma unroll
         for (int c = 0; c < C; ++c) {
             const uint8_t* src = wsrc + c * kTileBytes;
-            const uint32_t d = static_cast<uint32_t>(chunk_scales(src, col_lane, b) >> (16 * kq));
-            const float g0 = __builtin_amdgcn_cvt_f32_fp8(d, 0);
-            const float g1 = __builtin_amdgcn_cvt_f32_fp8(d, 1);
-            const u32x4 w = chunk_piece(src, col_lane, 4 * b + kq);
+            o.d[c] = chunk_scale_pair(src, col_lane, b, kq);
+            o.w[c] = chunk_piece(src, col_lane, 4 * b + kq);
+        }
+    };
+    fetch(ops[0], 0);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const BlockOps<C, MT>& o = ops[b & 1];
+        // Block b's reads (issued one block earlier) are waited for before
+        // block b + 1's go out, so this wait does not also cover those.
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0); vmcnt and expcnt not waited for
+        __builtin_amdgcn_sched_barrier(0);
+        if (b + 1 < 4) fetch(ops[(b + 1) & 1], b + 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const float g0 = __builtin_amdgcn_cvt_f32_fp8(o.d[c], 0);
+            const float g1 = __builtin_amdgcn_cvt_f32_fp8(o.d[c], 1);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                bf16x8 bv = decode8(w[s], s < 2 ? g0 : g1);
+                bf16x8 bv = decode8(o.w[c][s], s < 2 ? g0 : g1);
 #pragma unroll
                 for (int t = 0; t < MT; ++t)
-                    acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[t][s]), bv, acc[c][t], 0, 0, 0);
+                    acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(o.xa[t][s]), bv, acc[c][t], 0, 0, 0);
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 

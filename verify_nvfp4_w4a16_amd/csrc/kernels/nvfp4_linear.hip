@@ -944,24 +944,41 @@ nvfp4_skinny_split(SplitArgs sa) {
         }
     };
 
-    // Window w is multiplied while window w + 1 (x and weights) is in flight.
-    // (Requesting windows 0 and 1 together measured slower: the second
-    // window's loads delay the first's.)
-    issue_x(0);
-    issue_w(0);
-    wait_vm<0>();
-    lds_barrier();
-    int win = 0;
-    for (; win + 1 < nwin; ++win) {
-        issue_x(win + 1);
-        issue_w(win + 1);
-        wait_vm<kXLoads + kDmaPerTile * C>();       // window win's weights have landed
+    if (MT == 1 && nwin == 2) {
+        // Both windows requested at once: with one row tile the multiply of
+        // window 0 is short, and issuing window 1 only after window 0 has
+        // landed left the wavefronts waiting about one memory latency for it
+        // (measured on MI355X; with two row tiles, or more windows, the
+        // one-ahead schedule below is faster).
+        issue_x(0);
+        issue_w(0);
+        issue_x(1);
+        issue_w(1);
+        wait_vm<kXLoads + kDmaPerTile * C>();       // window 0 (x rows and weights) has landed
+        lds_barrier();                              // ... for every wavefront
+        compute(0);
+        wait_vm<0>();
+        lds_barrier();
+        compute(1);
+    } else {
+        // Window w is multiplied while window w + 1 (x and weights) is in
+        // flight.
+        issue_x(0);
+        issue_w(0);
+        wait_vm<0>();
+        lds_barrier();
+        int win = 0;
+        for (; win + 1 < nwin; ++win) {
+            issue_x(win + 1);
+            issue_w(win + 1);
+            wait_vm<kXLoads + kDmaPerTile * C>();   // window win's weights have landed
+            compute(win);
+            wait_vm<kDmaPerTile * C>();             // this wavefront's x rows of win + 1 have landed
+            lds_barrier();                          // ... and everyone's; buffer win & 1 is free
+        }
+        wait_vm<0>();
         compute(win);
-        wait_vm<kDmaPerTile * C>();                 // this wavefront's x rows of win + 1 have landed
-        lds_barrier();                              // ... and everyone's; buffer win & 1 is free
     }
-    wait_vm<0>();
-    compute(win);
 
     if (sa.split > 1) {
         constexpr int kSlot = W * C * MT * 4 * kWave;   // floats of one workgroup's group sums

@@ -177,14 +177,15 @@ def _run_tiled(xd, w, m, tile, out_dtype=torch.bfloat16):
 def test_ragged_columns_every_kernel_and_split():
     # N = 4136: the last column group of every kernel is partly past N (its
     # loads repeat row N-1, its stores are skipped).  For each segment
-    # grouping (split 1, 2, 8; 8 crosses workgroups in the many-row kernel)
-    # every kernel that can run the shape gives the same bits, within the
-    # oracle's tolerance.
+    # grouping (split 1, 2, 4, 8; above 1 the many-row kernel's groups meet
+    # across workgroups; split 4 gives two-window groups, which one row tile
+    # requests together) every kernel that can run the shape gives the same
+    # bits, within the oracle's tolerance.
     n, k = 4136, 4096
     w = Weight.from_f32(workload.weights_f32(n, k, 91))
-    for split in (1, 2, 8):
+    for split in (1, 2, 4, 8):
         base = nv.table_tile(n, k).replace(split=split)
-        for m in (1, 3, 17, 32):
+        for m in (1, 3, 16, 17, 32):
             x = workload.activations_bf16(m, k, 92 + m)
             xd = upload_bits(x)
             outs = {}

@@ -45,6 +45,7 @@
 #include <atomic>
 #include <mutex>
 #include <string>
+#include <type_traits>
 
 #include "nvfp4_w4a16.h"
 #include "../host/tiles.h"
@@ -364,18 +365,23 @@ nvfp4_skinny(Args a) {
 // instruction (half of each 128-byte line), which streams at roughly half the
 // HBM bandwidth.  The operands are then read from LDS in the MFMA layout.
 //
-// Layout of one column tile's chunk: 4 groups of 4 rows (1024 bytes + 64 of
-// padding per group); row r of a group at 256 r, its 16-byte piece p at
-// 16 (p ^ r).  The load lane l = 16 r + j fetches piece j ^ r of row r and
-// lands at 16 l, so each instruction reads whole 256-byte runs, and the 16
-// rows of one operand read fall into 16 different 16-byte bank groups.  Then
-// 16 rows x 32 scale bytes, row-major.
+// Layout of one column tile's chunk: 16 rows x 32 scale bytes, loaded first,
+// then 4 groups (1024 bytes + 64 of padding each) of 8 rows x 128 bytes:
+// group u holds half h = u / 2 of the chunk (k 256h .. 256h + 255) of rows
+// 8 (u % 2) .. 8 (u % 2) + 7.  Row r of a group sits at 128 r, its 16-byte
+// piece p (of 8 in the half) at 16 (p ^ (r / 2)); the load lane l = 8 r + j
+// fetches piece j ^ (r / 2) of row r and lands at 16 l, so each instruction
+// reads whole 128-byte lines, and the 16 rows of one operand read fall into
+// 16 different 16-byte bank groups.  The first half of a chunk is complete
+// once its scale loads and first two weight loads have landed, so the
+// multiply of blocks 0 and 1 starts while the second half is in flight.
 constexpr int kChunkK = 512;                      // k per chunk
-constexpr int kGrpBytes = 4 * 256 + 64;
-constexpr int kWBytes = 4 * kGrpBytes;
+constexpr int kGrpBytes = 8 * 128 + 64;
 constexpr int kSBytes = 16 * 32;
-constexpr int kTileBytes = kWBytes + kSBytes;     // one column tile's chunk in LDS
+constexpr int kWBytes = 4 * kGrpBytes;
+constexpr int kTileBytes = kSBytes + kWBytes;     // one column tile's chunk in LDS
 constexpr int kDmaPerTile = 6;                    // load instructions per column tile's chunk
+constexpr int kDmaHalf1 = 2;                      // of those, the last ones: the chunk's second half
 
 // Waits until at most N vector memory operations of this wavefront are
 // outstanding (the direct-to-LDS loads count there), and keeps both the
@@ -474,31 +480,34 @@ __device__ __forceinline__ void fold_waves(f32x4 (&acc)[C][MT], PartFn part, int
 __device__ __forceinline__ void issue_tile_chunk(uint8_t* dst, const uint8_t* wp, const uint8_t* sc, int row0,
                                                  int nmax, uint32_t row_bytes, uint32_t scale_bytes, uint32_t kb,
                                                  int lane) {
-    const int r = lane / 16, j = lane % 16;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const uint32_t row = static_cast<uint32_t>(min(row0 + 4 * u + r, nmax));
-        __builtin_amdgcn_global_load_lds(wp + static_cast<uint64_t>(row) * row_bytes + kb + 16 * (j ^ r),
-                                         dst + u * kGrpBytes, 16, 0, 0);
-    }
+    const int r = lane / 8, j = lane % 8;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const uint32_t row = static_cast<uint32_t>(min(row0 + 8 * h + lane / 8, nmax));
-        __builtin_amdgcn_global_load_lds(sc + static_cast<uint64_t>(row) * scale_bytes + kb / 8 + 4 * (lane % 8),
-                                         dst + kWBytes + h * 256, 4, 0, 0);
+        const uint32_t row = static_cast<uint32_t>(min(row0 + 8 * h + r, nmax));
+        __builtin_amdgcn_global_load_lds(sc + static_cast<uint64_t>(row) * scale_bytes + kb / 8 + 4 * j,
+                                         dst + h * 256, 4, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const uint32_t row = static_cast<uint32_t>(min(row0 + 8 * (u % 2) + r, nmax));
+        __builtin_amdgcn_global_load_lds(wp + static_cast<uint64_t>(row) * row_bytes + kb + 128 * (u / 2) +
+                                             16 * (j ^ (r / 2)),
+                                         dst + kSBytes + u * kGrpBytes, 16, 0, 0);
     }
 }
 
 // 16-byte piece p (32 k) of row n of a staged chunk: the B operand of lane
 // (n, kq) for 128-k block b is piece 4 b + kq.
 __device__ __forceinline__ u32x4 chunk_piece(const uint8_t* src, int n, int p) {
-    return *reinterpret_cast<const u32x4*>(src + (n / 4) * kGrpBytes + 256 * (n % 4) + 16 * (p ^ (n % 4)));
+    const int r = n % 8;
+    return *reinterpret_cast<const u32x4*>(src + kSBytes + (2 * (p / 8) + n / 8) * kGrpBytes + 128 * r +
+                                           16 * ((p % 8) ^ (r / 2)));
 }
 
 // The two scale bytes of row n that lane quarter kq needs in 128-k block b
 // of a staged chunk (groups 8b + 2kq and 8b + 2kq + 1), in the low 16 bits.
 __device__ __forceinline__ uint32_t chunk_scale_pair(const uint8_t* src, int n, int b, int kq) {
-    return *reinterpret_cast<const uint16_t*>(src + kWBytes + 32 * n + 8 * b + 2 * kq);
+    return *reinterpret_cast<const uint16_t*>(src + 32 * n + 8 * b + 2 * kq);
 }
 
 // LDS operands of one 128-k block: A pieces of every row tile, and per
@@ -518,9 +527,9 @@ struct BlockOps {
 // The LDS reads of block b + 1 are issued before block b is decoded and
 // multiplied (a scheduling barrier keeps them there), so their latency is
 // covered by block b's work instead of stalling each MFMA.
-template <int C, int MT>
-__device__ __forceinline__ void mma_chunk(f32x4 (&acc)[C][MT], const uint8_t* wsrc, const uint16_t* xsrc,
-                                          int pitch, const int (&xr)[MT], int col_lane, int kq) {
+template <int C, int MT, int H>
+__device__ __forceinline__ void mma_half(f32x4 (&acc)[C][MT], const uint8_t* wsrc, const uint16_t* xsrc,
+                                         int pitch, const int (&xr)[MT], int col_lane, int kq) {
     BlockOps<C, MT> ops[2];
     auto fetch = [&](BlockOps<C, MT>& o, int b) {
 #pragma unroll
@@ -535,16 +544,16 @@ __device__ __forceinline__ void mma_chunk(f32x4 (&acc)[C][MT], const uint8_t* ws
             o.w[c] = chunk_piece(src, col_lane, 4 * b + kq);
         }
     };
-    fetch(ops[0], 0);
+    fetch(ops[0], 2 * H);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
+    for (int b = 2 * H; b < 2 * H + 2; ++b) {
         const BlockOps<C, MT>& o = ops[b & 1];
         // Block b's reads (issued one block earlier) are waited for before
         // block b + 1's go out, so this wait does not also cover those.
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0); vmcnt and expcnt not waited for
         __builtin_amdgcn_sched_barrier(0);
-        if (b + 1 < 4) fetch(ops[(b + 1) & 1], b + 1);
+        if (b + 1 < 2 * H + 2) fetch(ops[(b + 1) & 1], b + 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int c = 0; c < C; ++c) {
@@ -560,6 +569,18 @@ __device__ __forceinline__ void mma_chunk(f32x4 (&acc)[C][MT], const uint8_t* ws
         }
         __builtin_amdgcn_sched_barrier(0);
     }
+}
+
+// Multiplies a staged chunk whose loads are the last ones issued except for
+// `After` more: waits for its first half, multiplies blocks 0 and 1, waits
+// for the second half, multiplies blocks 2 and 3.
+template <int C, int MT, int After>
+__device__ __forceinline__ void mma_chunk(f32x4 (&acc)[C][MT], const uint8_t* wsrc, const uint16_t* xsrc,
+                                          int pitch, const int (&xr)[MT], int col_lane, int kq) {
+    wait_vm<After + kDmaHalf1>();
+    mma_half<C, MT, 0>(acc, wsrc, xsrc, pitch, xr, col_lane, kq);
+    wait_vm<After>();
+    mma_half<C, MT, 1>(acc, wsrc, xsrc, pitch, xr, col_lane, kq);
 }
 
 // Persistent kernel for x small enough to sit in LDS whole (the M = 1 GEMV
@@ -645,9 +666,10 @@ nvfp4_skinny_persistent(Args a) {
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](int j) {
-        mma_chunk<C, MT>(acc, wbuf + (j % NB) * C * kTileBytes, lds + k0 + (j % nch) * kChunkK, pitch, xr,
-                         col_lane, kq);
+    // chunk j, once at most `after` loads issued after its own are outstanding
+    auto compute = [&](int j, auto after) {
+        mma_chunk<C, MT, decltype(after)::value>(acc, wbuf + (j % NB) * C * kTileBytes,
+                                                 lds + k0 + (j % nch) * kChunkK, pitch, xr, col_lane, kq);
     };
 
     // After the last chunk of a tile: segment partials through LDS (two
@@ -701,18 +723,15 @@ nvfp4_skinny_persistent(Args a) {
     int j = 0;
     for (; j + kAhead < total; ++j) {
         issue(j + kAhead);
-        wait_vm<kAhead * kDmaPerTile * C>();          // chunk j has landed
-        compute(j);
+        compute(j, std::integral_constant<int, kAhead * kDmaPerTile * C>{});
         if (j % nch == nch - 1) finish_tile(j);
     }
     if (NB > 2 && j + 1 < total) {
-        wait_vm<kDmaPerTile * C>();
-        compute(j);
+        compute(j, std::integral_constant<int, kDmaPerTile * C>{});
         if (j % nch == nch - 1) finish_tile(j);
         ++j;
     }
-    wait_vm<0>();
-    compute(j);
+    compute(j, std::integral_constant<int, 0>{});
     finish_tile(j);                                   // the last chunk ends a tile
 }
 
@@ -776,8 +795,10 @@ nvfp4_skinny_tile(Args a) {
     for (int c = 0; c < C; ++c)
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto compute = [&](int j) {
-        mma_chunk<C, MT>(acc, wbuf + (j % NB) * C * kTileBytes, xs + j * kChunkK, xpitch, xr, col_lane, kq);
+    // chunk j, once at most `after` loads issued after its own are outstanding
+    auto compute = [&](int j, auto after) {
+        mma_chunk<C, MT, decltype(after)::value>(acc, wbuf + (j % NB) * C * kTileBytes, xs + j * kChunkK, xpitch,
+                                                 xr, col_lane, kq);
     };
 
     // NB - 1 chunks ahead; the last ones peeled so no load is repeated.
@@ -786,18 +807,13 @@ nvfp4_skinny_tile(Args a) {
     int j = 0;
     for (; j + kAhead < nch; ++j) {
         issue(j + kAhead);
-        wait_vm<kAhead * kDmaPerTile * C>();          // x and chunk j have landed
-        compute(j);
+        compute(j, std::integral_constant<int, kAhead * kDmaPerTile * C>{});   // x and chunk j have landed
     }
     if (NB > 2 && j + 1 < nch) {
-        wait_vm<kDmaPerTile * C>();
-        compute(j);
+        compute(j, std::integral_constant<int, kDmaPerTile * C>{});
         ++j;
     }
-    if (j < nch) {
-        wait_vm<0>();
-        compute(j);
-    }
+    if (j < nch) compute(j, std::integral_constant<int, 0>{});
 
     // segment sums: each wavefront's into its first chunk buffer, then
     // wavefront 0 adds them in the two-level order
@@ -927,9 +943,17 @@ nvfp4_skinny_split(SplitArgs sa) {
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[c][t] = grp[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](int win) {
-        mma_chunk<C, MT>(acc, wbuf + (win & 1) * C * kTileBytes, lds + (win & 1) * slice, kXPitch, xr, col_lane,
-                         kq);
+    auto compute_half = [&](int win, auto h) {
+        mma_half<C, MT, decltype(h)::value>(acc, wbuf + (win & 1) * C * kTileBytes, lds + (win & 1) * slice,
+                                            kXPitch, xr, col_lane, kq);
+    };
+    // window win: its first half is in LDS (and, with `barrier`, every
+    // wavefront's x rows of it); waits for the second half (at most `after`
+    // later loads outstanding), multiplies it, folds at a segment end
+    auto compute = [&](int win, auto after) {
+        compute_half(win, std::integral_constant<int, 0>{});
+        wait_vm<decltype(after)::value>();
+        compute_half(win, std::integral_constant<int, 1>{});
         // end of a segment: its chain joins the group sum (the first chain
         // is taken as it is, so a -0 sum keeps its sign)
         if ((win + 1) % seg_chunks == 0) {
@@ -954,30 +978,30 @@ nvfp4_skinny_split(SplitArgs sa) {
         issue_w(0);
         issue_x(1);
         issue_w(1);
-        wait_vm<kXLoads + kDmaPerTile * C>();       // window 0 (x rows and weights) has landed
-        lds_barrier();                              // ... for every wavefront
-        compute(0);
-        wait_vm<0>();
+        wait_vm<kXLoads + kDmaPerTile * C + kDmaHalf1>();   // window 0's x rows and first half have landed
+        lds_barrier();                                      // ... for every wavefront
+        compute(0, std::integral_constant<int, kXLoads + kDmaPerTile * C>{});
+        wait_vm<kDmaHalf1>();
         lds_barrier();
-        compute(1);
+        compute(1, std::integral_constant<int, 0>{});
     } else {
         // Window w is multiplied while window w + 1 (x and weights) is in
         // flight.
         issue_x(0);
         issue_w(0);
-        wait_vm<0>();
+        wait_vm<kDmaHalf1>();                       // x rows and the first half of window 0
         lds_barrier();
         int win = 0;
         for (; win + 1 < nwin; ++win) {
             issue_x(win + 1);
             issue_w(win + 1);
-            wait_vm<kXLoads + kDmaPerTile * C>();   // window win's weights have landed
-            compute(win);
+            wait_vm<kXLoads + kDmaPerTile * C + kDmaHalf1>();   // window win's first half has landed
+            compute(win, std::integral_constant<int, kXLoads + kDmaPerTile * C>{});
             wait_vm<kDmaPerTile * C>();             // this wavefront's x rows of win + 1 have landed
             lds_barrier();                          // ... and everyone's; buffer win & 1 is free
         }
-        wait_vm<0>();
-        compute(win);
+        wait_vm<kDmaHalf1>();
+        compute(win, std::integral_constant<int, 0>{});
     }
 
     if (sa.split > 1) {

@@ -147,6 +147,18 @@ struct Chunk {
 // one A-operand read touches start in different banks.
 __device__ __forceinline__ int lds_pitch(int k) { return k + 8; }
 
+// x rows staged by direct-to-LDS loads keep the four 32-k quarters of each
+// 128-k block rotated by the row's group of four: quarter q of row r sits at
+// slot (q + r / 4) % 4.  An A read (16 rows x 4 quarters) of unrotated rows
+// took 8 LDS cycles per instruction, half of them bank conflicts; rotated, it
+// takes 4, as a contiguous read does (ds_read_b128 pattern probe on MI355X).
+__device__ __forceinline__ int xslot(int q, int r) { return (q + (r >> 2)) & 3; }
+// Global 16-byte piece of x row r that load lane u (LDS piece u of a 1 KB
+// run: block u / 16, slot (u / 4) % 4, eighth u % 4) fetches.
+__device__ __forceinline__ int xpiece(int u, int r) {
+    return (u & ~12) | ((((u >> 2) - (r >> 2)) & 3) << 2);
+}
+
 // C: 16-column tiles per wavefront.  MT: 16-row A tiles (1 for M <= 16).
 // U: 128-k blocks per pipeline step.  OUT_F32: y element type.
 //
@@ -536,7 +548,8 @@ __device__ __forceinline__ void mma_half(f32x4 (&acc)[C][MT], const uint8_t* wsr
         for (int t = 0; t < MT; ++t)
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-                o.xa[t][s] = *reinterpret_cast<const u32x4*>(xsrc + xr[t] * pitch + kBlockK * b + 32 * kq + 8 * s);
+                o.xa[t][s] = *reinterpret_cast<const u32x4*>(xsrc + xr[t] * pitch + kBlockK * b +
+                                                             32 * xslot(kq, xr[t]) + 8 * s);
 #pragma unroll
         for (int c = 0; c < C; ++c) {
             const uint8_t* src = wsrc + c * kTileBytes;
@@ -647,7 +660,7 @@ nvfp4_skinny_persistent(Args a) {
             const int r = i / per_row, p = i % per_row;
             const int valid = min(kWave, (a.k - p * kChunkK) / 8);    // 16-byte pieces in this load
             if (lane < valid)
-                __builtin_amdgcn_global_load_lds(a.x + (int64_t)r * a.k + p * kChunkK + 8 * lane,
+                __builtin_amdgcn_global_load_lds(a.x + (int64_t)r * a.k + p * kChunkK + 8 * xpiece(lane, r),
                                                  lds + r * pitch + p * kChunkK, 16, 0, 0);
         }
         issue(0);
@@ -778,7 +791,7 @@ nvfp4_skinny_tile(Args a) {
     // this wavefront's x slice: M x nch loads of 1 KB
     for (int i = 0; i < a.m * nch; ++i) {
         const int r = i / nch, p = i % nch;
-        __builtin_amdgcn_global_load_lds(a.x + (int64_t)r * a.k + k0 + p * kChunkK + 8 * lane,
+        __builtin_amdgcn_global_load_lds(a.x + (int64_t)r * a.k + k0 + p * kChunkK + 8 * xpiece(lane, r),
                                          xs + r * xpitch + p * kChunkK, 16, 0, 0);
     }
     auto issue = [&](int j) {
@@ -924,7 +937,7 @@ nvfp4_skinny_split(SplitArgs sa) {
 #pragma unroll
         for (int i = 0; i < kXLoads; ++i) {
             const int r = min(wave + i * W, a.m - 1);
-            __builtin_amdgcn_global_load_lds(a.x + (int64_t)r * a.k + kbase + win * kChunkK + 8 * lane,
+            __builtin_amdgcn_global_load_lds(a.x + (int64_t)r * a.k + kbase + win * kChunkK + 8 * xpiece(lane, r),
                                              dst + r * kXPitch, 16, 0, 0);
         }
     };

@@ -377,8 +377,11 @@ nvfp4_skinny(Args a) {
 // instruction (half of each 128-byte line), which streams at roughly half the
 // HBM bandwidth.  The operands are then read from LDS in the MFMA layout.
 //
-// Layout of one column tile's chunk: 16 rows x 32 scale bytes, loaded first,
-// then 4 groups (1024 bytes + 64 of padding each) of 8 rows x 128 bytes:
+// Layout of one column tile's chunk: 16 rows x 32 scale bytes, loaded first
+// (rows 8..15 16 bytes further on, so that rows n and n + 8 fall into
+// different LDS banks: the two-byte scale read of a block took 8 LDS cycles,
+// three quarters of them bank conflicts, with the rows 32 bytes apart
+// throughout), then 4 groups (1024 bytes + 64 of padding each) of 8 rows x 128 bytes:
 // group u holds half h = u / 2 of the chunk (k 256h .. 256h + 255) of rows
 // 8 (u % 2) .. 8 (u % 2) + 7.  Row r of a group sits at 128 r, its 16-byte
 // piece p (of 8 in the half) at 16 (p ^ (r / 2)); the load lane l = 8 r + j
@@ -389,7 +392,8 @@ nvfp4_skinny(Args a) {
 // multiply of blocks 0 and 1 starts while the second half is in flight.
 constexpr int kChunkK = 512;                      // k per chunk
 constexpr int kGrpBytes = 8 * 128 + 64;
-constexpr int kSBytes = 16 * 32;
+constexpr int kSHalfBytes = 8 * 32 + 16;          // 8 rows of scale bytes + padding
+constexpr int kSBytes = 2 * kSHalfBytes;
 constexpr int kWBytes = 4 * kGrpBytes;
 constexpr int kTileBytes = kSBytes + kWBytes;     // one column tile's chunk in LDS
 constexpr int kDmaPerTile = 6;                    // load instructions per column tile's chunk
@@ -497,7 +501,7 @@ __device__ __forceinline__ void issue_tile_chunk(uint8_t* dst, const uint8_t* wp
     for (int h = 0; h < 2; ++h) {
         const uint32_t row = static_cast<uint32_t>(min(row0 + 8 * h + r, nmax));
         __builtin_amdgcn_global_load_lds(sc + static_cast<uint64_t>(row) * scale_bytes + kb / 8 + 4 * j,
-                                         dst + h * 256, 4, 0, 0);
+                                         dst + h * kSHalfBytes, 4, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -519,7 +523,7 @@ __device__ __forceinline__ u32x4 chunk_piece(const uint8_t* src, int n, int p) {
 // The two scale bytes of row n that lane quarter kq needs in 128-k block b
 // of a staged chunk (groups 8b + 2kq and 8b + 2kq + 1), in the low 16 bits.
 __device__ __forceinline__ uint32_t chunk_scale_pair(const uint8_t* src, int n, int b, int kq) {
-    return *reinterpret_cast<const uint16_t*>(src + 32 * n + 8 * b + 2 * kq);
+    return *reinterpret_cast<const uint16_t*>(src + (n / 8) * kSHalfBytes + 32 * (n % 8) + 8 * b + 2 * kq);
 }
 
 // LDS operands of one 128-k block: A pieces of every row tile, and per

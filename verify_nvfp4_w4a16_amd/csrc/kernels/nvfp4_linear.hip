@@ -1393,12 +1393,22 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
     SplitPlan plan;
     const bool split_ok = plan_split(tile, m, n, k, d, &plan);
     // The per-tile kernel: each wavefront's x slice and chunk buffers (up to
-    // three, at most one per chunk of its segment) within the LDS.
-    // The most chunk buffers (up to three, at most one per chunk of the
-    // segment) that fit.
+    // three, at most one per chunk of its segment) within the LDS: the most
+    // that fit, except that where a CU has to take several workgroups, fewer
+    // buffers are used if that keeps at least three of them resident
+    // (measured on MI355X: 24576x4096 at M = 2 and 4, two buffers leave two
+    // workgroups per CU and take 17.4 and 19.0 us, one buffer four and three,
+    // 14.9 and 17.6 us; at M = 1 three fit with two buffers, which is faster).
     const int64_t ks = k / tile.waves;
     int tnb = int(std::min<int64_t>(3, std::max<int64_t>(1, ks / kChunkK)));
     while (tnb > 1 && tile_lds_bytes(m, ks, tile.waves, pc, tnb) + 256 > size_t(kMaxLdsBytes)) --tnb;
+    {
+        const int cus = d.cus > 0 ? d.cus : 256;
+        const int64_t per_cu = ((n + 16 * pc - 1) / (16 * pc) + cus - 1) / cus;   // workgroups each CU must run
+        auto resident = [&](int nb) { return int64_t(kMaxLdsBytes) / int64_t(tile_lds_bytes(m, ks, tile.waves, pc, nb) + 256); };
+        const int64_t want = std::min<int64_t>(3, per_cu);
+        while (tnb > 1 && resident(tnb) < want && resident(tnb - 1) > resident(tnb)) --tnb;
+    }
     const size_t tile_bytes = tile_lds_bytes(m, ks, tile.waves, pc, tnb);
     const bool tile_ok = tile.cols <= 32 && ks % kChunkK == 0 && tile_bytes + 256 <= size_t(kMaxLdsBytes);
     // Measured on MI355X: the per-tile kernel leads up to four rows (its

@@ -1402,23 +1402,31 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
     const int64_t ks = k / tile.waves;
     int tnb = int(std::min<int64_t>(3, std::max<int64_t>(1, ks / kChunkK)));
     while (tnb > 1 && tile_lds_bytes(m, ks, tile.waves, pc, tnb) + 256 > size_t(kMaxLdsBytes)) --tnb;
+    const int cus = d.cus > 0 ? d.cus : 256;
+    const int64_t tile_per_cu = ((n + 16 * pc - 1) / (16 * pc) + cus - 1) / cus;   // workgroups each CU must run
+    auto tile_resident = [&](int nb) {
+        return int64_t(kMaxLdsBytes) / int64_t(tile_lds_bytes(m, ks, tile.waves, pc, nb) + 256);
+    };
     {
-        const int cus = d.cus > 0 ? d.cus : 256;
-        const int64_t per_cu = ((n + 16 * pc - 1) / (16 * pc) + cus - 1) / cus;   // workgroups each CU must run
-        auto resident = [&](int nb) { return int64_t(kMaxLdsBytes) / int64_t(tile_lds_bytes(m, ks, tile.waves, pc, nb) + 256); };
-        const int64_t want = std::min<int64_t>(3, per_cu);
-        while (tnb > 1 && resident(tnb) < want && resident(tnb - 1) > resident(tnb)) --tnb;
+        const int64_t want = std::min<int64_t>(3, tile_per_cu);
+        while (tnb > 1 && tile_resident(tnb) < want && tile_resident(tnb - 1) > tile_resident(tnb)) --tnb;
     }
     const size_t tile_bytes = tile_lds_bytes(m, ks, tile.waves, pc, tnb);
     const bool tile_ok = tile.cols <= 32 && ks % kChunkK == 0 && tile_bytes + 256 <= size_t(kMaxLdsBytes);
-    // Measured on MI355X: the per-tile kernel leads up to four rows (its
-    // workgroups are short and several share a CU), then the persistent one
-    // while x fits, then the many-row kernel.
+    // Measured on MI355X (decode-round shapes, M = 1..8): the per-tile kernel
+    // leads up to four rows (its workgroups are short and several share a
+    // CU), and up to eight rows while all its workgroups are resident at once
+    // (each workgroup stages all of x, so its x traffic grows with M); then
+    // the many-row kernel where its segment groups need no exchange between
+    // workgroups (split 1), the persistent one while x fits, and the
+    // many-row kernel.
+    const bool tile_first = tile_ok && (m <= 4 || (m <= 8 && tile_resident(tnb) >= tile_per_cu));
     if (kernel == NVFP4_KERNEL_AUTO)
-        kernel = tile_ok && m <= 4 ? NVFP4_KERNEL_TILE
-                 : pers_ok         ? NVFP4_KERNEL_PERSISTENT
-                 : split_ok        ? NVFP4_KERNEL_SPLIT
-                                   : NVFP4_KERNEL_GENERIC;
+        kernel = tile_first                   ? NVFP4_KERNEL_TILE
+                 : split_ok && tile.split == 1 ? NVFP4_KERNEL_SPLIT
+                 : pers_ok                     ? NVFP4_KERNEL_PERSISTENT
+                 : split_ok                    ? NVFP4_KERNEL_SPLIT
+                                               : NVFP4_KERNEL_GENERIC;
     if ((kernel == NVFP4_KERNEL_PERSISTENT && !pers_ok) || (kernel == NVFP4_KERNEL_SPLIT && !split_ok) ||
         (kernel == NVFP4_KERNEL_TILE && !tile_ok))
         return NVFP4_ERR_TILE;

@@ -74,6 +74,11 @@ def test_qkv_outliers_parity_and_invariance():
 
 
 def test_round_shapes_parity():
+    # The decode round's shapes at its row counts, and at every row count the
+    # kernel choice distinguishes (per-tile kernel with one or more chunk
+    # buffers, persistent, many-row with one or two windows requested at
+    # once): each row of a 32-row block, computed at M rows, is bit-equal to
+    # the same row computed alone, and within the oracle's tolerance.
     rng = workload.rng(77)
     for proj, s in enumerate(workload.ROUND_SHAPES):
         w = Weight.from_f32(workload.weights_f32(s.n, s.k, workload.round_weight_seed(0, proj)))
@@ -82,6 +87,13 @@ def test_round_shapes_parity():
         for m in workload.ROUND_M:
             x = workload.activations_bf16(m, s.k, workload.round_act_seed(0, proj, m))
             check_parity(run(x, w), x, w, cols=cols, label=f"round proj{proj}")
+        xb = workload.activations_bf16(32, s.k, workload.round_act_seed(0, proj, 99))
+        alone = torch.cat([bits(run(xb[r:r + 1], w)) for r in range(32)])
+        for m in (2, 3, 4, 5, 6, 7, 8, 12, 16, 17, 24, 32):
+            y = run(xb[:m], w)
+            assert torch.equal(bits(y), alone[:m]), f"round proj{proj} M={m}: rows differ from M=1"
+            if m <= 8:
+                check_parity(y, xb[:m], w, cols=cols, label=f"round proj{proj} block")
 
 
 def test_head_fp32_parity_and_gemv_vs_mfma_rows():

@@ -141,11 +141,12 @@ int nvfp4_linear(const void* x_bf16, const uint8_t* w_packed,
 /* Kernel choice of nvfp4_linear_tiled (nvfp4_linear always chooses itself).
  * Every kernel computes the same bits for the same tile waves and split. */
 enum {
-    NVFP4_KERNEL_AUTO = 0,       /* as nvfp4_linear: by M, K and the workspace */
+    NVFP4_KERNEL_AUTO = 0,       /* as nvfp4_linear: by M, the shape, the LDS fit and the workspace */
     NVFP4_KERNEL_PERSISTENT = 1, /* workgroups walk the column tiles with x [M, K] whole in LDS; needs
                                     K / waves % 512 == 0, M * (K + 8) * 2 <= 64 KB, cols <= 32 */
     NVFP4_KERNEL_TILE = 2,       /* one workgroup per column tile, each wavefront streaming its K segment
-                                    through LDS; needs K / waves % 512 == 0, cols <= 32 and small M */
+                                    through LDS; needs K / waves % 512 == 0, cols <= 32 and M small enough
+                                    for the wavefronts' x slices to fit the LDS */
     NVFP4_KERNEL_SPLIT = 3,      /* many-row kernel: one segment group per workgroup, x windows in LDS;
                                     needs K / waves % 512 == 0 and, for split > 1, the device workspace */
     NVFP4_KERNEL_GENERIC = 4     /* one workgroup per column tile, register loads; any shape */

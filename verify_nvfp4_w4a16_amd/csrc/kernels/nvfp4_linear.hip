@@ -13,7 +13,7 @@
 //    row (output column) l % 16 and, per instruction, 8 consecutive k of it.
 //    A lane's 16-byte operand piece holds 32 k of one row (4 instructions'
 //    worth).  The streaming kernels bring weights into LDS with direct-to-LDS
-//    loads that read 4 rows x 256 contiguous bytes each (an XOR swizzle keeps
+//    loads that read 8 rows x 128 contiguous bytes each (an XOR swizzle keeps
 //    the 16 rows of one operand read in different bank groups); the generic
 //    kernel loads the pieces straight into registers.
 //  * Decode is in registers: v_cvt_scalef32_pk_f32_fp4 turns one packed byte
@@ -369,10 +369,10 @@ nvfp4_skinny(Args a) {
 }
 
 // ---- Weight chunks staged in LDS ---------------------------------------
-// The two fast kernels stream weights through LDS.  A chunk is 512 k of the
+// The streaming kernels bring weights through LDS.  A chunk is 512 k of the
 // 16 weight rows of one column tile: 256 bytes of nibbles and 32 scale bytes
 // per row.  Direct-to-LDS loads (global_load_lds) bring it in, each load
-// instruction reading 4 rows x 256 contiguous bytes; loading the MFMA operand
+// instruction reading whole 128-byte lines (8 rows x 128 bytes); loading the MFMA operand
 // layout straight into registers instead touches 16 rows x 64 bytes per
 // instruction (half of each 128-byte line), which streams at roughly half the
 // HBM bandwidth.  The operands are then read from LDS in the MFMA layout.

@@ -1413,14 +1413,19 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
     }
     const size_t tile_bytes = tile_lds_bytes(m, ks, tile.waves, pc, tnb);
     const bool tile_ok = tile.cols <= 32 && ks % kChunkK == 0 && tile_bytes + 256 <= size_t(kMaxLdsBytes);
-    // Measured on MI355X (decode-round shapes, M = 1..8): the per-tile kernel
-    // leads up to four rows (its workgroups are short and several share a
-    // CU), and up to eight rows while all its workgroups are resident at once
-    // (each workgroup stages all of x, so its x traffic grows with M); then
-    // the many-row kernel where its segment groups need no exchange between
-    // workgroups (split 1), the persistent one while x fits, and the
-    // many-row kernel.
-    const bool tile_first = tile_ok && (m <= 4 || (m <= 8 && tile_resident(tnb) >= tile_per_cu));
+    // Measured on MI355X (decode-round and output-head shapes, M = 1..8): the
+    // per-tile kernel leads at one row; up to four rows too (its workgroups
+    // are short and several share a CU), unless each CU would run more than
+    // three rounds of them and the many-row kernel needs no exchange between
+    // workgroups (151552x4096 at M = 2..4: 89-96 us per-tile, 69-76 us
+    // many-row); up to eight rows while all its workgroups are resident at
+    // once (each workgroup stages all of x, so its x traffic grows with M).
+    // Then the many-row kernel where its segment groups need no exchange
+    // (split 1), the persistent one while x fits, and the many-row kernel.
+    const bool many_rounds = tile_per_cu > 3 * tile_resident(tnb);
+    const bool tile_first =
+        tile_ok && (m == 1 || (m <= 4 && !(many_rounds && split_ok && tile.split == 1)) ||
+                    (m <= 8 && tile_resident(tnb) >= tile_per_cu));
     if (kernel == NVFP4_KERNEL_AUTO)
         kernel = tile_first                   ? NVFP4_KERNEL_TILE
                  : split_ok && tile.split == 1 ? NVFP4_KERNEL_SPLIT

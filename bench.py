@@ -338,7 +338,7 @@ def main() -> int:
         "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"decode round: {args.layers} layers x {{(8192,4096), (4096,8192), "
-                               "(24576,4096), (4096,12288)}} NVFP4 W4A16, back-to-back per M, HIP graph",
+                               "(24576,4096), (4096,12288)} NVFP4 W4A16, back-to-back per M, HIP graph",
                    "m": ms_list, "layers": args.layers, "launches_per_round": launches_per_round,
                    "weight_stream_bytes_per_round": weight_bytes, "parallelism": "single GPU"},
         "pct_of_peak": 100 * value / PEAK_HBM_GBPS,

@@ -1,5 +1,6 @@
-"""The shape contract's largest sizes through the HIP path (gpu): K = 2^20
-with a ragged N, and N = 2^28, where weight offsets pass 2^32 bytes."""
+"""The shape contract's limits through the HIP path (gpu): K = 2^20 with a
+ragged N, N = 2^28 (weight offsets past 2^32 bytes), and one output column
+with the smallest K."""
 import numpy as np
 import pytest
 import torch
@@ -94,3 +95,36 @@ def test_largest_n_sampled_columns():
         del y, ys
     del wp, sc
     torch.cuda.empty_cache()
+
+
+def test_smallest_shapes_every_kernel():
+    # One output column (15 of the 16 MFMA columns past N) with the smallest
+    # K (256) and with K = 4096 (every kernel can run it), at every M: all
+    # kernels give the same bits, row r's bits do not depend on M, and the
+    # values are within the oracle's tolerance.
+    for k in (256, 4096):
+        packed, scales = workload.random_codes(1, k, 90 + k)
+        w = Weight(packed, scales, 0.25)
+        x = workload.activations_bf16(32, k, 91 + k)
+        xd = upload_bits(x)
+        full = None
+        for m in range(32, 0, -1):
+            outs = {}
+            for kernel in (nv.KERNEL_AUTO, nv.KERNEL_TILE, nv.KERNEL_PERSISTENT, nv.KERNEL_SPLIT,
+                           nv.KERNEL_GENERIC):
+                st, y = _launch(xd, w.wp, w.sc, w.t, m, 1, k, nv.table_tile(1, k).replace(kernel=kernel),
+                                out_dtype=torch.float32)
+                if st == nv.ERR_TILE:
+                    continue
+                assert st == nv.OK, (k, m, kernel, st)
+                outs[kernel] = y
+            assert {nv.KERNEL_AUTO, nv.KERNEL_GENERIC} <= set(outs), (k, m, sorted(outs))
+            if k == 4096 and m <= 3:
+                assert {nv.KERNEL_TILE, nv.KERNEL_PERSISTENT, nv.KERNEL_SPLIT} <= set(outs), (m, sorted(outs))
+            ref = bits(outs[nv.KERNEL_AUTO])
+            for kernel, y in outs.items():
+                assert torch.equal(bits(y), ref), f"K={k} M={m} kernel {kernel}"
+            if full is None:
+                full = ref.clone()
+                check_parity(outs[nv.KERNEL_AUTO], x, w, label=f"N=1 K={k}")
+            assert torch.equal(ref, full[:m]), f"K={k}: rows at M={m} differ from M=32"

@@ -95,7 +95,12 @@ int nvfp4_check_scales(const uint8_t* scales_e4m3, int64_t n, int64_t k);
 int nvfp4_linear_shape_ok(int64_t m, int64_t n, int64_t k);
 
 /*
- * Host.  Checks that the current HIP device is gfx950, loads the kernels'
+ * Host.  Set-up before graph capture: "CUDA Kernel Engineering" (CUDA graphs)
+ * captures every launch once at start-up and needs fixed buffer addresses and
+ * no allocation in the replayed loop; "10 Kernels" 10.6 replays every verify
+ * from graphs.  This call does every allocation and code-object load the
+ * launches need, so nothing of the kind happens under capture.
+ * Checks that the current HIP device is gfx950, loads the kernels'
  * code objects and the (N, K) tile table once per process (the table may be
  * overridden by the file named in the environment variable NVFP4_TILES, read
  * here only), and sets up the current device's workspace once per device: 32
@@ -114,7 +119,10 @@ int nvfp4_init(void);
 
 /*
  * Device, asynchronous on `stream` (a hipStream_t; NULL = the null stream).
- *   y[M, N] = x[M, K] . Wd[N, K]^T with Wd as at the top of this file.
+ *   y[M, N] = x[M, K] . Wd[N, K]^T with Wd as at the top of this file: the
+ * product of "Module ops" w4a16_gemm / w4a16_tc_rows (C = A @ dequant(B)) at
+ * the 1..32-row decode and verify counts of "10 Kernels" 10.2, with the row
+ * invariance of 10.1.
  * x:           device, bf16 [M, K] row-major (pitch K elements), 16-byte aligned.
  * w_packed:    device, [N, K/2] bytes, 16-byte aligned.
  * scales_e4m3: device, [N, K/16] bytes, 16-byte aligned.
@@ -172,7 +180,9 @@ typedef struct nvfp4_tile {
 /*
  * Device, asynchronous: nvfp4_linear with an explicit launch tile and kernel
  * instead of the (N, K) table's, for tile sweeps and for tests that every
- * kernel gives the same bits for the same waves and split.  `tile` is a host
+ * kernel gives the same bits for the same waves and split.  "10 Kernels" 10.1
+ * keeps only tile choices bit-identical to the default at 1 to 32 rows and
+ * 10.2 fills the per-shape tables from such sweeps.  `tile` is a host
  * pointer read during the call only.
  * Errors: those of nvfp4_linear, NULL for tile == NULL, and TILE for a tile
  * that does not fit the shape or a kernel that cannot run it.
@@ -185,7 +195,10 @@ int nvfp4_linear_tiled(const void* x_bf16, const uint8_t* w_packed,
 /*
  * Host.  Writes a one-line text description of the tile nvfp4_linear uses for
  * an (N, K) weight into buf (NUL-terminated): the table entry, the K split and
- * the grid.  Errors: NULL, SHAPE, BUFFER, TILEFILE.
+ * the grid.  The tile is the per-shape table entry of "10 Kernels" 10.2 (launch
+ * settings a sweep picked, one per weight shape), keyed by (N, K) and never by
+ * the row count as 10.1 requires; tests read it to launch every kernel with
+ * the same K order.  Errors: NULL, SHAPE, BUFFER, TILEFILE.
  */
 int nvfp4_tile_info(int64_t n, int64_t k, char* buf, int64_t buflen);
 

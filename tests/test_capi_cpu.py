@@ -19,6 +19,31 @@ def _declared_functions():
     return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(nvfp4_\w+)\s*\(", text, re.M)))
 
 
+PAGES = ('"10 Kernels"', '"CUDA Kernel Engineering"', '"Module ops"')
+
+
+def _declaration_comments():
+    """{function: the comment block right above its declaration}."""
+    text = open(HEADER).read()
+    out = {}
+    for m in re.finditer(r"/\*(?:(?!\*/).)*\*/\s*(?:(?:int|const char\*)\s+)(nvfp4_\w+)\s*\(", text, re.S):
+        out[m.group(1)] = m.group(0)
+    return out
+
+
+def test_every_declaration_cites_a_passage():
+    # Each entry point's comment names the page (and section or entry) that
+    # defines what it does, or, for the entry point that allocates nothing,
+    # the callers it is for.
+    comments = _declaration_comments()
+    assert set(comments) == set(_declared_functions())
+    for name, block in comments.items():
+        if name == "nvfp4_strerror":
+            continue                      # static text of the status codes
+        cited = any(p in block for p in PAGES) or "cannot allocate" in block
+        assert cited, f"{name}: no passage cited in its declaration comment"
+
+
 def test_library_exports_every_declared_function():
     declared = _declared_functions()
     assert set(declared) == set(nv.EXPORTED)
@@ -266,3 +291,18 @@ def test_tile_override_file(tmp_path):
     assert _tile_info_in_fresh_process(str(f)) == f"status {nv.ERR_TILEFILE}"
     assert _tile_info_in_fresh_process(str(tmp_path / "missing.txt")) == f"status {nv.ERR_TILEFILE}"
     assert "cols=32" not in _tile_info_in_fresh_process(None)
+
+
+def test_build_rejects_kernels_that_spill():
+    # The build reads the compiler's per-kernel resource report and refuses a
+    # library in which any kernel spills registers to scratch memory.
+    from verify_nvfp4_w4a16_amd import build
+    report = "\n".join([
+        "x.hip:1:1: remark: Function Name: _Z1av [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:1:1: remark:     VGPRs: 80 [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:9:1: remark: Function Name: _Z1bv [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:9:1: remark:     ScratchSize [bytes/lane]: 44 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    assert build.scratch_users(report) == [("_Z1bv", 44)]
+    assert build.RESOURCE_REMARKS in " ".join([build.RESOURCE_REMARKS])

@@ -172,12 +172,73 @@ def test_row_blocks_do_not_change_the_result(monkeypatch):
     assert np.all(np.abs(oracle.linear_ref(x, packed, scales, 0.5) - a) <= gamma * bnd)
 
 
-def test_bound_is_sum_of_absolute_products():
-    packed, scales = workload.random_codes(4, 32, 16)
-    x = workload.activations_bf16(2, 32, 17)
-    bnd = oracle.bound(x, packed, scales, 1.0)
-    exact = _brute_force(x, packed, scales, 1.0)
-    assert np.all(bnd >= np.abs(np.array([[float(v) for v in r] for r in exact])))
+def _exact_abs_sums(x_bits, packed, scales, t):
+    """Sum over k of |x[m, k] * Wd[n, k]| in exact rationals, nibble by nibble."""
+    e2m1 = _golden_e2m1()
+    m, k = x_bits.shape
+    n = packed.shape[0]
+    tf = Fraction(float(np.float32(t)))
+    out = [[Fraction(0)] * n for _ in range(m)]
+    for i in range(m):
+        for j in range(n):
+            acc = Fraction(0)
+            for kk in range(k):
+                byte = int(packed[j, kk // 2])
+                code = (byte & 0xF) if kk % 2 == 0 else (byte >> 4)
+                w = tf * _exact_e4m3(int(scales[j, kk // 16])) * e2m1[code]
+                acc += abs(_bf16_fraction(int(x_bits[i, kk])) * w)
+            out[i][j] = acc
+    return out
+
+
+# Bound cases: tensor scales away from 1 (so a bound that drops t is caught),
+# shapes with several 16-k groups per row and rows in several row blocks.
+_BOUND_CASES = [(2, 9, 64, 0.000123, 31), (3, 5, 48, 37.5, 32), (1, 12, 32, 2.0 ** -20, 33)]
+
+
+def _bound_pinned(bound_fn, monkeypatch) -> bool:
+    """bound_fn(x, packed, scales, t, cols) equals the exact sum of |x * Wd|
+    to within the float64 rounding of a K-term sum, for full outputs (row-block
+    path, with blocks smaller than N) and for sampled columns."""
+    monkeypatch.setattr(olin, "ROW_BLOCK", 4)
+    ok = True
+    for m, n, k, t, seed in _BOUND_CASES:
+        packed, scales = workload.random_codes(n, k, seed)
+        scales[:, 0] = 0x7E                      # include the largest group scale
+        x = workload.activations_bf16(m, k, seed + 50, outliers=True)
+        exact = _exact_abs_sums(x, packed, scales, t)
+        gamma = Fraction(k + 1) * Fraction(1, 2 ** 53) * 2
+        cols = np.array([n - 1, 0, 3])
+        full = bound_fn(x, packed, scales, t, None)
+        some = bound_fn(x, packed, scales, t, cols)
+        for i in range(m):
+            for j in range(n):
+                e = exact[i][j]
+                ok &= abs(Fraction(float(full[i, j])) - e) <= gamma * e
+            for c, j in enumerate(cols):
+                e = exact[i][int(j)]
+                ok &= abs(Fraction(float(some[i, c])) - e) <= gamma * e
+    return bool(ok)
+
+
+def test_bound_is_sum_of_absolute_products(monkeypatch):
+    assert _bound_pinned(oracle.bound, monkeypatch)
+
+
+def test_bound_mutants_fail_the_pin(monkeypatch):
+    # Plausible mistakes in bound(): the tensor scale dropped, a constant
+    # factor, a signed (not absolute) sum, the activations' sign kept.
+    real = oracle.bound
+    mutants = {
+        "drops t": lambda x, p, s, t, c: real(x, p, s, 1.0, c),
+        "x4": lambda x, p, s, t, c: 4.0 * real(x, p, s, t, c),
+        "signed": lambda x, p, s, t, c: oracle.linear_ref(x, p, s, t, c),
+        "abs of x only": lambda x, p, s, t, c: (np.abs(olin.bf16_bits_to_f64(x)) @
+                                                (olin.dequant(p[c], s[c], t) if c is not None
+                                                 else olin.dequant(p, s, t)).T),
+    }
+    for name, fn in mutants.items():
+        assert not _bound_pinned(fn, monkeypatch), name
 
 
 def test_accept_tolerance():
@@ -209,10 +270,23 @@ def test_bf16_output_allowance_covers_exact_rounding():
     bnd = oracle.bound(x, packed, scales, 0.03)
     y16 = torch.from_numpy(y_ref).to(torch.bfloat16).double().numpy()
     assert oracle.accept(y16, y_ref, bnd, out="bf16")
-    # but a full bf16 ulp off is not
-    worst = np.abs(y_ref) >= 0.9 * bnd
-    if worst.any():
-        bumped = y16 + np.where(worst, np.abs(y16) * 2.0 ** -6, 0)
-        assert not oracle.accept(bumped, y_ref, bnd, out="bf16")
+    # but not an output a further bf16 step away.  One product decides the
+    # sum: x = 1 + 2^-7 (bf16), w = e2m1 1.5 at scale 1, so y_ref = bound =
+    # 1.51171875, halfway between the bf16 neighbours 1.5078125 and 1.515625.
+    # Both neighbours are accepted (they miss by 2^-8, which the 2e-3 term
+    # alone would reject); 1.5234375, one more step up, is not.
+    one_x = np.zeros((1, 32), np.uint16)
+    one_x[0, 3] = 0x3F81                                      # bf16 1 + 2^-7
+    one_p = np.zeros((1, 16), np.uint8)
+    one_p[0, 1] = 0x30                                        # k = 3: code 3 = 1.5
+    one_s = np.full((1, 2), 0x38, np.uint8)                   # scale 1.0
+    y1 = oracle.linear_ref(one_x, one_p, one_s, 1.0)
+    b1 = oracle.bound(one_x, one_p, one_s, 1.0)
+    assert y1[0, 0] == 1.51171875 and b1[0, 0] == y1[0, 0]
+    for near in (1.5078125, 1.515625):
+        assert not oracle.accept(np.array([[near]]), y1, b1, out="f32")
+        assert oracle.accept(np.array([[near]]), y1, b1, out="bf16")
+    assert not oracle.accept(np.array([[1.5234375]]), y1, b1, out="bf16")
+    assert not oracle.accept(np.array([[1.5]]), y1, b1, out="bf16")
     with pytest.raises(ValueError):
         oracle.tolerance(y_ref, bnd, out="f16")

@@ -6,6 +6,7 @@ Always recompiles every source.
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -38,12 +39,33 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _run(cmd: list[str]) -> None:
+def _run(cmd: list[str]) -> str:
     proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in proc.stdout.splitlines()
                     if "packed-fp32-ops' is not a recognized feature" not in l)
     if proc.returncode != 0:
         raise RuntimeError(f"build step failed ({proc.returncode}): {' '.join(cmd)}\n{out}")
+    return out
+
+
+# The compiler's per-kernel resource report (one remark block per kernel).
+RESOURCE_REMARKS = "-Rpass-analysis=kernel-resource-usage"
+
+
+def scratch_users(report: str) -> list[tuple[str, int]]:
+    """(kernel, bytes per lane) for every kernel in a resource report that
+    spills to scratch memory."""
+    users = []
+    name = None
+    for line in report.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name is not None and int(m.group(1)) > 0:
+            users.append((name, int(m.group(1))))
+    return users
 
 
 def build(verbose: bool = False) -> str:
@@ -60,10 +82,13 @@ def build(verbose: bool = False) -> str:
         objs.append(obj)
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-        cmd = [hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *HIP_FLAGS, RESOURCE_REMARKS, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        _run(cmd)
+        spills = scratch_users(_run(cmd))
+        if spills:
+            # every kernel the library can launch must keep its registers
+            raise RuntimeError(f"{src}: kernels spill to scratch: {spills}")
         objs.append(obj)
     tmp = LIB + ".tmp"
     cmd = [hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-pthread", *objs, "-o", tmp]

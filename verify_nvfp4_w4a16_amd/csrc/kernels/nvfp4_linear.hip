@@ -1131,19 +1131,27 @@ size_t split_lds_bytes(int64_t m, int w, int c) {
 using KernelFn = void (*)(Args);
 using SplitFn = void (*)(SplitArgs);
 
-template <int C, int MT, int U>
-KernelFn pick_out(bool xlds, int y_dtype) {
-    if (xlds)
-        return y_dtype == NVFP4_OUT_F32 ? nvfp4_skinny<C, MT, U, true, true> : nvfp4_skinny<C, MT, U, true, false>;
-    return y_dtype == NVFP4_OUT_F32 ? nvfp4_skinny<C, MT, U, false, true> : nvfp4_skinny<C, MT, U, false, false>;
+template <int C, int MT, int U, bool XLDS>
+KernelFn pick_out(int y_dtype) {
+    return y_dtype == NVFP4_OUT_F32 ? nvfp4_skinny<C, MT, U, XLDS, true> : nvfp4_skinny<C, MT, U, XLDS, false>;
+}
+
+// Pipeline depth of the generic kernel, capped where deeper steps would spill
+// registers to scratch (measured with the compiler's resource-usage report):
+// with A operands fetched per chunk (no x in LDS) one 128-k block per step,
+// and with four column tiles per wavefront at most two blocks per step.  The
+// depth never changes bits.
+constexpr int generic_unroll(int unroll, int c, bool xlds) {
+    return !xlds ? 1 : (c == 4 && unroll > 2) ? 2 : unroll;
 }
 
 template <int C, int MT>
 KernelFn pick_u(int unroll, bool xlds, int y_dtype) {
-    switch (unroll) {
-        case 1: return pick_out<C, MT, 1>(xlds, y_dtype);
-        case 2: return pick_out<C, MT, 2>(xlds, y_dtype);
-        default: return pick_out<C, MT, 4>(xlds, y_dtype);
+    if (!xlds) return pick_out<C, MT, 1, false>(y_dtype);
+    switch (generic_unroll(unroll, C, true)) {
+        case 1: return pick_out<C, MT, 1, true>(y_dtype);
+        case 2: return pick_out<C, MT, 2, true>(y_dtype);
+        default: return pick_out<C, MT, C == 4 ? 2 : 4, true>(y_dtype);
     }
 }
 
@@ -1465,16 +1473,14 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
                            dim3(static_cast<unsigned>(kWave * tile.waves)), tile_bytes, hs, a);
     } else {
         // The generic per-tile kernel (register loads, any shape); x goes
-        // through LDS when it fits in 64 KB.  With x fetched per chunk, one
-        // 128-k block per step keeps the A operands of two row tiles in
-        // registers (the pipeline depth never changes bits).
+        // through LDS when it fits in 64 KB.  pick_kernel caps the pipeline
+        // depth where a deeper one would spill (generic_unroll).
         const bool xlds = x_bytes <= size_t(64 * 1024);
         const size_t part_bytes = tile.waves > 1 ? size_t(tile.waves) * c * mt * 4 * kWave * sizeof(float) : 0;
         const size_t lds = xlds && x_bytes > part_bytes ? x_bytes : part_bytes;
         const dim3 grid(static_cast<unsigned>((n + tile.cols - 1) / tile.cols));
         const dim3 block(static_cast<unsigned>(kWave * tile.waves));
-        const int unroll = xlds ? tile.unroll : 1;
-        hipLaunchKernelGGL(pick_kernel(mt, tile.cols, unroll, xlds, y_dtype), grid, block, lds, hs, a);
+        hipLaunchKernelGGL(pick_kernel(mt, tile.cols, tile.unroll, xlds, y_dtype), grid, block, lds, hs, a);
     }
     if (hipGetLastError() != hipSuccess) return NVFP4_ERR_HIP;
     return NVFP4_OK;

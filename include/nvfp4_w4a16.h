@@ -104,15 +104,18 @@ int nvfp4_linear_shape_ok(int64_t m, int64_t n, int64_t k);
  * code objects and the (N, K) tile table once per process (the table may be
  * overridden by the file named in the environment variable NVFP4_TILES, read
  * here only), and sets up the current device's workspace once per device: 32
- * MiB of partial sums plus 1 MiB of flag words in uncached device memory, kept
- * until the process ends (the many-row kernel exchanges segment-group sums
- * through it).  Call on every device before capturing nvfp4_linear into a HIP
- * graph; the first nvfp4_linear call on a device runs it otherwise.  Safe to
- * call more than once.  If the workspace cannot be allocated, nvfp4_linear
- * still works (with kernels that do not need it) and gives the same bits.
- * Test hook, read here once per process: NVFP4_TEST_SPLIT_TIMEOUT=1 makes the
- * many-row kernel's producer workgroups skip their flags and its consumers
- * give up after a few polls, so tests can check that a time-out writes NaN.
+ * MiB of tagged partial sums plus 16 KiB of generation words in uncached
+ * device memory, zeroed once and kept until the process ends (the many-row
+ * kernel exchanges segment-group sums through it; generations only advance,
+ * so it is never cleared again).  Call on every device before capturing
+ * nvfp4_linear into a HIP graph; the first nvfp4_linear call on a device runs
+ * it otherwise.  Safe to call more than once.  If the workspace cannot be
+ * allocated, nvfp4_linear still works (with kernels that do not need it) and
+ * gives the same bits.
+ * Test hook, read once per process: NVFP4_TEST_SPLIT_TIMEOUT=1 makes the
+ * many-row kernel's producer workgroups store no partial sums, =2 makes them
+ * store them only after a long bounded delay; with either, its consumers give
+ * up after a few polls, so tests can check the time-out path.
  * Errors: HIP, DEVICE, TILEFILE.
  */
 int nvfp4_init(void);
@@ -139,12 +142,23 @@ int nvfp4_init(void);
  * workspace set up by nvfp4_init: such calls on one device must not overlap in
  * time (calls on one stream, or on streams ordered by events, never do).  A
  * workgroup that waits for another's partial sums gives up after about a
- * second and writes NaN to its outputs instead of hanging.
+ * second, writes NaN to its outputs instead of hanging and sets the device's
+ * time-out word (nvfp4_timeout_status).
  * Errors: NULL, SHAPE, ALIGN, DTYPE, HIP, DEVICE, TILEFILE.
  */
 int nvfp4_linear(const void* x_bf16, const uint8_t* w_packed,
                  const uint8_t* scales_e4m3, float tensor_scale, void* y,
                  int64_t m, int64_t n, int64_t k, int y_dtype, void* stream);
+
+/*
+ * Host, synchronous (waits for the current device to finish its work).  For
+ * callers that need to know whether an exchange of partial sums gave up (see
+ * nvfp4_linear): *timed_out = 1 if a many-row workgroup on the current device
+ * gave up waiting since the last call, else 0; the word is then cleared.
+ * "10 Kernels" 10.7 checks results before timing them; this is the check the
+ * bounded wait leaves to the host.  Errors: NULL, HIP, DEVICE, TILEFILE.
+ */
+int nvfp4_timeout_status(int* timed_out);
 
 /* Kernel choice of nvfp4_linear_tiled (nvfp4_linear always chooses itself).
  * Every kernel computes the same bits for the same tile waves and split. */
@@ -157,7 +171,10 @@ enum {
                                     for the wavefronts' x slices to fit the LDS */
     NVFP4_KERNEL_SPLIT = 3,      /* many-row kernel: one segment group per workgroup, x windows in LDS;
                                     needs K / waves % 512 == 0 and, for split > 1, the device workspace */
-    NVFP4_KERNEL_GENERIC = 4     /* one workgroup per column tile, register loads; any shape */
+    NVFP4_KERNEL_GENERIC = 4,    /* one workgroup per column tile, register loads; any shape */
+    NVFP4_KERNEL_WHOLE = 5       /* many-row kernel with every segment group of a column group in one
+                                    workgroup (two-level sum inside it, no workspace); needs
+                                    K / waves % 512 == 0 */
 };
 
 /*

@@ -194,7 +194,7 @@ def test_tiled_entry_validates_the_tile():
     assert call(16, 4, 2, split=3) == nv.ERR_TILE    # split not a power of two
     assert call(16, 2, 2, split=4) == nv.ERR_TILE    # more groups than segments
     assert call(16, 4, 2, mwaves=2) == nv.ERR_TILE   # many-row workgroups are 4, 6 or 8 wavefronts
-    assert call(16, 4, 2, kernel=5) == nv.ERR_TILE   # no such kernel
+    assert call(16, 4, 2, kernel=6) == nv.ERR_TILE   # no such kernel
     assert call(16, 4, 2, kernel=-1) == nv.ERR_TILE
     assert call(16, 2, 2, k=100) == nv.ERR_SHAPE
     assert call(16, 2, 2, m=0) == nv.OK              # M == 0: nothing launched
@@ -208,7 +208,8 @@ def test_tile_struct_matches_the_header():
     body = re.search(r"typedef struct nvfp4_tile \{(.*?)\} nvfp4_tile_t;", header, re.S).group(1)
     names = re.findall(r"int (\w+);", body)
     assert names == [f for f, _ in nv.Tile._fields_]
-    for name in ("KERNEL_AUTO", "KERNEL_PERSISTENT", "KERNEL_TILE", "KERNEL_SPLIT", "KERNEL_GENERIC"):
+    for name in ("KERNEL_AUTO", "KERNEL_PERSISTENT", "KERNEL_TILE", "KERNEL_SPLIT", "KERNEL_GENERIC",
+                 "KERNEL_WHOLE"):
         value = int(re.search(r"NVFP4_%s = (\d+)" % name, header).group(1))
         assert getattr(nv, name) == value
 

@@ -116,7 +116,7 @@ def test_subnormal_inputs_and_products_recorded():
     ref = bits(run(x, w, torch.float32)).clone()
     assert torch.equal(bits(run(x[:1], w, torch.float32)), ref[:1])
     xt = upload_bits(x)
-    for kernel in (nv.KERNEL_PERSISTENT, nv.KERNEL_TILE, nv.KERNEL_SPLIT, nv.KERNEL_GENERIC):
+    for kernel in (nv.KERNEL_PERSISTENT, nv.KERNEL_TILE, nv.KERNEL_SPLIT, nv.KERNEL_GENERIC, nv.KERNEL_WHOLE):
         yk = torch.empty((2, n), dtype=torch.float32, device=DEV)
         st = nv.linear_tiled_raw(xt.data_ptr(), w.wp.data_ptr(), w.sc.data_ptr(), w.t, yk.data_ptr(), 2, n, k,
                                  nv.OUT_F32, nv.table_tile(n, k).replace(kernel=kernel),
@@ -138,6 +138,7 @@ packed, scales, t = nv.pack(w)
 dev = torch.device("cuda:0")
 wp, sc = torch.from_numpy(packed).to(dev), torch.from_numpy(scales).to(dev)
 assert nv.table_tile(n, k).split > 1
+assert not nv.timeout_status()
 for m, expect_nan in ((17, True), (32, True), (1, False)):
     xb = workload.activations_bf16(m, k, 6 + m)
     x = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -145,8 +146,70 @@ for m, expect_nan in ((17, True), (32, True), (1, False)):
     torch.cuda.synchronize()
     nan = torch.isnan(y)
     assert bool(nan.all()) if expect_nan else not bool(nan.any()), (m, int(nan.sum()))
+    # the host sees the time-out through the status word, which reading clears
+    assert nv.timeout_status() == expect_nan, m
+    assert not nv.timeout_status()
 print("timeout path ok", flush=True)
 """
+
+_LATE_PRODUCER_CHILD = r"""
+import numpy as np, torch
+import verify_nvfp4_w4a16_amd as nv
+import workload
+# NVFP4_TEST_SPLIT_TIMEOUT=2: producers set their flags only long after their
+# consumer gave up.  A replayed graph reuses every launch argument, so the
+# next replay must not take those late flags (and the sums behind them) for
+# its own: every replay, with new x each time, must give NaN everywhere.
+n, k, m = 4096, 8192, 17
+w = workload.weights_f32(n, k, 5)
+packed, scales, t = nv.pack(w)
+dev = torch.device("cuda:0")
+wp, sc = torch.from_numpy(packed).to(dev), torch.from_numpy(scales).to(dev)
+assert nv.table_tile(n, k).split > 1
+nv.init()
+x = torch.empty((m, k), dtype=torch.bfloat16, device=dev)
+y = torch.empty((m, n), dtype=torch.float32, device=dev)
+s = torch.cuda.Stream()
+s.wait_stream(torch.cuda.current_stream())
+g = torch.cuda.CUDAGraph()
+with torch.cuda.stream(s):
+    with torch.cuda.graph(g, stream=s):
+        nv.linear(x, wp, sc, t, out=y)
+torch.cuda.current_stream().wait_stream(s)
+torch.cuda.synchronize()
+for rep in range(4):
+    xb = workload.activations_bf16(m, k, 40 + rep)
+    x.copy_(torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16))
+    y.fill_(0.0)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    finite = int(torch.isfinite(y).sum())
+    print(f"replay {rep}: finite outputs {finite}", flush=True)
+    assert finite == 0, (rep, finite)
+    assert nv.timeout_status()
+print("late producers ok", flush=True)
+"""
+
+
+def _run_child(code, mode):
+    import os, subprocess, sys
+    env = dict(os.environ, NVFP4_TEST_SPLIT_TIMEOUT=mode)
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env["PYTHONPATH"] = root + os.pathsep + os.path.join(root, "tests") + os.pathsep + env.get("PYTHONPATH", "")
+    r = subprocess.run([sys.executable, "-c", code], env=env, cwd=root, capture_output=True, text=True,
+                       timeout=300)
+    print(r.stdout[-2000:], r.stderr[-2000:], flush=True)
+    return r
+
+
+def test_replay_after_time_out_never_takes_late_flags():
+    # The generation word of a column group advances with every call, so a
+    # flag stored late by a timed-out call's producer never matches what a
+    # later call (here: the next replay of the same captured graph) waits for.
+    r = _run_child(_LATE_PRODUCER_CHILD, "2")
+    assert r.returncode == 0 and "late producers ok" in r.stdout
+
 
 
 def test_many_row_time_out_writes_nan():
@@ -154,11 +217,5 @@ def test_many_row_time_out_writes_nan():
     # many-row kernel set no flags and the consumers give up after a few
     # polls; every output of the product must then be NaN rather than a
     # hang or a partial sum.  The per-tile kernel (M = 1) has no exchange.
-    import os, subprocess, sys
-    env = dict(os.environ, NVFP4_TEST_SPLIT_TIMEOUT="1")
-    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-    env["PYTHONPATH"] = root + os.pathsep + os.path.join(root, "tests") + os.pathsep + env.get("PYTHONPATH", "")
-    r = subprocess.run([sys.executable, "-c", _TIMEOUT_CHILD], env=env, cwd=root, capture_output=True, text=True,
-                       timeout=300)
-    print(r.stdout[-2000:], r.stderr[-2000:], flush=True)
+    r = _run_child(_TIMEOUT_CHILD, "1")
     assert r.returncode == 0 and "timeout path ok" in r.stdout

@@ -42,7 +42,7 @@ def test_largest_k_every_kernel():
     alone = None
     for m in (1, 17, 32):
         outs = {}
-        for kernel in (nv.KERNEL_AUTO, nv.KERNEL_TILE, nv.KERNEL_PERSISTENT, nv.KERNEL_SPLIT, nv.KERNEL_GENERIC):
+        for kernel in (nv.KERNEL_AUTO, nv.KERNEL_TILE, nv.KERNEL_PERSISTENT, nv.KERNEL_SPLIT, nv.KERNEL_GENERIC, nv.KERNEL_WHOLE):
             st, y = _launch(xd, w.wp, w.sc, w.t, m, n, k, nv.table_tile(n, k).replace(kernel=kernel))
             if st == nv.ERR_TILE:
                 continue                                  # x does not fit this kernel's LDS
@@ -111,7 +111,7 @@ def test_smallest_shapes_every_kernel():
         for m in range(32, 0, -1):
             outs = {}
             for kernel in (nv.KERNEL_AUTO, nv.KERNEL_TILE, nv.KERNEL_PERSISTENT, nv.KERNEL_SPLIT,
-                           nv.KERNEL_GENERIC):
+                           nv.KERNEL_GENERIC, nv.KERNEL_WHOLE):
                 st, y = _launch(xd, w.wp, w.sc, w.t, m, 1, k, nv.table_tile(1, k).replace(kernel=kernel),
                                 out_dtype=torch.float32)
                 if st == nv.ERR_TILE:

@@ -21,12 +21,13 @@ ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_NONFINITE = -1, -2, -3, -4, -5
 ERR_BADSCALE, ERR_HIP, ERR_DEVICE, ERR_TILEFILE, ERR_BUFFER = -6, -7, -8, -9, -10
 ERR_TILE = -11
 OUT_BF16, OUT_F32 = 0, 1
-KERNEL_AUTO, KERNEL_PERSISTENT, KERNEL_TILE, KERNEL_SPLIT, KERNEL_GENERIC = 0, 1, 2, 3, 4
+KERNEL_AUTO, KERNEL_PERSISTENT, KERNEL_TILE, KERNEL_SPLIT, KERNEL_GENERIC, KERNEL_WHOLE = 0, 1, 2, 3, 4, 5
 MAX_M = 32
 K_MULTIPLE = 256
 
 EXPORTED = ("nvfp4_pack", "nvfp4_check_scales", "nvfp4_linear_shape_ok", "nvfp4_init",
-            "nvfp4_linear", "nvfp4_linear_tiled", "nvfp4_tile_info", "nvfp4_strerror")
+            "nvfp4_linear", "nvfp4_linear_tiled", "nvfp4_tile_info", "nvfp4_strerror",
+            "nvfp4_timeout_status")
 
 
 class Tile(ctypes.Structure):
@@ -66,6 +67,7 @@ def _load() -> ctypes.CDLL:
     lib.nvfp4_linear_tiled.argtypes = [vp, vp, vp, ctypes.c_float, vp, i64, i64, i64, ctypes.c_int,
                                        ctypes.POINTER(Tile), vp]
     lib.nvfp4_tile_info.argtypes = [i64, i64, ctypes.c_char_p, i64]
+    lib.nvfp4_timeout_status.argtypes = [ctypes.POINTER(ctypes.c_int)]
     lib.nvfp4_strerror.argtypes = [ctypes.c_int]
     lib.nvfp4_strerror.restype = ctypes.c_char_p
     for name in EXPORTED:
@@ -120,6 +122,14 @@ def linear_shape_ok(m: int, n: int, k: int) -> bool:
 
 def init() -> None:
     _check(_lib().nvfp4_init(), "nvfp4_init")
+
+
+def timeout_status() -> bool:
+    """True if a many-row workgroup on the current device gave up waiting for
+    partial sums since the last call (waits for the device; clears the word)."""
+    v = ctypes.c_int()
+    _check(_lib().nvfp4_timeout_status(ctypes.byref(v)), "nvfp4_timeout_status")
+    return bool(v.value)
 
 
 def tile_info(n: int, k: int) -> str:

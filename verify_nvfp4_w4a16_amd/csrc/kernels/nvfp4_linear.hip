@@ -111,6 +111,20 @@ __device__ __forceinline__ bf16x8 decode8(uint32_t w, float scale) {
     return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// fp32 <-> its bits through memcpy: with this compiler, bit-casting a vector
+// element (v[j]) yields element 0 for every j.
+__device__ __forceinline__ uint32_t f32_bits(float f) {
+    uint32_t u;
+    __builtin_memcpy(&u, &f, sizeof u);
+    return u;
+}
+
+__device__ __forceinline__ float bits_f32(uint32_t u) {
+    float f;
+    __builtin_memcpy(&f, &u, sizeof f);
+    return f;
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
     bf16x8 r;
     __builtin_memcpy(&r, &v, sizeof r);
@@ -872,41 +886,54 @@ size_t tile_lds_bytes(int64_t m, int64_t ks, int waves, int c, int nb) {
 
 // Many-row kernel (x too large to sit whole in one workgroup's LDS).  A
 // workgroup owns 16*C*W output columns (W wavefronts with C column tiles
-// each) and one segment group: K range [part * K/split, (part+1) * K/split),
-// i.e. `group` consecutive segments.  x comes into LDS in windows of 512 k
-// (one chunk), double-buffered, each row of a window one direct-to-LDS load;
-// every window is read by all W wavefronts, so x is fetched once per 16*C*W
-// columns instead of once per 16*C.  Each wavefront streams its weight chunks
-// through two LDS buffers of its own, runs the chains of the group's segments
-// one after the other and keeps the group sum (chains added in segment order).
+// each) and a K range of whole segment groups: one group when the groups of
+// a column group meet across workgroups (parts == split), all of them when
+// one workgroup runs the whole K (parts == 1).  x comes into LDS in windows
+// of 512 k (one chunk), double-buffered, each row of a window one
+// direct-to-LDS load; every window is read by all W wavefronts, so x is
+// fetched once per 16*C*W columns instead of once per 16*C.  Each wavefront
+// streams its weight chunks through two LDS buffers of its own, runs the
+// chains of its segments one after the other and adds them in the two-level
+// order (chains in segment order within a group, group sums in group order).
 //
-// With split == 1 that sum is the output.  Otherwise the column group's
-// `split` workgroups are blockIdx = part * groups + column_group: those of
-// parts 0..split-2 store their group sums in `work` (uncached device memory,
-// so a store that has completed is visible to every CU) and then write the
-// call's epoch (a nonzero number that differs between consecutive calls) to
-// their flag word; the workgroup of the last part waits for the flags to hold
-// the epoch (bounded: past the limit it writes NaN instead of hanging), adds
-// the group sums in group order with its own last, stores y and clears the
-// flags, so a replayed graph (same epoch) starts from clear flags too.  A flag
-// left behind by a call that timed out holds an old epoch and is ignored.
-// Workgroups are dispatched in index order, so each part's producers are
-// resident or done before its consumer waits, and producers never wait.  No
-// read-modify-write atomics are used.
+// With parts == split > 1 the column group's `split` workgroups are
+// blockIdx = part * groups + column_group and meet through device memory
+// (the uncached workspace).  Producers (parts 0..split-2) store each group sum
+// as one 64-bit word, a tag in the high half and the fp32 bits in the low
+// half, so no flag, fence or barrier has to order one location against
+// another: a consumer (the workgroup of the last part) that reads a word with
+// the tag it expects has read the value stored with it.  Tags come from
+// generation words, one per 1024-word block of the workspace.  A column
+// group's words sit in blocks of its own (its region is rounded up to whole
+// blocks), every workgroup reads the generations g of the blocks it touches as
+// it starts, producers tag with g + 1, and the consumer, once it has read
+// every word (bounded wait), advances each block of its region to g + 1.  Every
+// word's tag is therefore at most its block's generation, and a call waits for
+// a tag above it: no word left by an earlier call (another shape's, a replayed
+// graph's, a late producer's) is ever taken.  A consumer that gives up (about
+// a second) writes NaN to its outputs, sets the time-out word the host reads
+// with nvfp4_timeout_status and still advances its generations.  Workgroups
+// are dispatched in index order, so each part's producers are resident or done
+// before its consumer waits, and producers never wait.  No read-modify-write
+// atomics are used.
 struct SplitArgs {
     Args a;               // a.k_per_wave: segment length; a.group: segments per group
-    float* work;          // [groups][split-1][W][C][MT][4][64] fp32 group sums
-    uint32_t* flags;      // [groups][split]: `epoch` once a group sum is in `work`
-    uint32_t epoch;
-    int split;
+    uint64_t* work;       // column group g at work + g * region: [split-1][W][C][MT][4][64] tagged sums
+    uint32_t* gens;       // generation of each 1024-word block of `work`
+    int region;           // words per column group, a whole number of blocks
+    uint32_t* status;     // time-out word (set to 1 by a consumer that gave up)
+    int split;            // segment groups of the tile
+    int parts;            // workgroups per column group: split, or 1 (every group in one workgroup)
     int groups;           // column groups of 16*C*W
-    uint32_t spin_limit;  // polls of a flag before giving up
-    int drop_flags;       // test hook: producers set no flag, so the consumer times out
+    uint32_t spin_limit;  // polls of the tagged sums before giving up
+    int test_mode;        // test hook: 1 producers store nothing; 2 producers store late
 };
 
-constexpr uint32_t kSpinLimit = 1u << 20;   // polls of a flag before giving up (about a second)
+constexpr uint32_t kSpinLimit = 1u << 20;   // polls of the tagged sums before giving up (about a second)
 constexpr uint32_t kTestSpinLimit = 64;     // with the NVFP4_TEST_SPLIT_TIMEOUT hook
 constexpr int kXPitch = kChunkK + 8;        // LDS row pitch of an x window (bf16 elements)
+constexpr int kGenBlock = 1024;             // workspace words per generation word
+constexpr int kMaxParts = 8;                // largest split
 
 template <int C, int MT, int W, bool OUT_F32>
 __global__ void __launch_bounds__(64 * W)
@@ -920,10 +947,42 @@ nvfp4_skinny_split(SplitArgs sa) {
     const int kq = lane / 16;
     const int cgroup = (int)blockIdx.x % sa.groups;
     const int part = (int)blockIdx.x / sa.groups;
-    const int krange = a.k / sa.split;
+    const int krange = a.k / sa.parts;
     const int kbase = part * krange;
     const int nwin = krange / kChunkK;
     const int seg_chunks = a.k_per_wave / kChunkK;
+    const int group_chunks = seg_chunks * a.group;
+    const bool exchange = sa.parts > 1;
+    // Exchange words of this lane: part q's row i (of kVals) is word
+    // region0 + q * kSlot + lrow + 64 i (+ lane).  The generations of their
+    // blocks are read as the workgroup starts (waited for only where they are
+    // used, after the last window): for each part whose words the lane
+    // touches, those of the blocks of its first and last row (the rows of one
+    // part span at most two blocks); the consumer's wavefront 0 also reads one
+    // block of its region per lane, the ones it advances at the end.
+    constexpr int kSlot = W * C * MT * 4 * kWave;
+    constexpr int kVals = C * MT * 4;
+    const int64_t region0 = (int64_t)cgroup * sa.region;
+    const int lrow = wave * kVals * kWave;
+    auto blk = [&](int q, int i) { return (region0 + (int64_t)q * kSlot + lrow + i * kWave) / kGenBlock; };
+    uint32_t glo[kMaxParts - 1] = {}, ghi[kMaxParts - 1] = {};
+    uint32_t gown = 0;
+    const int nblk = exchange ? ((sa.split - 1) * kSlot + kGenBlock - 1) / kGenBlock : 0;
+    if (exchange) {
+        const bool consumer = part == sa.split - 1;
+#pragma unroll
+        for (int q = 0; q < kMaxParts - 1; ++q)
+            if ((consumer && q < sa.split - 1) || q == part) {
+                glo[q] = __hip_atomic_load(sa.gens + blk(q, 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ghi[q] = __hip_atomic_load(sa.gens + blk(q, kVals - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        // (every lane of every part loads it, clamped, to keep the load out
+        // of a divergent branch)
+        gown = __hip_atomic_load(sa.gens + region0 / kGenBlock + min(lane, nblk - 1), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // tag of row i of part q: one above its block's generation
+    auto tag_of = [&](int q, int i) { return (blk(q, i) == blk(q, 0) ? glo[q] : ghi[q]) + 1; };
     const int slice = a.m * kXPitch;
     const int col_base = (cgroup * W + wave) * 16 * C;
     const uint32_t row_bytes = static_cast<uint32_t>(a.k) / 2;
@@ -954,11 +1013,11 @@ nvfp4_skinny_split(SplitArgs sa) {
                              kb, lane);
     };
 
-    f32x4 acc[C][MT], grp[C][MT];
+    f32x4 acc[C][MT], grp[C][MT], tot[C][MT];
 #pragma unroll
     for (int c = 0; c < C; ++c)
 #pragma unroll
-        for (int t = 0; t < MT; ++t) acc[c][t] = grp[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < MT; ++t) acc[c][t] = grp[c][t] = tot[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     auto compute_half = [&](int win, auto h) {
         mma_half<C, MT, decltype(h)::value>(acc, wbuf + (win & 1) * C * kTileBytes, lds + (win & 1) * slice,
@@ -971,10 +1030,12 @@ nvfp4_skinny_split(SplitArgs sa) {
         compute_half(win, std::integral_constant<int, 0>{});
         wait_vm<decltype(after)::value>();
         compute_half(win, std::integral_constant<int, 1>{});
-        // end of a segment: its chain joins the group sum (the first chain
-        // is taken as it is, so a -0 sum keeps its sign)
+        // end of a segment: its chain joins the group sum; at the end of a
+        // group (several per workgroup only when parts == 1) the group sum
+        // joins the total.  The first chain and the first group sum are
+        // taken as they are, so a -0 sum keeps its sign.
         if ((win + 1) % seg_chunks == 0) {
-            const bool first = win + 1 == seg_chunks;
+            const bool first = (win + 1 - seg_chunks) % group_chunks == 0;
 #pragma unroll
             for (int c = 0; c < C; ++c)
 #pragma unroll
@@ -982,6 +1043,13 @@ nvfp4_skinny_split(SplitArgs sa) {
                     grp[c][t] = first ? acc[c][t] : grp[c][t] + acc[c][t];
                     acc[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
+            if (!exchange && (win + 1) % group_chunks == 0) {
+                const bool gfirst = win + 1 == group_chunks;
+#pragma unroll
+                for (int c = 0; c < C; ++c)
+#pragma unroll
+                    for (int t = 0; t < MT; ++t) tot[c][t] = gfirst ? grp[c][t] : tot[c][t] + grp[c][t];
+            }
         }
     };
 
@@ -1021,63 +1089,63 @@ nvfp4_skinny_split(SplitArgs sa) {
         compute(win, std::integral_constant<int, 0>{});
     }
 
-    if (sa.split > 1) {
-        constexpr int kSlot = W * C * MT * 4 * kWave;   // floats of one workgroup's group sums
+    if (exchange) {
         const int P = sa.split;
-        float* work = sa.work + (size_t)cgroup * (P - 1) * kSlot;
-        uint32_t* flags = sa.flags + (size_t)cgroup * P;
-        const int base = wave * C * MT * 4 * kWave + lane;
+        uint64_t* work = sa.work + region0;
+        const int base = lrow + lane;
         if (part < P - 1) {
-            float* slot = work + (size_t)part * kSlot + base;
+            if (sa.test_mode == 1) return;                   // test hook: nothing arrives
+            if (sa.test_mode == 2)                           // test hook: a producer far behind its consumer
+                for (int i = 0; i < 4096; ++i) __builtin_amdgcn_s_sleep(127);
+            uint64_t* slot = work + (size_t)part * kSlot + base;
 #pragma unroll
-            for (int c = 0; c < C; ++c)
+            for (int q = 0; q < kMaxParts - 1; ++q)
+                if (q == part)
 #pragma unroll
-                for (int t = 0; t < MT; ++t)
+                    for (int c = 0; c < C; ++c)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) slot[((c * MT + t) * 4 + j) * kWave] = grp[c][t][j];
-            // every store of the workgroup has completed before the flag is set
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            if (threadIdx.x == 0 && !sa.drop_flags)
-                __hip_atomic_store(flags + part, sa.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        for (int t = 0; t < MT; ++t)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                const int i = (c * MT + t) * 4 + j;
+                                __hip_atomic_store(slot + i * kWave,
+                                                   (uint64_t(tag_of(q, i)) << 32) |
+                                                       f32_bits(grp[c][t][j]),
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            }
             return;
         }
-        __shared__ uint32_t timed_out;
-        if (threadIdx.x == 0) timed_out = 0;
-        __syncthreads();
-        if ((int)threadIdx.x < P - 1) {
-            // Two polls in flight: each round issues the next load before
-            // looking at the previous one, halving the time between a flag
-            // landing and its being seen.
-            const uint32_t* f = flags + threadIdx.x;
-            uint32_t prev = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // The consumer reads the tagged sums of the parts in batches (all
+        // loads of a batch in flight together) until every tag of the batch
+        // is this call's, polling a bounded number of times; then adds them
+        // in group order, its own last.  Each wavefront waits on its own
+        // lanes' words only.
+        constexpr int kBatch = 32 / kVals;
+        bool bad = false;
+#pragma unroll
+        for (int q0 = 0; q0 < kMaxParts - 1; q0 += kBatch) {
+            if (q0 >= P - 1 || bad) break;
+            uint64_t v[kBatch][kVals];
             for (uint32_t spins = 0;; ++spins) {
-                const uint32_t next = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (prev == sa.epoch) break;
+#pragma unroll
+                for (int b = 0; b < kBatch; ++b)
+                    if (q0 + b < P - 1)
+#pragma unroll
+                        for (int i = 0; i < kVals; ++i)
+                            v[b][i] = __hip_atomic_load(work + (size_t)(q0 + b) * kSlot + base + i * kWave,
+                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                bool here = true;
+#pragma unroll
+                for (int b = 0; b < kBatch; ++b)
+                    if (q0 + b < P - 1)
+#pragma unroll
+                        for (int i = 0; i < kVals; ++i) here &= uint32_t(v[b][i] >> 32) == tag_of(q0 + b, i);
+                if (__all(here)) break;
                 if (spins >= sa.spin_limit) {
-                    timed_out = 1;
+                    bad = true;
                     break;
                 }
                 __builtin_amdgcn_s_sleep(1);
-                prev = next;
-            }
-        }
-        __syncthreads();
-        // The group sums are read in batches of parts, all loads of a batch
-        // in flight together (one round trip per batch, not per part); a
-        // batch past the last part re-reads that part (unused), so the loads
-        // need no branches.
-        constexpr int kVals = C * MT * 4;
-        constexpr int kBatch = 32 / kVals;
-        f32x4 tot[C][MT] = {};
-        for (int q0 = 0; q0 < P - 1; q0 += kBatch) {
-            float v[kBatch][kVals];
-#pragma unroll
-            for (int b = 0; b < kBatch; ++b) {
-                const float* slot = work + (size_t)min(q0 + b, P - 2) * kSlot + base;
-#pragma unroll
-                for (int i = 0; i < kVals; ++i)
-                    v[b][i] = __hip_atomic_load(slot + i * kWave, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
 #pragma unroll
             for (int b = 0; b < kBatch; ++b)
@@ -1088,11 +1156,10 @@ nvfp4_skinny_split(SplitArgs sa) {
                         for (int t = 0; t < MT; ++t)
 #pragma unroll
                             for (int j = 0; j < 4; ++j) {
-                                const float g = v[b][(c * MT + t) * 4 + j];
+                                const float g = bits_f32(uint32_t(v[b][(c * MT + t) * 4 + j]));
                                 tot[c][t][j] = q0 + b == 0 ? g : tot[c][t][j] + g;
                             }
         }
-        const bool bad = timed_out != 0;
 #pragma unroll
         for (int c = 0; c < C; ++c)
 #pragma unroll
@@ -1100,8 +1167,20 @@ nvfp4_skinny_split(SplitArgs sa) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     grp[c][t][j] = bad ? __builtin_nanf("") : tot[c][t][j] + grp[c][t][j];
-        if ((int)threadIdx.x < P - 1)
-            __hip_atomic_store(flags + threadIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (bad && lane == 0) __hip_atomic_store(sa.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // The next call on these blocks waits for the next tag.  (The empty
+        // asm keeps the compiler from adding 1 to the loaded generation right
+        // after its load, which would wait for it before the first window.)
+        asm volatile("" : "+v"(gown));
+        if (wave == 0 && lane < nblk)
+            __hip_atomic_store(sa.gens + region0 / kGenBlock + lane, gown + 1, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    } else if (a.group < a.k / a.k_per_wave) {
+        // every group in this workgroup: the output is the total
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int t = 0; t < MT; ++t) grp[c][t] = tot[c][t];
     }
 
 #pragma unroll
@@ -1218,18 +1297,29 @@ SplitFn pick_split(int mt, int c, int w, int y_dtype) {
     return mt == 1 ? pick_s_w<1>(c, w, y_dtype) : pick_s_w<2>(c, w, y_dtype);
 }
 
-// Per-device state, set up once per device by nvfp4_init (or the first call
-// on that device).
 constexpr int kMaxDevices = 64;
-constexpr size_t kWorkBytes = size_t(32) << 20;      // group sums of the many-row kernel
-constexpr size_t kFlagWords = size_t(1) << 18;       // 1 MiB of flag words
+constexpr size_t kWorkBytes = size_t(32) << 20;      // tagged group sums of the many-row kernel
+constexpr size_t kGenWords = kWorkBytes / sizeof(uint64_t) / kGenBlock;   // one per block of them
+constexpr size_t kStatusWords = 64;                  // the time-out word, on its own 256 bytes
+
+// Where the many-row kernel's column groups meet: tagged group sums, the
+// generation words of their blocks, the time-out word.  All start at zero;
+// generations only ever advance, so the memory is never cleared again.
+struct Workspace {
+    float* sums = nullptr;
+    uint32_t* gens = nullptr;
+    uint32_t* status = nullptr;
+    size_t sum_bytes = 0;
+    size_t gen_words = 0;
+};
+
+// Per-device state: the set-up that allocates nothing (kernel attributes),
+// and the uncached workspace nvfp4_init allocates.
 struct DeviceState {
-    std::once_flag once;
-    int status = NVFP4_OK;
+    std::once_flag setup_once, alloc_once;
+    int setup_status = NVFP4_OK;
     int cus = 0;
-    float* work = nullptr;          // uncached, never freed
-    uint32_t* flags = nullptr;      // uncached, zero between calls, never freed
-    std::atomic<uint32_t> epoch{0};
+    Workspace heap;                 // uncached device memory, never freed
 };
 DeviceState g_dev[kMaxDevices];
 
@@ -1243,7 +1333,8 @@ bool allow_full_lds(Fn fn) {
     return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) == hipSuccess;
 }
 
-int init_device(int dev) {
+// Set-up of the current device `dev`, once per device; allocates nothing.
+int setup_device(int dev) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return NVFP4_ERR_HIP;
     if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return NVFP4_ERR_DEVICE;
@@ -1268,28 +1359,39 @@ int init_device(int dev) {
                 for (int w = 4; w <= 8; w += 2)
                     if (!allow_full_lds(pick_split(mt, c, w, od))) return NVFP4_ERR_HIP;
         }
-    // Workspace of the many-row kernel.  Without it that kernel runs only
-    // where the tile has split == 1 (the other kernels give the same bits).
+    return NVFP4_OK;
+}
+
+// The uncached workspace of `dev`, once per device.  Without it the
+// many-row kernel runs only where no exchange is needed (the other kernels
+// give the same bits).
+void alloc_workspace(int dev) {
+    DeviceState& d = g_dev[dev];
     void* work = nullptr;
-    void* flags = nullptr;
+    void* gens = nullptr;
+    const size_t gen_bytes = (kGenWords + kStatusWords) * sizeof(uint32_t);
     if (hipExtMallocWithFlags(&work, kWorkBytes, hipDeviceMallocUncached) == hipSuccess &&
-        hipExtMallocWithFlags(&flags, kFlagWords * sizeof(uint32_t), hipDeviceMallocUncached) == hipSuccess &&
-        hipMemset(flags, 0, kFlagWords * sizeof(uint32_t)) == hipSuccess && hipDeviceSynchronize() == hipSuccess) {
-        d.work = static_cast<float*>(work);
-        d.flags = static_cast<uint32_t*>(flags);
+        hipExtMallocWithFlags(&gens, gen_bytes, hipDeviceMallocUncached) == hipSuccess &&
+        hipMemset(gens, 0, gen_bytes) == hipSuccess && hipMemset(work, 0, kWorkBytes) == hipSuccess &&
+        hipDeviceSynchronize() == hipSuccess) {
+        d.heap.sums = static_cast<float*>(work);
+        d.heap.gens = static_cast<uint32_t*>(gens);
+        d.heap.status = d.heap.gens + kGenWords;
+        d.heap.sum_bytes = kWorkBytes;
+        d.heap.gen_words = kGenWords;
     } else {
         (void)hipGetLastError();   // clear the failure; the memory (if any) stays unused
     }
-    return NVFP4_OK;
 }
 
 std::once_flag g_init_once;
 int g_init_status = NVFP4_OK;
-// Test hook, read once per process: with NVFP4_TEST_SPLIT_TIMEOUT=1 the
-// many-row kernel's producers set no flags and its consumers give up after a
-// few polls, so a test can see the time-out path write NaN (every kernel
-// still exits normally).
-bool g_test_split_timeout = false;
+// Test hook, read once per process (NVFP4_TEST_SPLIT_TIMEOUT): 1 makes the
+// many-row kernel's producers store no group sums, 2 makes them store them
+// only after a long bounded delay; either way its consumers give up after a
+// few polls, so a test can see the time-out path (every kernel still exits
+// normally).
+int g_test_split_timeout = 0;
 
 int current_device(int* dev) {
     if (hipGetDevice(dev) != hipSuccess) return NVFP4_ERR_HIP;
@@ -1297,21 +1399,54 @@ int current_device(int* dev) {
     return NVFP4_OK;
 }
 
-}  // namespace
-
-extern "C" int nvfp4_init(void) {
+// Process-wide set-up (test hook, tile override) and the current device's
+// set-up; allocates nothing.  *dev is the current device.
+int setup_current(int* dev) {
     std::call_once(g_init_once, [] {
         const char* hook = std::getenv("NVFP4_TEST_SPLIT_TIMEOUT");
-        g_test_split_timeout = hook && std::strcmp(hook, "1") == 0;
+        g_test_split_timeout = hook ? std::atoi(hook) : 0;
+        if (g_test_split_timeout != 1 && g_test_split_timeout != 2) g_test_split_timeout = 0;
         g_init_status = nvfp4::load_tile_override();
     });
     if (g_init_status != NVFP4_OK) return g_init_status;
+    int st = current_device(dev);
+    if (st != NVFP4_OK) return st;
+    DeviceState& d = g_dev[*dev];
+    std::call_once(d.setup_once, [&] { d.setup_status = setup_device(*dev); });
+    return d.setup_status;
+}
+
+}  // namespace
+
+extern "C" int nvfp4_init(void) {
     int dev = 0;
-    int st = current_device(&dev);
+    const int st = setup_current(&dev);
     if (st != NVFP4_OK) return st;
     DeviceState& d = g_dev[dev];
-    std::call_once(d.once, [&] { d.status = init_device(dev); });
-    return d.status;
+    std::call_once(d.alloc_once, [&] { alloc_workspace(dev); });
+    return NVFP4_OK;
+}
+
+extern "C" int nvfp4_timeout_status(int* timed_out) {
+    if (!timed_out) return NVFP4_ERR_NULL;
+    int dev = 0;
+    const int st = setup_current(&dev);
+    if (st != NVFP4_OK) return st;
+    DeviceState& d = g_dev[dev];
+    if (hipDeviceSynchronize() != hipSuccess) return NVFP4_ERR_HIP;
+    uint32_t any = 0;
+    for (const Workspace* w : {&d.heap}) {
+        if (!w->status) continue;
+        uint32_t v = 0;
+        if (hipMemcpy(&v, w->status, sizeof v, hipMemcpyDeviceToHost) != hipSuccess) return NVFP4_ERR_HIP;
+        if (v != 0) {
+            const uint32_t zero = 0;
+            if (hipMemcpy(w->status, &zero, sizeof zero, hipMemcpyHostToDevice) != hipSuccess) return NVFP4_ERR_HIP;
+        }
+        any |= v;
+    }
+    *timed_out = any != 0;
+    return NVFP4_OK;
 }
 
 extern "C" int nvfp4_tile_info(int64_t n, int64_t k, char* buf, int64_t buflen) {
@@ -1327,13 +1462,18 @@ extern "C" int nvfp4_tile_info(int64_t n, int64_t k, char* buf, int64_t buflen) 
 namespace {
 
 // Launch plan of the many-row kernel; false if it cannot run this call.
+// `ws` is the workspace the call may use (NULL: none), `parts` what runs:
+// split when the groups meet through the workspace, else 1.
 struct SplitPlan {
     int c = 1, w = 8;
+    int parts = 1;
+    int64_t region = 0;             // exchange words per column group
     int64_t groups = 0;
     size_t lds = 0;
 };
 
-bool plan_split(const nvfp4::Tile& tile, int64_t m, int64_t n, int64_t k, const DeviceState& d, SplitPlan* p) {
+bool plan_split(const nvfp4::Tile& tile, int64_t m, int64_t n, int64_t k, const Workspace* ws, bool whole,
+                SplitPlan* p) {
     const int64_t seg = k / tile.waves;
     if (seg % kChunkK != 0) return false;
     p->c = tile.cols == 16 ? 1 : 2;
@@ -1344,12 +1484,17 @@ bool plan_split(const nvfp4::Tile& tile, int64_t m, int64_t n, int64_t k, const 
     p->groups = (n + cols - 1) / cols;
     p->lds = split_lds_bytes(m, p->w, p->c);
     if (p->lds + 256 > size_t(kMaxLdsBytes)) return false;
-    if (tile.split > 1) {
+    p->parts = 1;
+    if (tile.split > 1 && !whole) {
         const int mt = m <= 16 ? 1 : 2;
-        const size_t slot = size_t(p->w) * p->c * mt * 4 * kWave * sizeof(float);
-        if (!d.work || !d.flags) return false;
-        if (size_t(p->groups) * (tile.split - 1) * slot > kWorkBytes) return false;
-        if (size_t(p->groups) * tile.split > kFlagWords) return false;
+        const int64_t slot = int64_t(p->w) * p->c * mt * 4 * kWave;     // words of one workgroup
+        p->region = ((tile.split - 1) * slot + kGenBlock - 1) / kGenBlock * kGenBlock;
+        if (!ws || !ws->sums) return false;
+        // the words, and one generation word per block of them
+        if (size_t(p->groups) * size_t(p->region) * sizeof(uint64_t) > ws->sum_bytes ||
+            size_t(p->groups) * size_t(p->region) / kGenBlock > ws->gen_words)
+            return false;
+        p->parts = tile.split;
     }
     return p->groups * tile.split <= int64_t(0x7fffffff);
 }
@@ -1372,6 +1517,7 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
     st = current_device(&dev);
     if (st != NVFP4_OK) return st;
     const DeviceState& d = g_dev[dev];
+    const Workspace* ws = &d.heap;
 
     const int mt = m <= 16 ? 1 : 2;
     Args a;
@@ -1399,7 +1545,9 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
     const bool pers_ok = tile.cols <= 32 && (k / tile.waves) % kChunkK == 0 &&
                          pers_bytes + 256 <= size_t(kMaxLdsBytes) && x_bytes <= size_t(64 * 1024);
     SplitPlan plan;
-    const bool split_ok = plan_split(tile, m, n, k, d, &plan);
+    const bool whole = kernel == NVFP4_KERNEL_WHOLE;
+    const bool split_ok = plan_split(tile, m, n, k, ws, whole, &plan);
+    if (whole) kernel = NVFP4_KERNEL_SPLIT;
     // The per-tile kernel: each wavefront's x slice and chunk buffers (up to
     // three, at most one per chunk of its segment) within the LDS: the most
     // that fit, except that where a CU has to take several workgroups, fewer
@@ -1445,7 +1593,6 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
         return NVFP4_ERR_TILE;
 
     if (kernel == NVFP4_KERNEL_PERSISTENT) {
-        const int cus = d.cus > 0 ? d.cus : 256;
         const int64_t tiles = (n + tile.cols - 1) / tile.cols;
         const int per_cu = std::max(1, std::min(64 / tile.waves, int(kMaxLdsBytes / (pers_bytes + 256))));
         const int64_t grid_p = tiles < int64_t(per_cu) * cus ? tiles : int64_t(per_cu) * cus;
@@ -1455,18 +1602,17 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
     } else if (kernel == NVFP4_KERNEL_SPLIT) {
         SplitArgs sa;
         sa.a = a;
-        sa.work = d.work;
-        sa.flags = d.flags;
+        sa.work = reinterpret_cast<uint64_t*>(ws->sums);
+        sa.gens = ws->gens;
+        sa.region = static_cast<int>(plan.region);
+        sa.status = ws->status;
         sa.split = tile.split;
+        sa.parts = plan.parts;
         sa.spin_limit = g_test_split_timeout ? kTestSpinLimit : kSpinLimit;
-        sa.drop_flags = g_test_split_timeout ? 1 : 0;
+        sa.test_mode = g_test_split_timeout;
         sa.groups = static_cast<int>(plan.groups);
-        DeviceState& dm = g_dev[dev];
-        uint32_t e = dm.epoch.fetch_add(1, std::memory_order_relaxed) + 1;
-        if (e == 0) e = dm.epoch.fetch_add(1, std::memory_order_relaxed) + 1;   // 0 means clear
-        sa.epoch = e;
         hipLaunchKernelGGL(pick_split(mt, plan.c, plan.w, y_dtype),
-                           dim3(static_cast<unsigned>(plan.groups * tile.split)),
+                           dim3(static_cast<unsigned>(plan.groups * plan.parts)),
                            dim3(static_cast<unsigned>(kWave * plan.w)), plan.lds, hs, sa);
     } else if (kernel == NVFP4_KERNEL_TILE) {
         hipLaunchKernelGGL(pick_tile(mt, pc, tnb, y_dtype), dim3(static_cast<unsigned>((n + 16 * pc - 1) / (16 * pc))),
@@ -1511,6 +1657,6 @@ extern "C" int nvfp4_linear_tiled(const void* x_bf16, const uint8_t* w_packed, c
     tile.split = t->split;
     tile.mwaves = t->mwaves;
     if (!nvfp4::tile_valid(tile, n, k)) return NVFP4_ERR_TILE;
-    if (t->kernel < NVFP4_KERNEL_AUTO || t->kernel > NVFP4_KERNEL_GENERIC) return NVFP4_ERR_TILE;
+    if (t->kernel < NVFP4_KERNEL_AUTO || t->kernel > NVFP4_KERNEL_WHOLE) return NVFP4_ERR_TILE;
     return launch(x_bf16, w_packed, scales_e4m3, tensor_scale, y, m, n, k, y_dtype, stream, tile, t->kernel);
 }

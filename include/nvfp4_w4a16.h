@@ -52,7 +52,8 @@ enum {
     NVFP4_ERR_DEVICE = -8,    /* the current device is not gfx950 */
     NVFP4_ERR_TILEFILE = -9,  /* the NVFP4_TILES override file is unreadable or invalid */
     NVFP4_ERR_BUFFER = -10,   /* nvfp4_tile_info: the text buffer is too small */
-    NVFP4_ERR_TILE = -11      /* nvfp4_linear_tiled: the tile does not fit the shape */
+    NVFP4_ERR_TILE = -11,     /* nvfp4_linear_tiled: the tile does not fit the shape */
+    NVFP4_ERR_SCRATCH = -12   /* nvfp4_linear_noalloc: the call needs more than the fixed scratch */
 };
 
 /* Largest row count of one nvfp4_linear call. */
@@ -159,6 +160,31 @@ int nvfp4_linear(const void* x_bf16, const uint8_t* w_packed,
  * bounded wait leaves to the host.  Errors: NULL, HIP, DEVICE, TILEFILE.
  */
 int nvfp4_timeout_status(int* timed_out);
+
+/*
+ * Device, asynchronous: nvfp4_linear for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, results (bits) and errors as
+ * nvfp4_linear, plus SCRATCH.  It never allocates: neither this call nor its
+ * set-up calls hipMalloc, hipFree or any allocating routine.  Where
+ * nvfp4_linear exchanges partial sums through the workspace nvfp4_init
+ * allocates, this call uses a fixed scratch array built into the library
+ * instead: 8 MiB of tagged sums plus 4 KiB of generation words per device,
+ * held by each device the library runs on until the process ends.  A call
+ * whose exchange needs more returns NVFP4_ERR_SCRATCH and launches nothing:
+ * a column group takes (split - 1) x 2 KiB per 16-row tile, 16-column tile and
+ * wavefront of its workgroups, e.g. 224 KiB for 128 columns at 17..32 rows and
+ * split 8, so N up to 4608 fits there; every product of the 48-layer decode
+ * round fits.  Every call on a device shares that device's array, which keeps the last call's contents (no
+ * clearing is needed: generations only advance); calls on one device that
+ * overlap in time race on it, as calls of nvfp4_linear do on the workspace.
+ * The first call on a device does the device's set-up (kernel attributes, the
+ * array's device address) unless nvfp4_init has done it.
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, HIP, DEVICE, TILEFILE, SCRATCH.
+ */
+int nvfp4_linear_noalloc(const void* x_bf16, const uint8_t* w_packed,
+                         const uint8_t* scales_e4m3, float tensor_scale, void* y,
+                         int64_t m, int64_t n, int64_t k, int y_dtype, void* stream);
 
 /* Kernel choice of nvfp4_linear_tiled (nvfp4_linear always chooses itself).
  * Every kernel computes the same bits for the same tile waves and split. */

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "libnvfp4_w4a16.so")
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_NONFINITE = -1, -2, -3, -4, -5
 ERR_BADSCALE, ERR_HIP, ERR_DEVICE, ERR_TILEFILE, ERR_BUFFER = -6, -7, -8, -9, -10
-ERR_TILE = -11
+ERR_TILE, ERR_SCRATCH = -11, -12
 OUT_BF16, OUT_F32 = 0, 1
 KERNEL_AUTO, KERNEL_PERSISTENT, KERNEL_TILE, KERNEL_SPLIT, KERNEL_GENERIC, KERNEL_WHOLE = 0, 1, 2, 3, 4, 5
 MAX_M = 32
@@ -27,7 +27,7 @@ K_MULTIPLE = 256
 
 EXPORTED = ("nvfp4_pack", "nvfp4_check_scales", "nvfp4_linear_shape_ok", "nvfp4_init",
             "nvfp4_linear", "nvfp4_linear_tiled", "nvfp4_tile_info", "nvfp4_strerror",
-            "nvfp4_timeout_status")
+            "nvfp4_timeout_status", "nvfp4_linear_noalloc")
 
 
 class Tile(ctypes.Structure):
@@ -64,6 +64,7 @@ def _load() -> ctypes.CDLL:
     lib.nvfp4_linear_shape_ok.argtypes = [i64, i64, i64]
     lib.nvfp4_init.argtypes = []
     lib.nvfp4_linear.argtypes = [vp, vp, vp, ctypes.c_float, vp, i64, i64, i64, ctypes.c_int, vp]
+    lib.nvfp4_linear_noalloc.argtypes = [vp, vp, vp, ctypes.c_float, vp, i64, i64, i64, ctypes.c_int, vp]
     lib.nvfp4_linear_tiled.argtypes = [vp, vp, vp, ctypes.c_float, vp, i64, i64, i64, ctypes.c_int,
                                        ctypes.POINTER(Tile), vp]
     lib.nvfp4_tile_info.argtypes = [i64, i64, ctypes.c_char_p, i64]
@@ -149,6 +150,13 @@ def linear_raw(x_ptr: int, w_ptr: int, s_ptr: int, tensor_scale: float, y_ptr: i
     """nvfp4_linear on raw device addresses; returns the status."""
     return _lib().nvfp4_linear(x_ptr, w_ptr, s_ptr, ctypes.c_float(tensor_scale), y_ptr,
                             m, n, k, y_dtype, stream)
+
+
+def linear_noalloc_raw(x_ptr: int, w_ptr: int, s_ptr: int, tensor_scale: float, y_ptr: int,
+                       m: int, n: int, k: int, y_dtype: int, stream: int) -> int:
+    """nvfp4_linear_noalloc on raw device addresses; returns the status."""
+    return _lib().nvfp4_linear_noalloc(x_ptr, w_ptr, s_ptr, ctypes.c_float(tensor_scale), y_ptr,
+                                       m, n, k, y_dtype, stream)
 
 
 def linear_tiled_raw(x_ptr: int, w_ptr: int, s_ptr: int, tensor_scale: float, y_ptr: int,

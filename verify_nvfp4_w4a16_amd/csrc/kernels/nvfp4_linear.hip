@@ -898,7 +898,8 @@ size_t tile_lds_bytes(int64_t m, int64_t ks, int waves, int c, int nb) {
 //
 // With parts == split > 1 the column group's `split` workgroups are
 // blockIdx = part * groups + column_group and meet through device memory
-// (the uncached workspace).  Producers (parts 0..split-2) store each group sum
+// (the uncached workspace, or the fixed scratch array of
+// nvfp4_linear_noalloc).  Producers (parts 0..split-2) store each group sum
 // as one 64-bit word, a tag in the high half and the fp32 bits in the low
 // half, so no flag, fence or barrier has to order one location against
 // another: a consumer (the workgroup of the last part) that reads a word with
@@ -1302,6 +1303,22 @@ constexpr size_t kWorkBytes = size_t(32) << 20;      // tagged group sums of the
 constexpr size_t kGenWords = kWorkBytes / sizeof(uint64_t) / kGenBlock;   // one per block of them
 constexpr size_t kStatusWords = 64;                  // the time-out word, on its own 256 bytes
 
+// Fixed scratch of nvfp4_linear_noalloc, in 32-bit words: 8 MiB of tagged
+// group sums, their generation words, then the time-out word.
+constexpr size_t kScratchSumBytes = size_t(8) << 20;
+constexpr size_t kScratchGenWords = kScratchSumBytes / sizeof(uint64_t) / kGenBlock;
+constexpr size_t kScratchWords = kScratchSumBytes / 4 + kScratchGenWords + kStatusWords;
+
+}  // namespace
+
+// The many-row kernel's exchange memory for callers that cannot allocate
+// (nvfp4_linear_noalloc): one copy per device, zero when the code object is
+// loaded, held until the process ends.  Host code never passes this name to a
+// kernel: it uses the device address hipGetSymbolAddress returns for it.
+static __device__ __align__(256) uint32_t scratch[kScratchWords];
+
+namespace {
+
 // Where the many-row kernel's column groups meet: tagged group sums, the
 // generation words of their blocks, the time-out word.  All start at zero;
 // generations only ever advance, so the memory is never cleared again.
@@ -1313,13 +1330,14 @@ struct Workspace {
     size_t gen_words = 0;
 };
 
-// Per-device state: the set-up that allocates nothing (kernel attributes),
-// and the uncached workspace nvfp4_init allocates.
+// Per-device state: the set-up that allocates nothing (kernel attributes,
+// the fixed scratch address), and the uncached workspace nvfp4_init allocates.
 struct DeviceState {
     std::once_flag setup_once, alloc_once;
     int setup_status = NVFP4_OK;
     int cus = 0;
     Workspace heap;                 // uncached device memory, never freed
+    Workspace fixed;                // this device's `scratch` array
 };
 DeviceState g_dev[kMaxDevices];
 
@@ -1359,6 +1377,15 @@ int setup_device(int dev) {
                 for (int w = 4; w <= 8; w += 2)
                     if (!allow_full_lds(pick_split(mt, c, w, od))) return NVFP4_ERR_HIP;
         }
+    // This device's copy of the fixed scratch array, by its device address.
+    void* sp = nullptr;
+    if (hipGetSymbolAddress(&sp, HIP_SYMBOL(scratch)) != hipSuccess || sp == nullptr) return NVFP4_ERR_HIP;
+    uint32_t* words = static_cast<uint32_t*>(sp);
+    d.fixed.sums = reinterpret_cast<float*>(words);
+    d.fixed.gens = words + kScratchSumBytes / 4;
+    d.fixed.status = d.fixed.gens + kScratchGenWords;
+    d.fixed.sum_bytes = kScratchSumBytes;
+    d.fixed.gen_words = kScratchGenWords;
     return NVFP4_OK;
 }
 
@@ -1435,7 +1462,7 @@ extern "C" int nvfp4_timeout_status(int* timed_out) {
     DeviceState& d = g_dev[dev];
     if (hipDeviceSynchronize() != hipSuccess) return NVFP4_ERR_HIP;
     uint32_t any = 0;
-    for (const Workspace* w : {&d.heap}) {
+    for (const Workspace* w : {&d.heap, &d.fixed}) {
         if (!w->status) continue;
         uint32_t v = 0;
         if (hipMemcpy(&v, w->status, sizeof v, hipMemcpyDeviceToHost) != hipSuccess) return NVFP4_ERR_HIP;
@@ -1468,6 +1495,7 @@ struct SplitPlan {
     int c = 1, w = 8;
     int parts = 1;
     int64_t region = 0;             // exchange words per column group
+    bool scratch_short = false;     // an exchange was needed and did not fit `ws`
     int64_t groups = 0;
     size_t lds = 0;
 };
@@ -1492,8 +1520,10 @@ bool plan_split(const nvfp4::Tile& tile, int64_t m, int64_t n, int64_t k, const 
         if (!ws || !ws->sums) return false;
         // the words, and one generation word per block of them
         if (size_t(p->groups) * size_t(p->region) * sizeof(uint64_t) > ws->sum_bytes ||
-            size_t(p->groups) * size_t(p->region) / kGenBlock > ws->gen_words)
+            size_t(p->groups) * size_t(p->region) / kGenBlock > ws->gen_words) {
+            p->scratch_short = true;
             return false;
+        }
         p->parts = tile.split;
     }
     return p->groups * tile.split <= int64_t(0x7fffffff);
@@ -1501,7 +1531,7 @@ bool plan_split(const nvfp4::Tile& tile, int64_t m, int64_t n, int64_t k, const 
 
 int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4m3, float tensor_scale,
            void* y, int64_t m, int64_t n, int64_t k, int y_dtype, void* stream, const nvfp4::Tile& tile,
-           int kernel) {
+           int kernel, bool noalloc) {
     int st = nvfp4_linear_shape_ok(m, n, k);
     if (st != NVFP4_OK) return st;
     if (y_dtype != NVFP4_OUT_BF16 && y_dtype != NVFP4_OUT_F32) return NVFP4_ERR_DTYPE;
@@ -1511,13 +1541,16 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
     if (misaligned(x_bf16, 16) || misaligned(w_packed, 16) || misaligned(scales_e4m3, 16) ||
         misaligned(y, y_dtype == NVFP4_OUT_F32 ? 4 : 2))
         return NVFP4_ERR_ALIGN;
-    st = nvfp4_init();
-    if (st != NVFP4_OK) return st;
     int dev = 0;
-    st = current_device(&dev);
+    if (noalloc) {
+        st = setup_current(&dev);               // no allocation: the fixed scratch
+    } else {
+        st = nvfp4_init();
+        if (st == NVFP4_OK) st = current_device(&dev);
+    }
     if (st != NVFP4_OK) return st;
     const DeviceState& d = g_dev[dev];
-    const Workspace* ws = &d.heap;
+    const Workspace* ws = noalloc ? &d.fixed : &d.heap;
 
     const int mt = m <= 16 ? 1 : 2;
     Args a;
@@ -1582,12 +1615,16 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
     const bool tile_first =
         tile_ok && (m == 1 || (m <= 4 && !(many_rounds && split_ok && tile.split == 1)) ||
                     (m <= 8 && tile_resident(tnb) >= tile_per_cu));
-    if (kernel == NVFP4_KERNEL_AUTO)
+    if (kernel == NVFP4_KERNEL_AUTO) {
+        // The fixed scratch has a stated size: a call whose exchange would
+        // need more of it is refused, not run another way.
+        if (noalloc && plan.scratch_short && !tile_first && !pers_ok) return NVFP4_ERR_SCRATCH;
         kernel = tile_first                   ? NVFP4_KERNEL_TILE
                  : split_ok && tile.split == 1 ? NVFP4_KERNEL_SPLIT
                  : pers_ok                     ? NVFP4_KERNEL_PERSISTENT
                  : split_ok                    ? NVFP4_KERNEL_SPLIT
                                                : NVFP4_KERNEL_GENERIC;
+    }
     if ((kernel == NVFP4_KERNEL_PERSISTENT && !pers_ok) || (kernel == NVFP4_KERNEL_SPLIT && !split_ok) ||
         (kernel == NVFP4_KERNEL_TILE && !tile_ok))
         return NVFP4_ERR_TILE;
@@ -1641,7 +1678,17 @@ extern "C" int nvfp4_linear(const void* x_bf16, const uint8_t* w_packed, const u
     if (st != NVFP4_OK) return st;
     if (nvfp4::load_tile_override() != NVFP4_OK) return NVFP4_ERR_TILEFILE;
     return launch(x_bf16, w_packed, scales_e4m3, tensor_scale, y, m, n, k, y_dtype, stream,
-                  nvfp4::tile_for(n, k), NVFP4_KERNEL_AUTO);
+                  nvfp4::tile_for(n, k), NVFP4_KERNEL_AUTO, false);
+}
+
+extern "C" int nvfp4_linear_noalloc(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4m3,
+                                    float tensor_scale, void* y, int64_t m, int64_t n, int64_t k, int y_dtype,
+                                    void* stream) {
+    int st = nvfp4_linear_shape_ok(m, n, k);
+    if (st != NVFP4_OK) return st;
+    if (nvfp4::load_tile_override() != NVFP4_OK) return NVFP4_ERR_TILEFILE;
+    return launch(x_bf16, w_packed, scales_e4m3, tensor_scale, y, m, n, k, y_dtype, stream,
+                  nvfp4::tile_for(n, k), NVFP4_KERNEL_AUTO, true);
 }
 
 extern "C" int nvfp4_linear_tiled(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4m3,
@@ -1658,5 +1705,6 @@ extern "C" int nvfp4_linear_tiled(const void* x_bf16, const uint8_t* w_packed, c
     tile.mwaves = t->mwaves;
     if (!nvfp4::tile_valid(tile, n, k)) return NVFP4_ERR_TILE;
     if (t->kernel < NVFP4_KERNEL_AUTO || t->kernel > NVFP4_KERNEL_WHOLE) return NVFP4_ERR_TILE;
-    return launch(x_bf16, w_packed, scales_e4m3, tensor_scale, y, m, n, k, y_dtype, stream, tile, t->kernel);
+    return launch(x_bf16, w_packed, scales_e4m3, tensor_scale, y, m, n, k, y_dtype, stream, tile, t->kernel,
+                  false);
 }

@@ -9,7 +9,15 @@ one captured HIP graph of 192 nvfp4_linear launches.
 
 value: weight-stream GB/s = packed + scale bytes of every timed product over
 the timed wall time (decimal GB/s), all three M together; per-M figures and %
-of the 8.0 TB/s MI355X peak are in "per_m".  Prints one JSON line on stdout.
+of the 8.0 TB/s MI355X peak are in "per_m".  After the timed steps (outside
+the timed region) the benchmark also measures, each from graphs of its own:
+every kernel of the round on its own launches (the roofline is the kernel
+with the most GPU time per round), a plain read of the round's bytes (the
+ceiling of 192 separate launches), and the other workloads of the product
+(one 1024 x 1024 linear, the 4096 x 4096 product at M = 1..32, the
+12288 x 4096 QKV-style product at M = 16..32, the 151552 x 4096 output head
+at M = 1..32), each over weight copies rotated through more than 512 MB so
+every launch reads HBM.  Prints one JSON line on stdout.
 """
 from __future__ import annotations
 
@@ -17,6 +25,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 from concurrent.futures import ThreadPoolExecutor
@@ -30,8 +39,13 @@ if ROOT not in sys.path:
 import workload  # noqa: E402
 
 PEAK_HBM_GBPS = 8000.0
-CPU_BASELINE_LAYERS = 2   # layers whose products the oracle times (about 10 s of CPU work)
-KERNEL_SOURCE = os.path.join(ROOT, "verify_nvfp4_w4a16_amd", "csrc", "kernels", "nvfp4_linear.hip")
+PEAK_BF16_MFMA_TFLOPS = 2500.0
+BYTES_PER_WEIGHT = 0.5625          # 4-bit code + one e4m3 byte per 16 weights
+CPU_BASELINE_MIN_S = 10.0           # the oracle runs products until this much CPU time has passed ...
+CPU_BASELINE_MAX_S = 30.0           # ... and stops starting new ones past this
+COLD_BYTES = 512 << 20              # weight copies rotated per timed launch sequence
+KERNEL_SOURCES = [os.path.join(ROOT, "verify_nvfp4_w4a16_amd", "csrc", "kernels", f)
+                  for f in ("nvfp4_linear.hip",)]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_round.json")
 
 
@@ -39,20 +53,57 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_budget() -> int:
+def cpu_cores() -> int:
     try:
         return max(1, min(16, len(os.sched_getaffinity(0))))
     except AttributeError:
         return max(1, min(16, os.cpu_count() or 1))
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
 def kernel_source_hash() -> str:
-    """SHA-256 prefix of the kernel source with its comment lines and blank
-    lines removed, so a counter profile stays attached to the code it
-    measured across comment-only edits."""
-    with open(KERNEL_SOURCE, encoding="utf-8") as f:
-        code = [ln.rstrip() for ln in f if ln.strip() and not ln.lstrip().startswith("//")]
-    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
+    """SHA-256 prefix of the kernel sources with comment and blank lines
+    removed, so a counter profile stays attached to the code it measured
+    across comment-only edits."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, encoding="utf-8") as f:
+            code = [ln.rstrip() for ln in f if ln.strip() and not ln.lstrip().startswith("//")]
+        h.update("\n".join(code).encode())
+    return h.hexdigest()[:16]
+
+
+def timed_graph(torch, stream, fn, reps: int = 5, warm: int = 2) -> float:
+    """Median milliseconds of one replay of a graph capturing fn(stream_handle)."""
+    g = torch.cuda.CUDAGraph()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            fn(stream.cuda_stream)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    ts = []
+    with torch.cuda.stream(stream):
+        for i in range(warm + reps):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            g.replay()
+            e.record(stream)
+            e.synchronize()
+            if i >= warm:
+                ts.append(s.elapsed_time(e))
+    del g
+    return float(np.median(ts))
 
 
 class Round:
@@ -62,7 +113,7 @@ class Round:
         import verify_nvfp4_w4a16_amd as nv
         self.layers = layers
         self.items = []           # (layer, proj, shape, wp, sc, t)
-        self.host = {}            # (layer, proj) -> (packed, scales, t) of the CPU-baseline layers
+        self.host = {}            # (layer, proj) -> (packed, scales, t), layers 0..1 for the CPU baseline
         jobs = [(l, p) for l in range(layers) for p in range(len(workload.ROUND_SHAPES))]
 
         def gen(job):
@@ -71,13 +122,13 @@ class Round:
             return job, workload.weights_f32(s.n, s.k, workload.round_weight_seed(l, p))
 
         t0 = time.time()
-        with ThreadPoolExecutor(max(1, cpu_budget() // 2)) as ex:
+        with ThreadPoolExecutor(max(1, cpu_cores() // 2)) as ex:
             for (l, p), w in ex.map(gen, jobs):
                 packed, scales, t = nv.pack(w)
                 del w
                 wp = torch.from_numpy(packed).to(dev, non_blocking=False)
                 sc = torch.from_numpy(scales).to(dev, non_blocking=False)
-                if l < CPU_BASELINE_LAYERS:
+                if l < 2:
                     self.host[(l, p)] = (packed, scales, t)
                 self.items.append((l, p, workload.ROUND_SHAPES[p], wp, sc, t))
         torch.cuda.synchronize()
@@ -92,7 +143,7 @@ class Round:
 
 
 class Launches:
-    """Activations and outputs of one round at row count m, launched on `stream`."""
+    """Activations and outputs of one round at row count m."""
 
     def __init__(self, torch, dev, rnd: Round, m: int):
         import verify_nvfp4_w4a16_amd as nv
@@ -108,9 +159,11 @@ class Launches:
             self.calls.append((x.data_ptr(), wp.data_ptr(), sc.data_ptr(), t, y.data_ptr(),
                                m, s.n, s.k, x))
 
-    def launch_all(self, stream_handle: int) -> None:
+    def launch(self, stream_handle: int, which=None) -> None:
         nv = self.nv
-        for xp, wpp, scp, t, yp, m, n, k, _ in self.calls:
+        for i, (xp, wpp, scp, t, yp, m, n, k, _) in enumerate(self.calls):
+            if which is not None and i not in which:
+                continue
             st = nv.linear_raw(xp, wpp, scp, t, yp, m, n, k, nv.OUT_BF16, stream_handle)
             if st != nv.OK:
                 raise nv.Nvfp4Error(st, "nvfp4_linear")
@@ -132,21 +185,157 @@ def copy_bandwidth(torch, dev) -> float:
     return 2 * (1 << 30) / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(torch, dev, rnd: Round, graphs: dict, launches: dict, ms_list) -> dict:
-    """The oracle on this host's cores over a bounded sample (the four
-    products of the first CPU_BASELINE_LAYERS layers at each timed M, about
-    10 s), checked against the GPU's output for the same products; reported,
-    never optimised."""
+def per_kernel(torch, stream, rnd: Round, launches: dict, ms_list) -> list:
+    """Every kernel of the round at each timed M, timed on its own launches
+    (a graph of those launches in round order, HIP events on its stream)."""
+    nv = launches[ms_list[0]].nv
+    rows = []
+    for m in ms_list:
+        groups = {}
+        for i, (_, _, s, _, _, _) in enumerate(rnd.items):
+            groups.setdefault(nv.kernel_name(m, s.n, s.k), []).append(i)
+        lc = launches[m]
+        for name, idx in groups.items():
+            which = set(idx)
+            ms = timed_graph(torch, stream, lambda h: lc.launch(h, which))
+            avg_us = ms * 1e3 / len(idx)
+            shapes = sorted({(rnd.items[i][2].n, rnd.items[i][2].k) for i in idx})
+            wbytes = sum(rnd.items[i][2].n * rnd.items[i][2].k * BYTES_PER_WEIGHT for i in idx) / len(idx)
+            xy = sum(2 * m * (rnd.items[i][2].n + rnd.items[i][2].k) for i in idx) / len(idx)
+            flops = sum(2.0 * m * rnd.items[i][2].n * rnd.items[i][2].k for i in idx) / len(idx)
+            rows.append({"m": m, "kernel": name, "launches_per_round": len(idx),
+                         "shapes": [f"{n}x{k}" for n, k in shapes],
+                         "avg_launch_us": avg_us, "round_share_us": avg_us * len(idx),
+                         "weight_bytes_per_launch": wbytes, "xy_bytes_per_launch": xy,
+                         "weight_GBps": wbytes / (avg_us * 1e-6) / 1e9,
+                         "frac_of_peak": wbytes / (avg_us * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+                         "mfma_TFLOPs": flops / (avg_us * 1e-6) / 1e12})
+    return rows
+
+
+def read_ceiling(torch, stream, rnd: Round) -> dict:
+    """A plain read of each product's packed weights and scales, one launch per
+    product in round order: the round ceiling of separate launches, and per
+    shape the time of one read (cold: the round is 5.9 GB)."""
+    import verify_nvfp4_w4a16_amd as nv
+    sink = torch.zeros(64, dtype=torch.int32, device=rnd.items[0][3].device)
+
+    def run(h, which=None):
+        for i, (_, _, s, wp, sc, _) in enumerate(rnd.items):
+            if which is not None and i not in which:
+                continue
+            st = nv.read_probe_raw(wp.data_ptr(), wp.numel(), sc.data_ptr(), sc.numel(), sink.data_ptr(), h)
+            if st != nv.OK:
+                raise nv.Nvfp4Error(st, "nvfp4_read_probe")
+
+    ms = timed_graph(torch, stream, run)
+    out = {"round_ms": ms, "round_GBps": rnd.weight_bytes() / (ms * 1e-3) / 1e9, "per_shape_us": {}}
+    for p, s in enumerate(workload.ROUND_SHAPES):
+        which = {i for i, it in enumerate(rnd.items) if it[1] == p}
+        ms_p = timed_graph(torch, stream, lambda h: run(h, which))
+        us = ms_p * 1e3 / len(which)
+        out["per_shape_us"][f"{s.n}x{s.k}"] = {"us": us, "GBps": s.n * s.k * BYTES_PER_WEIGHT / (us * 1e-6) / 1e9}
+    return out
+
+
+def config_timings(torch, dev, stream) -> dict:
+    """The product's other workloads, each over weight copies rotated through
+    more than 512 MB (distinct addresses, so every launch reads HBM)."""
+    import verify_nvfp4_w4a16_amd as nv
+    out = {}
+
+    def copies(shape, seed):
+        packed, scales, t = nv.pack(workload.weights_f32(shape.n, shape.k, seed))
+        wp0, sc0 = torch.from_numpy(packed).to(dev), torch.from_numpy(scales).to(dev)
+        wbytes = packed.nbytes + scales.nbytes
+        count = max(2, -(-COLD_BYTES // wbytes))
+        return [(wp0.clone(), sc0.clone()) for _ in range(count)], t, wbytes
+
+    def timing(ws, t, n, k, x, y, dtype):
+        def run(h):
+            for wp, sc in ws:
+                st = nv.linear_raw(x.data_ptr(), wp.data_ptr(), sc.data_ptr(), t, y.data_ptr(), x.shape[0], n, k,
+                                   dtype, h)
+                if st != nv.OK:
+                    raise nv.Nvfp4Error(st, "nvfp4_linear")
+        return timed_graph(torch, stream, run) * 1e3 / len(ws)
+
+    def xs(m, k, seed, outliers=False):
+        xb = workload.activations_bf16(m, k, seed, outliers=outliers)
+        return torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    s = workload.SINGLE
+    ws, t, wb = copies(s, workload.SEEDS["single"][0])
+    x = xs(1, s.k, workload.SEEDS["single"][1])
+    y = torch.empty((1, s.n), dtype=torch.bfloat16, device=dev)
+    us = timing(ws, t, s.n, s.k, x, y, nv.OUT_BF16)
+    out["single_1024x1024_M1"] = {"us_per_launch": us, "weight_GBps": wb / (us * 1e-6) / 1e9, "copies": len(ws),
+                                  "kernel": nv.kernel_name(1, s.n, s.k),
+                                  "note": "launch-latency bound (0.59 MB): the GB/s is not a bandwidth figure"}
+    del ws
+
+    s = workload.INVARIANCE
+    ws, t, wb = copies(s, workload.SEEDS["invariance"][0])
+    xfull = xs(32, s.k, workload.SEEDS["invariance"][1])
+    per = {}
+    for m in range(1, 33):
+        y = torch.empty((m, s.n), dtype=torch.bfloat16, device=dev)
+        us = timing(ws, t, s.n, s.k, xfull[:m], y, nv.OUT_BF16)
+        per[str(m)] = {"us": us, "weight_GBps": wb / (us * 1e-6) / 1e9, "kernel": nv.kernel_name(m, s.n, s.k)}
+    out["invariance_4096x4096_M1to32"] = {"copies": len(ws), "per_m": per}
+    del ws
+
+    s = workload.QKV
+    ws, t, wb = copies(s, workload.SEEDS["qkv"][0])
+    xfull = xs(32, s.k, workload.SEEDS["qkv"][1], outliers=True)
+    per = {}
+    for m in range(16, 33):
+        y = torch.empty((m, s.n), dtype=torch.bfloat16, device=dev)
+        us = timing(ws, t, s.n, s.k, xfull[:m], y, nv.OUT_BF16)
+        per[str(m)] = {"us": us, "weight_GBps": wb / (us * 1e-6) / 1e9, "kernel": nv.kernel_name(m, s.n, s.k)}
+    out["qkv_12288x4096_M16to32"] = {"copies": len(ws), "per_m": per,
+                                     "step_17_over_16": per["17"]["us"] / per["16"]["us"]}
+    del ws
+
+    s = workload.HEAD
+    ws, t, wb = copies(s, workload.SEEDS["head"][0])
+    xfull = xs(32, s.k, workload.SEEDS["head"][1])
+    per = {}
+    for m in range(1, 33):
+        y = torch.empty((m, s.n), dtype=torch.float32, device=dev)
+        us = timing(ws, t, s.n, s.k, xfull[:m], y, nv.OUT_F32)
+        per[str(m)] = {"us": us, "weight_GBps": wb / (us * 1e-6) / 1e9,
+                       "kernel": nv.kernel_name(m, s.n, s.k, nv.OUT_F32)}
+    out["head_151552x4096_fp32_M1to32"] = {"copies": len(ws), "per_m": per}
+    del ws
+    torch.cuda.synchronize()
+    return out
+
+
+def cpu_baseline(torch, dev, rnd: Round, launches: dict, ms_list) -> dict:
+    """The oracle on this host's cores over a bounded sample of the same
+    workload: the decode round's products of layers 0 and 1, in round order at
+    each timed M, until about CPU_BASELINE_MIN_S seconds of oracle time; each
+    product's columns are split over one worker thread per core (NumPy's
+    decode and matmul release the GIL), BLAS single-threaded per worker.  The
+    GPU's outputs of the same products are checked against it."""
     import threadpoolctl
     import oracle
+    cores = cpu_cores()
     total_s = 0.0
     weight_bytes = 0
     worst = 0.0
-    for m in ms_list:
-        # GPU outputs of those products: rerun their launches eagerly
-        lc = launches[m]
-        for idx, (l, p, s, wp, sc, t) in enumerate(rnd.items[:4 * CPU_BASELINE_LAYERS]):
-            xp, wpp, scp, tt, yp, mm, n, k, x = lc.calls[idx]
+    done = []
+    jobs = [(m, idx) for idx in range(8) for m in ms_list]
+    with threadpoolctl.threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(cores) as ex:
+        for m, idx in jobs:
+            if total_s >= CPU_BASELINE_MIN_S and len(done) >= len(ms_list) * 4:
+                break
+            if total_s >= CPU_BASELINE_MAX_S:
+                break
+            l, p, s, wp, sc, t = rnd.items[idx]
+            lc = launches[m]
+            xp, wpp, scp, tt, _, mm, n, k, _ = lc.calls[idx]
             y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
             st = lc.nv.linear_raw(xp, wpp, scp, tt, y.data_ptr(), mm, n, k, lc.nv.OUT_BF16,
                                   torch.cuda.current_stream().cuda_stream)
@@ -154,39 +343,28 @@ def cpu_baseline(torch, dev, rnd: Round, graphs: dict, launches: dict, ms_list) 
             torch.cuda.synchronize()
             packed, scales, t0 = rnd.host[(l, p)]
             xb = workload.activations_bf16(m, k, workload.round_act_seed(l, p, m))
+            blocks = np.array_split(np.arange(n), cores)
             c0 = time.perf_counter()
-            y_ref = oracle.linear_ref(xb, packed, scales, t0)
+            parts = list(ex.map(lambda cols: oracle.linear_ref(xb, packed, scales, t0, cols), blocks))
             total_s += time.perf_counter() - c0
+            y_ref = np.concatenate(parts, axis=1)
             weight_bytes += packed.nbytes + scales.nbytes
-            bnd = oracle.bound(xb, packed, scales, t0)
+            bnd = np.concatenate(list(ex.map(lambda cols: oracle.bound(xb, packed, scales, t0, cols), blocks)),
+                                 axis=1)
             y64 = y.float().cpu().numpy().astype(np.float64)
             worst = max(worst, oracle.max_violation(y64, y_ref, bnd, "bf16"))
-    blas = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
-    threads = max([i["num_threads"] for i in blas] or [1])
-    return {"value": weight_bytes / total_s / 1e9, "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"the 4 products of layers 0..{CPU_BASELINE_LAYERS - 1} at M={','.join(map(str, ms_list))} "
-                      f"({weight_bytes} weight-stream bytes, {total_s:.1f} s; fp64 decode "
-                      f"single-threaded, BLAS dgemm on {threads} threads)",
+            done.append(f"L{l}P{p}M{m}")
+    return {"value": weight_bytes / total_s / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"{len(done)} decode-round products ({', '.join(done)}; {weight_bytes} weight-stream "
+                      f"bytes) in {total_s:.1f} s of oracle time: fp64 decode and dgemm, columns split over "
+                      f"{cores} worker threads, BLAS single-threaded per worker",
             "seconds": total_s, "parity_max_err_over_tol": worst}
 
 
-def kernel_name(m: int) -> str:
-    """The kernel nvfp4_linear runs for the decode round's products at M rows
-    (the dispatch rule of the library: per-tile kernel up to 4 rows, else the
-    many-row kernel for these shapes, whose x does not fit one LDS)."""
-    if m <= 4:
-        return f"nvfp4_skinny_tile<1, 1, NB, bf16> (per-tile kernel, M={m} round)"
-    if m <= 16:
-        return (f"nvfp4_skinny_split<1, 1, W, bf16> (many-row kernel, M={m} round; "
-                f"W = 6 for the 24576-column product, 4 for the others)")
-    return (f"nvfp4_skinny_split<1, 2, W, bf16> (many-row kernel, M={m} round; "
-            f"W = 6 for the 24576-column product, 8 for the others)")
-
-
-def traffic_from_profile(per_launch_alg: float):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source."""
+def traffic_from_profile(kernel: str, m: int):
+    """Calibrated HBM bytes per launch of `kernel` at `m` rows from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -194,7 +372,10 @@ def traffic_from_profile(per_launch_alg: float):
         return None
     if rec.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    for row in rec.get("kernels", []):
+        if row.get("kernel") == kernel and row.get("m") == m:
+            return row.get("hbm_bytes_per_launch")
+    return None
 
 
 def main() -> int:
@@ -206,7 +387,8 @@ def main() -> int:
     ap.add_argument("--m", type=str, default="1,16,32", help="row counts timed in each step")
     ap.add_argument("--extra-m", type=str, default="8", help="row counts timed after the steps, reported only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--eager", action="store_true", help="also time eager launches")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the per-kernel, plain-read and other-workload timings")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of graph replays (for counter collection)")
     ap.add_argument("--copy-only", action="store_true",
@@ -241,13 +423,13 @@ def main() -> int:
     stream = torch.cuda.Stream(device=dev)
     graphs = {}
     for m, lc in launches.items():
-        lc.launch_all(torch.cuda.current_stream().cuda_stream)       # warm, eager
+        lc.launch(torch.cuda.current_stream().cuda_stream)       # warm, eager
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         stream.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(stream):
             with torch.cuda.graph(g, stream=stream):
-                lc.launch_all(stream.cuda_stream)
+                lc.launch(stream.cuda_stream)
         torch.cuda.current_stream().wait_stream(stream)
         graphs[m] = g
     torch.cuda.synchronize()
@@ -266,7 +448,7 @@ def main() -> int:
                 s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 s.record(stream)
                 if args.no_graph:
-                    launches[m].launch_all(stream.cuda_stream)
+                    launches[m].launch(stream.cuda_stream)
                 else:
                     graphs[m].replay()
                 e.record(stream)
@@ -299,35 +481,33 @@ def main() -> int:
         gbps = weight_bytes / (med * 1e-3) / 1e9
         per_m[str(m)] = {"round_ms_median": med, "weight_stream_GBps": gbps,
                          "pct_of_peak": 100 * gbps / PEAK_HBM_GBPS, "timed_in_steps": False}
+    for g in graphs.values():
+        del g
+    graphs.clear()
 
-    eager = None
-    if args.eager:
-        eager = {}
-        for m in ms_list:
-            torch.cuda.synchronize()
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record()
-            for _ in range(3):
-                launches[m].launch_all(torch.cuda.current_stream().cuda_stream)
-            e.record()
-            e.synchronize()
-            eager[str(m)] = weight_bytes / (s.elapsed_time(e) / 3 * 1e-3) / 1e9
-
-    # Roofline of the dominant kernel: the row count whose round takes longest.
-    dom = max(ms_list, key=lambda m: per_m[str(m)]["round_ms_median"])
-    launches_per_round = len(rnd.items)
-    avg_launch_s = per_m[str(dom)]["round_ms_median"] * 1e-3 / launches_per_round
-    alg_per_launch = rnd.algorithmic_bytes(dom) / launches_per_round
-    achieved = alg_per_launch / avg_launch_s / 1e9
-    traffic = traffic_from_profile(alg_per_launch)
-    roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
-                "kernel": kernel_name(dom),
-                "alg_bytes_per_launch": alg_per_launch, "avg_launch_us": avg_launch_s * 1e6}
+    kernels, ceiling, configs = None, None, None
+    roofline = None
+    if not args.no_extras:
+        kernels = per_kernel(torch, stream, rnd, launches, ms_list)
+        dom = max(kernels, key=lambda r: r["round_share_us"])
+        achieved = dom["weight_GBps"]
+        roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                    "frac": achieved / PEAK_HBM_GBPS,
+                    "traffic": traffic_from_profile(dom["kernel"], dom["m"]),
+                    "kernel": dom["kernel"], "m": dom["m"], "shapes": dom["shapes"],
+                    "launches_per_round": dom["launches_per_round"],
+                    "avg_launch_us": dom["avg_launch_us"],
+                    "alg_bytes_per_launch": dom["weight_bytes_per_launch"],
+                    "alg_bytes_rule": "0.5625 B per weight (packed e2m1 + e4m3 scale) x N x K, "
+                                      "averaged over the kernel's launches",
+                    "xy_bytes_per_launch": dom["xy_bytes_per_launch"],
+                    "mfma_frac_of_bf16_peak": dom["mfma_TFLOPs"] / PEAK_BF16_MFMA_TFLOPS}
+        ceiling = read_ceiling(torch, stream, rnd)
+        configs = config_timings(torch, dev, stream)
 
     base = None
     if not args.no_cpu_baseline:
-        base = cpu_baseline(torch, dev, rnd, graphs, launches, ms_list)
+        base = cpu_baseline(torch, dev, rnd, launches, ms_list)
 
     total_bytes = weight_bytes * len(ms_list) * args.steps
     value = total_bytes / wall / 1e9
@@ -339,17 +519,18 @@ def main() -> int:
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"decode round: {args.layers} layers x {{(8192,4096), (4096,8192), "
                                "(24576,4096), (4096,12288)} NVFP4 W4A16, back-to-back per M, HIP graph",
-                   "m": ms_list, "layers": args.layers, "launches_per_round": launches_per_round,
+                   "m": ms_list, "layers": args.layers, "launches_per_round": len(rnd.items),
                    "weight_stream_bytes_per_round": weight_bytes, "parallelism": "single GPU"},
         "pct_of_peak": 100 * value / PEAK_HBM_GBPS,
         "per_m": per_m,
         "roofline": roofline,
         "cpu_baseline": base,
+        "plain_read_ceiling": ceiling,
+        "kernels": kernels,
+        "configs": configs,
         "copy_GBps_read_plus_write": copy_bandwidth(torch, dev),
         "kernel_source_sha256_16": kernel_source_hash(),
     }
-    if eager is not None:
-        out["eager_weight_stream_GBps"] = eager
     print(json.dumps(out), flush=True)
     return 0
 

@@ -245,6 +245,29 @@ int nvfp4_linear_tiled(const void* x_bf16, const uint8_t* w_packed,
  */
 int nvfp4_tile_info(int64_t n, int64_t k, char* buf, int64_t buflen);
 
+/*
+ * Host.  Writes into buf (NUL-terminated) the kernel nvfp4_linear launches for
+ * an M x N x K product with this output type on the current device, as its
+ * template name reads in a kernel trace, then its grid, block and LDS bytes
+ * (and, for the many-row kernel, how many workgroups share a column group);
+ * "none" for M = 0.  For profiles, which "CUDA Kernel Engineering" (profiling)
+ * and "10 Kernels" 10.7 read per kernel.  Runs nvfp4_init's set-up.
+ * Errors: NULL, SHAPE, DTYPE, BUFFER, HIP, DEVICE, TILEFILE.
+ */
+int nvfp4_launch_info(int64_t m, int64_t n, int64_t k, int y_dtype, char* buf, int64_t buflen);
+
+/*
+ * Device, asynchronous on `stream`: reads a_bytes at a and b_bytes at b once
+ * with 16-byte loads and nothing else (e.g. a product's packed weights and
+ * its scales), a plain-read ceiling to time a product kernel against
+ * ("10 Kernels" 10.7 times kernels over working sets larger than the caches).
+ * a, b: device, 16-byte aligned, sizes multiples of 16 (either may be 0).
+ * sink: device, 4 bytes, written only in the unlikely case that the bytes
+ * read XOR to one fixed value.  Errors: NULL, SHAPE, ALIGN, HIP.
+ */
+int nvfp4_read_probe(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes, void* sink,
+                     void* stream);
+
 /* Host.  Static text for a status code; never NULL. */
 const char* nvfp4_strerror(int status);
 

@@ -248,8 +248,8 @@ def test_default_split_fills_the_chip():
 
 def test_builtin_table_entries():
     # Sweep-picked segment counts and groupings of the decode round's products.
-    for n, k, waves, split, mwaves in [(8192, 4096, 8, 4, 0), (4096, 8192, 8, 8, 0), (24576, 4096, 4, 1, 6),
-                                       (4096, 12288, 8, 8, 0)]:
+    for n, k, waves, split, mwaves in [(8192, 4096, 8, 4, 0), (4096, 8192, 8, 4, 4), (24576, 4096, 4, 1, 6),
+                                       (4096, 12288, 8, 4, 4)]:
         t = nv.table_tile(n, k)
         assert (t.cols, t.waves, t.split, t.mwaves) == (16, waves, split, mwaves), (n, k, t)
 
@@ -307,3 +307,17 @@ def test_build_rejects_kernels_that_spill():
     ])
     assert build.scratch_users(report) == [("_Z1bv", 44)]
     assert build.RESOURCE_REMARKS in " ".join([build.RESOURCE_REMARKS])
+
+
+def test_read_probe_validates_before_any_hip_call():
+    lib = ctypes.CDLL(nv.LIB_PATH)
+    lib.nvfp4_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                     ctypes.c_void_p, ctypes.c_void_p]
+    a16, sink = 0x10000, 0x20000
+    assert lib.nvfp4_read_probe(None, 16, None, 0, sink, None) == nv.ERR_NULL
+    assert lib.nvfp4_read_probe(a16, 16, None, 0, None, None) == nv.ERR_NULL
+    assert lib.nvfp4_read_probe(a16, 24, None, 0, sink, None) == nv.ERR_SHAPE
+    assert lib.nvfp4_read_probe(a16, -16, None, 0, sink, None) == nv.ERR_SHAPE
+    assert lib.nvfp4_read_probe(a16 + 8, 16, None, 0, sink, None) == nv.ERR_ALIGN
+    assert lib.nvfp4_read_probe(a16, 16, None, 0, sink + 2, None) == nv.ERR_ALIGN
+    assert lib.nvfp4_read_probe(None, 0, None, 0, sink, None) == nv.OK      # nothing to read

@@ -20,6 +20,31 @@ def test_init_reports_gfx950():
     nv.init()
 
 
+def test_launch_info_names_the_dispatched_kernel():
+    # The per-tile kernel at one row, the many-row kernel at 16 and 32 rows on
+    # the decode round's shapes; the trace name carries the template
+    # arguments (column tiles, row tiles, buffers or wavefronts, output type).
+    for n, k in ((8192, 4096), (4096, 8192), (24576, 4096), (4096, 12288)):
+        assert nv.kernel_name(1, n, k).startswith("nvfp4_skinny_tile<1, 1, ")
+        assert nv.kernel_name(16, n, k).startswith("nvfp4_skinny_split<1, 1, ")
+        assert nv.kernel_name(32, n, k).startswith("nvfp4_skinny_split<1, 2, ")
+        assert nv.kernel_name(32, n, k).endswith(", false>")
+    assert nv.kernel_name(1, 151552, 4096, nv.OUT_F32).endswith(", true>")
+    assert nv.launch_info(0, 8192, 4096) == "none"
+    info = nv.launch_info(32, 8192, 4096)
+    assert " grid=" in info and " block=" in info and " parts=4" in info
+
+
+def test_read_probe_reads_and_leaves_the_sink():
+    a = torch.zeros(1 << 20, dtype=torch.uint8, device=DEV)
+    b = torch.zeros(4096, dtype=torch.uint8, device=DEV)
+    sink = torch.full((1,), 7, dtype=torch.int32, device=DEV)
+    st = nv.read_probe_raw(a.data_ptr(), a.numel(), b.data_ptr(), b.numel(), sink.data_ptr(),
+                           torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == nv.OK and int(sink.item()) == 7
+
+
 def test_deterministic(weight):
     x = workload.activations_bf16(23, 2048, 92)
     a = bits(run(x, weight)).clone()

@@ -28,13 +28,13 @@ def _both(w, x, out_dtype=torch.bfloat16):
 
 
 def test_noalloc_matches_linear_two_calls_second_smaller():
-    # 4096 x 12288 at 32 rows exchanges through the scratch (split 8, 32
-    # column groups, 7 MiB), then 8192 x 4096 at 17 rows (split 4): each
+    # 4096 x 12288 at 32 rows exchanges through the scratch (split 4, 64
+    # column groups of 64), then 8192 x 4096 at 17 rows (split 4): each
     # output bit-equal to nvfp4_linear's, the first also within the oracle's
     # tolerance on sampled columns.
     big = Weight.from_f32(workload.weights_f32(4096, 12288, 501))
     small = Weight.from_f32(workload.weights_f32(8192, 4096, 502))
-    assert nv.table_tile(4096, 12288).split == 8 and nv.table_tile(8192, 4096).split > 1
+    assert nv.table_tile(4096, 12288).split > 1 and nv.table_tile(8192, 4096).split > 1
     xb = workload.activations_bf16(32, 12288, 503)
     st, y_ref, y_na = _both(big, upload_bits(xb))
     assert st == nv.OK

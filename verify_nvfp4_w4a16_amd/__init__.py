@@ -27,7 +27,8 @@ K_MULTIPLE = 256
 
 EXPORTED = ("nvfp4_pack", "nvfp4_check_scales", "nvfp4_linear_shape_ok", "nvfp4_init",
             "nvfp4_linear", "nvfp4_linear_tiled", "nvfp4_tile_info", "nvfp4_strerror",
-            "nvfp4_timeout_status", "nvfp4_linear_noalloc")
+            "nvfp4_timeout_status", "nvfp4_linear_noalloc", "nvfp4_launch_info",
+            "nvfp4_read_probe")
 
 
 class Tile(ctypes.Structure):
@@ -69,6 +70,8 @@ def _load() -> ctypes.CDLL:
                                        ctypes.POINTER(Tile), vp]
     lib.nvfp4_tile_info.argtypes = [i64, i64, ctypes.c_char_p, i64]
     lib.nvfp4_timeout_status.argtypes = [ctypes.POINTER(ctypes.c_int)]
+    lib.nvfp4_launch_info.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.c_char_p, i64]
+    lib.nvfp4_read_probe.argtypes = [vp, i64, vp, i64, vp, vp]
     lib.nvfp4_strerror.argtypes = [ctypes.c_int]
     lib.nvfp4_strerror.restype = ctypes.c_char_p
     for name in EXPORTED:
@@ -137,6 +140,23 @@ def tile_info(n: int, k: int) -> str:
     buf = ctypes.create_string_buffer(512)
     _check(_lib().nvfp4_tile_info(n, k, buf, len(buf)), "nvfp4_tile_info")
     return buf.value.decode()
+
+
+def launch_info(m: int, n: int, k: int, y_dtype: int = OUT_BF16) -> str:
+    """The kernel nvfp4_linear launches for this product (trace name, grid, block, LDS)."""
+    buf = ctypes.create_string_buffer(512)
+    _check(_lib().nvfp4_launch_info(m, n, k, y_dtype, buf, len(buf)), "nvfp4_launch_info")
+    return buf.value.decode()
+
+
+def kernel_name(m: int, n: int, k: int, y_dtype: int = OUT_BF16) -> str:
+    """Template name of the kernel nvfp4_linear launches, as a kernel trace shows it."""
+    return launch_info(m, n, k, y_dtype).split(" grid=")[0]
+
+
+def read_probe_raw(a_ptr: int, a_bytes: int, b_ptr: int, b_bytes: int, sink_ptr: int, stream: int) -> int:
+    """nvfp4_read_probe on raw device addresses; returns the status."""
+    return _lib().nvfp4_read_probe(a_ptr, a_bytes, b_ptr, b_bytes, sink_ptr, stream)
 
 
 def table_tile(n: int, k: int) -> Tile:

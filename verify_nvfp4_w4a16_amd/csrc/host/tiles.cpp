@@ -35,9 +35,9 @@ const std::map<Key, Tile>& builtin_table() {
             t[{n, k}] = x;
         };
         add(8192, 4096, 8, 4, 0);      // q/o-sized products of the decode round
-        add(4096, 8192, 8, 8, 0);
+        add(4096, 8192, 8, 4, 4);      // 64 columns per many-row workgroup at every row count
         add(24576, 4096, 4, 1, 6);     // gate/up: 96 columns per many-row workgroup, one per CU
-        add(4096, 12288, 8, 8, 0);     // down
+        add(4096, 12288, 8, 4, 4);     // down
         return t;
     }();
     return table;

@@ -1529,18 +1529,36 @@ bool plan_split(const nvfp4::Tile& tile, int64_t m, int64_t n, int64_t k, const 
     return p->groups * tile.split <= int64_t(0x7fffffff);
 }
 
+// The kernel a launch runs, as its template name reads in a kernel trace.
+std::string kernel_text(const char* fn, std::initializer_list<int> params, int y_dtype, dim3 grid, dim3 block,
+                        size_t lds) {
+    std::string s = fn;
+    s += "<";
+    for (int v : params) s += std::to_string(v) + ", ";
+    s += y_dtype == NVFP4_OUT_F32 ? "true>" : "false>";
+    s += " grid=" + std::to_string(grid.x) + " block=" + std::to_string(block.x) + " lds=" + std::to_string(lds);
+    return s;
+}
+
+// Validates and launches one product; with `describe` set it launches
+// nothing and writes there the kernel it would run (pointers unchecked).
 int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4m3, float tensor_scale,
            void* y, int64_t m, int64_t n, int64_t k, int y_dtype, void* stream, const nvfp4::Tile& tile,
-           int kernel, bool noalloc) {
+           int kernel, bool noalloc, std::string* describe = nullptr) {
     int st = nvfp4_linear_shape_ok(m, n, k);
     if (st != NVFP4_OK) return st;
     if (y_dtype != NVFP4_OUT_BF16 && y_dtype != NVFP4_OUT_F32) return NVFP4_ERR_DTYPE;
-    if (m == 0) return NVFP4_OK;
-    if (!x_bf16 || !w_packed || !scales_e4m3 || !y) return NVFP4_ERR_NULL;
-    auto misaligned = [](const void* p, uintptr_t al) { return (reinterpret_cast<uintptr_t>(p) & (al - 1)) != 0; };
-    if (misaligned(x_bf16, 16) || misaligned(w_packed, 16) || misaligned(scales_e4m3, 16) ||
-        misaligned(y, y_dtype == NVFP4_OUT_F32 ? 4 : 2))
-        return NVFP4_ERR_ALIGN;
+    if (m == 0) {
+        if (describe) *describe = "none";
+        return NVFP4_OK;
+    }
+    if (!describe) {
+        if (!x_bf16 || !w_packed || !scales_e4m3 || !y) return NVFP4_ERR_NULL;
+        auto misaligned = [](const void* p, uintptr_t al) { return (reinterpret_cast<uintptr_t>(p) & (al - 1)) != 0; };
+        if (misaligned(x_bf16, 16) || misaligned(w_packed, 16) || misaligned(scales_e4m3, 16) ||
+            misaligned(y, y_dtype == NVFP4_OUT_F32 ? 4 : 2))
+            return NVFP4_ERR_ALIGN;
+    }
     int dev = 0;
     if (noalloc) {
         st = setup_current(&dev);               // no allocation: the fixed scratch
@@ -1633,9 +1651,12 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
         const int64_t tiles = (n + tile.cols - 1) / tile.cols;
         const int per_cu = std::max(1, std::min(64 / tile.waves, int(kMaxLdsBytes / (pers_bytes + 256))));
         const int64_t grid_p = tiles < int64_t(per_cu) * cus ? tiles : int64_t(per_cu) * cus;
-        hipLaunchKernelGGL(pick_persistent(mt, pc, pnb, y_dtype),
-                           dim3(static_cast<unsigned>(grid_p)), dim3(static_cast<unsigned>(kWave * tile.waves)),
-                           pers_bytes, hs, a);
+        const dim3 grid(static_cast<unsigned>(grid_p)), block(static_cast<unsigned>(kWave * tile.waves));
+        if (describe) {
+            *describe = kernel_text("nvfp4_skinny_persistent", {pc, mt, pnb}, y_dtype, grid, block, pers_bytes);
+            return NVFP4_OK;
+        }
+        hipLaunchKernelGGL(pick_persistent(mt, pc, pnb, y_dtype), grid, block, pers_bytes, hs, a);
     } else if (kernel == NVFP4_KERNEL_SPLIT) {
         SplitArgs sa;
         sa.a = a;
@@ -1648,12 +1669,21 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
         sa.spin_limit = g_test_split_timeout ? kTestSpinLimit : kSpinLimit;
         sa.test_mode = g_test_split_timeout;
         sa.groups = static_cast<int>(plan.groups);
-        hipLaunchKernelGGL(pick_split(mt, plan.c, plan.w, y_dtype),
-                           dim3(static_cast<unsigned>(plan.groups * plan.parts)),
-                           dim3(static_cast<unsigned>(kWave * plan.w)), plan.lds, hs, sa);
+        const dim3 grid(static_cast<unsigned>(plan.groups * plan.parts)), block(static_cast<unsigned>(kWave * plan.w));
+        if (describe) {
+            *describe = kernel_text("nvfp4_skinny_split", {plan.c, mt, plan.w}, y_dtype, grid, block, plan.lds) +
+                        " parts=" + std::to_string(plan.parts);
+            return NVFP4_OK;
+        }
+        hipLaunchKernelGGL(pick_split(mt, plan.c, plan.w, y_dtype), grid, block, plan.lds, hs, sa);
     } else if (kernel == NVFP4_KERNEL_TILE) {
-        hipLaunchKernelGGL(pick_tile(mt, pc, tnb, y_dtype), dim3(static_cast<unsigned>((n + 16 * pc - 1) / (16 * pc))),
-                           dim3(static_cast<unsigned>(kWave * tile.waves)), tile_bytes, hs, a);
+        const dim3 grid(static_cast<unsigned>((n + 16 * pc - 1) / (16 * pc))),
+            block(static_cast<unsigned>(kWave * tile.waves));
+        if (describe) {
+            *describe = kernel_text("nvfp4_skinny_tile", {pc, mt, tnb}, y_dtype, grid, block, tile_bytes);
+            return NVFP4_OK;
+        }
+        hipLaunchKernelGGL(pick_tile(mt, pc, tnb, y_dtype), grid, block, tile_bytes, hs, a);
     } else {
         // The generic per-tile kernel (register loads, any shape); x goes
         // through LDS when it fits in 64 KB.  pick_kernel caps the pipeline
@@ -1663,6 +1693,11 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
         const size_t lds = xlds && x_bytes > part_bytes ? x_bytes : part_bytes;
         const dim3 grid(static_cast<unsigned>((n + tile.cols - 1) / tile.cols));
         const dim3 block(static_cast<unsigned>(kWave * tile.waves));
+        if (describe) {
+            *describe = kernel_text("nvfp4_skinny", {c, mt, generic_unroll(tile.unroll, c, xlds), xlds ? 1 : 0},
+                                    y_dtype, grid, block, lds);
+            return NVFP4_OK;
+        }
         hipLaunchKernelGGL(pick_kernel(mt, tile.cols, tile.unroll, xlds, y_dtype), grid, block, lds, hs, a);
     }
     if (hipGetLastError() != hipSuccess) return NVFP4_ERR_HIP;
@@ -1689,6 +1724,20 @@ extern "C" int nvfp4_linear_noalloc(const void* x_bf16, const uint8_t* w_packed,
     if (nvfp4::load_tile_override() != NVFP4_OK) return NVFP4_ERR_TILEFILE;
     return launch(x_bf16, w_packed, scales_e4m3, tensor_scale, y, m, n, k, y_dtype, stream,
                   nvfp4::tile_for(n, k), NVFP4_KERNEL_AUTO, true);
+}
+
+extern "C" int nvfp4_launch_info(int64_t m, int64_t n, int64_t k, int y_dtype, char* buf, int64_t buflen) {
+    if (!buf) return NVFP4_ERR_NULL;
+    int st = nvfp4_linear_shape_ok(m, n, k);
+    if (st != NVFP4_OK) return st;
+    if (nvfp4::load_tile_override() != NVFP4_OK) return NVFP4_ERR_TILEFILE;
+    std::string s;
+    st = launch(nullptr, nullptr, nullptr, 1.0f, nullptr, m, n, k, y_dtype, nullptr, nvfp4::tile_for(n, k),
+                NVFP4_KERNEL_AUTO, false, &s);
+    if (st != NVFP4_OK) return st;
+    if ((int64_t)s.size() + 1 > buflen) return NVFP4_ERR_BUFFER;
+    std::memcpy(buf, s.c_str(), s.size() + 1);
+    return NVFP4_OK;
 }
 
 extern "C" int nvfp4_linear_tiled(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4m3,

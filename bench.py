@@ -43,6 +43,7 @@ PEAK_BF16_MFMA_TFLOPS = 2500.0
 BYTES_PER_WEIGHT = 0.5625          # 4-bit code + one e4m3 byte per 16 weights
 CPU_BASELINE_MIN_S = 10.0           # the oracle runs products until this much CPU time has passed ...
 CPU_BASELINE_MAX_S = 30.0           # ... and stops starting new ones past this
+CPU_BASELINE_LAYERS = 8             # layers whose packed bytes stay on the host for it
 COLD_BYTES = 512 << 20              # weight copies rotated per timed launch sequence
 KERNEL_SOURCES = [os.path.join(ROOT, "verify_nvfp4_w4a16_amd", "csrc", "kernels", f)
                   for f in ("nvfp4_linear.hip",)]
@@ -113,7 +114,7 @@ class Round:
         import verify_nvfp4_w4a16_amd as nv
         self.layers = layers
         self.items = []           # (layer, proj, shape, wp, sc, t)
-        self.host = {}            # (layer, proj) -> (packed, scales, t), layers 0..1 for the CPU baseline
+        self.host = {}            # (layer, proj) -> (packed, scales, t) of the CPU-baseline layers
         jobs = [(l, p) for l in range(layers) for p in range(len(workload.ROUND_SHAPES))]
 
         def gen(job):
@@ -128,7 +129,7 @@ class Round:
                 del w
                 wp = torch.from_numpy(packed).to(dev, non_blocking=False)
                 sc = torch.from_numpy(scales).to(dev, non_blocking=False)
-                if l < 2:
+                if l < CPU_BASELINE_LAYERS:
                     self.host[(l, p)] = (packed, scales, t)
                 self.items.append((l, p, workload.ROUND_SHAPES[p], wp, sc, t))
         torch.cuda.synchronize()
@@ -314,8 +315,8 @@ def config_timings(torch, dev, stream) -> dict:
 
 def cpu_baseline(torch, dev, rnd: Round, launches: dict, ms_list) -> dict:
     """The oracle on this host's cores over a bounded sample of the same
-    workload: the decode round's products of layers 0 and 1, in round order at
-    each timed M, until about CPU_BASELINE_MIN_S seconds of oracle time; each
+    workload: the decode round's products of its first layers, in round order
+    at each timed M, until about CPU_BASELINE_MIN_S seconds of oracle time; each
     product's columns are split over one worker thread per core (NumPy's
     decode and matmul release the GIL), BLAS single-threaded per worker.  The
     GPU's outputs of the same products are checked against it."""
@@ -326,7 +327,7 @@ def cpu_baseline(torch, dev, rnd: Round, launches: dict, ms_list) -> dict:
     weight_bytes = 0
     worst = 0.0
     done = []
-    jobs = [(m, idx) for idx in range(8) for m in ms_list]
+    jobs = [(m, idx) for idx in range(4 * min(CPU_BASELINE_LAYERS, rnd.layers)) for m in ms_list]
     with threadpoolctl.threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(cores) as ex:
         for m, idx in jobs:
             if total_s >= CPU_BASELINE_MIN_S and len(done) >= len(ms_list) * 4:

@@ -26,7 +26,9 @@ from .formats import E2M1, E4M3, e2m1_value, e4m3_value
 from .linear import (unpack_codes, dequant, linear_ref, bound, accept,
                      max_violation, tolerance, bf16_bits_to_f64)
 from .quant import quantize_ref, e4m3_round, e2m1_round
+from .expand import round_to_bf16, dequant_bf16
 
 __all__ = ["E2M1", "E4M3", "e2m1_value", "e4m3_value", "unpack_codes",
            "dequant", "linear_ref", "bound", "accept", "max_violation", "tolerance",
-           "bf16_bits_to_f64", "quantize_ref", "e4m3_round", "e2m1_round"]
+           "bf16_bits_to_f64", "quantize_ref", "e4m3_round", "e2m1_round", "round_to_bf16",
+           "dequant_bf16"]

@@ -246,6 +246,63 @@ int nvfp4_linear_tiled(const void* x_bf16, const uint8_t* w_packed,
 int nvfp4_tile_info(int64_t n, int64_t k, char* buf, int64_t buflen);
 
 /*
+ * Host, pure.  The shape contract of nvfp4_gemm and nvfp4_gemm_expanded:
+ * 0 <= M <= 65535 * 128, 1 <= N <= 2^28, 256 <= K <= 2^20 with K % 256 == 0,
+ * M * N <= 2^40 ("Module ops" w4a16_tc_rows_shape_ok likewise checks a
+ * kernel's contract without a GPU).  Returns NVFP4_OK or NVFP4_ERR_SHAPE.
+ */
+int nvfp4_gemm_shape_ok(int64_t m, int64_t n, int64_t k);
+
+/*
+ * Device, asynchronous on `stream`.  The product of nvfp4_linear for any row
+ * count: the regime of "10 Kernels" 10.2 for 33 to about 1,024 rows
+ * (prefill chunks), the "Module ops" w4a16_gemm / w4a16_gemm_n128_m128
+ * operation C = A @ dequant(B).  Arguments, layouts, alignment and ownership
+ * as nvfp4_linear; M == 0 launches nothing.  The K order is the (N, K) tile's
+ * (as nvfp4_linear), so each row's bits are those nvfp4_linear gives it, for
+ * every M ("10 Kernels" 10.1).  No allocation, no host sync.  Workgroups own
+ * 128 rows x 64 columns.
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, HIP, DEVICE, TILEFILE.
+ */
+int nvfp4_gemm(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4m3,
+               float tensor_scale, void* y, int64_t m, int64_t n, int64_t k, int y_dtype,
+               void* stream);
+
+/*
+ * Device, asynchronous.  Picks the kernel by row count over one stored
+ * format, as "10 Kernels" 10.2's table does: nvfp4_linear for M <= 32,
+ * nvfp4_gemm above.  Both give every row the same bits.  Errors: those of the
+ * call it makes.
+ */
+int nvfp4_matmul(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4m3,
+                 float tensor_scale, void* y, int64_t m, int64_t n, int64_t k, int y_dtype,
+                 void* stream);
+
+/*
+ * Device, asynchronous.  Expands an NVFP4 weight to bf16 w_bf16[N, K]
+ * (caller-owned, 16-byte aligned, N * K * 2 bytes), like "Module ops"
+ * dequant_nvfp4_to_bf16: with apply_tensor_scale = 1 each element is the
+ * exact t * e4m3 * e2m1 rounded once to the nearest bf16 (ties to even); with
+ * 0 it is e4m3 * e2m1, exact in bf16 (the weight nvfp4_gemm_expanded takes).
+ * w_packed: device, [N, K/2], 4-byte aligned; scales_e4m3: device, [N, K/16].
+ * Shape: 1 <= N <= 2^28, 16 <= K <= 2^20, K % 16 == 0.
+ * Errors: NULL, SHAPE, ALIGN, DTYPE (apply_tensor_scale not 0 or 1), HIP.
+ */
+int nvfp4_dequant_bf16(const uint8_t* w_packed, const uint8_t* scales_e4m3, float tensor_scale,
+                       int apply_tensor_scale, void* w_bf16, int64_t n, int64_t k, void* stream);
+
+/*
+ * Device, asynchronous.  The third regime of "10 Kernels" 10.2 (above about
+ * 1,024 rows: expand to BF16 once, then a plain GEMM): nvfp4_gemm reading the
+ * weight as w_bf16[N, K] = e4m3 * e2m1 (nvfp4_dequant_bf16 with
+ * apply_tensor_scale = 0, 16-byte aligned), with tensor_scale applied once to
+ * the fp32 sum, so every row's bits equal nvfp4_gemm's.  Other arguments and
+ * errors as nvfp4_gemm.
+ */
+int nvfp4_gemm_expanded(const void* x_bf16, const void* w_bf16, float tensor_scale, void* y,
+                        int64_t m, int64_t n, int64_t k, int y_dtype, void* stream);
+
+/*
  * Host.  Writes into buf (NUL-terminated) the kernel nvfp4_linear launches for
  * an M x N x K product with this output type on the current device, as its
  * template name reads in a kernel trace, then its grid, block and LDS bytes

@@ -1,0 +1,147 @@
+"""The many-row regime (nvfp4_gemm), the expand-to-bf16 regime
+(nvfp4_dequant_bf16 + nvfp4_gemm_expanded) and the row-count dispatcher
+(nvfp4_matmul) on the GPU: parity with the fp64 oracle, bit-exact expansion,
+and every row's bits equal to nvfp4_linear's for the same row (gpu)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import verify_nvfp4_w4a16_amd as nv
+import workload
+from tests._gpu import DEV, Weight, bits, check_parity, upload_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _gemm(xd, w, m, out_dtype=torch.bfloat16, fn=None):
+    y = torch.empty((m, w.n), dtype=out_dtype, device=DEV)
+    od = nv.OUT_F32 if out_dtype == torch.float32 else nv.OUT_BF16
+    st = (fn or nv.gemm_raw)(xd.data_ptr(), w.wp.data_ptr(), w.sc.data_ptr(), w.t, y.data_ptr(), m, w.n, w.k,
+                             od, _stream())
+    torch.cuda.synchronize()
+    assert st == nv.OK, st
+    return y
+
+
+def _linear(xd, w, m, out_dtype=torch.bfloat16):
+    y = torch.empty((m, w.n), dtype=out_dtype, device=DEV)
+    od = nv.OUT_F32 if out_dtype == torch.float32 else nv.OUT_BF16
+    st = nv.linear_raw(xd.data_ptr(), w.wp.data_ptr(), w.sc.data_ptr(), w.t, y.data_ptr(), m, w.n, w.k, od,
+                       _stream())
+    torch.cuda.synchronize()
+    assert st == nv.OK, st
+    return y
+
+
+def _expanded(w, apply_t):
+    dst = torch.empty((w.n, w.k), dtype=torch.int16, device=DEV)
+    st = nv.dequant_bf16_raw(w.wp.data_ptr(), w.sc.data_ptr(), w.t, 1 if apply_t else 0, dst.data_ptr(),
+                             w.n, w.k, _stream())
+    torch.cuda.synchronize()
+    assert st == nv.OK, st
+    return dst
+
+
+@pytest.mark.parametrize("shape", workload.ROUND_SHAPES, ids=lambda s: f"{s.n}x{s.k}")
+def test_gemm_parity_and_rows_across_m(shape):
+    # The decode round's shapes at 33, 64, 256 and 1024 rows (the regime's
+    # span): within the oracle's tolerance on sampled columns, and each row's
+    # bits the same at every M (the first rows of the 1024-row product).
+    w = Weight.from_f32(workload.weights_f32(shape.n, shape.k, workload.round_weight_seed(0, 0) + shape.n))
+    x = workload.activations_bf16(1024, shape.k, 7000 + shape.k)
+    xd = upload_bits(x)
+    cols = np.unique(np.concatenate([np.arange(16), np.arange(shape.n - 16, shape.n),
+                                     workload.rng(71).integers(0, shape.n, 96)]))
+    full = bits(_gemm(xd, w, 1024)).clone()
+    rows = np.unique(np.concatenate([np.arange(8), workload.rng(72).integers(0, 1024, 56)]))
+    check_parity(_gemm(xd, w, 1024)[torch.from_numpy(rows).to(DEV)], x[rows], w, cols=cols,
+                 label=f"gemm {shape.n}x{shape.k} M=1024 sampled rows")
+    for m in (33, 64, 256):
+        y = _gemm(xd, w, m)
+        assert torch.equal(bits(y), full[:m]), f"{shape.n}x{shape.k}: rows at M={m} differ from M=1024"
+        if m == 33:
+            check_parity(y, x[:m], w, cols=cols, label=f"gemm {shape.n}x{shape.k} M={m}")
+
+
+def test_gemm_rows_equal_linear_rows():
+    # The same row gets the same bits from nvfp4_gemm at any M and from
+    # nvfp4_linear at 1..32 rows (one K order for both), on the row-count
+    # dispatcher's boundary too (32 -> linear, 33 -> gemm).
+    n, k = 4136, 4096                              # ragged columns for both kernels' tiles
+    w = Weight.from_f32(workload.weights_f32(n, k, 81))
+    x = workload.activations_bf16(96, k, 82)
+    xd = upload_bits(x)
+    g = bits(_gemm(xd, w, 96)).clone()
+    for r0 in (0, 32, 64):
+        lin = bits(_linear(upload_bits(x[r0:r0 + 32]), w, 32))
+        assert torch.equal(lin, g[r0:r0 + 32]), r0
+    assert torch.equal(bits(_linear(upload_bits(x[5:6]), w, 1)), g[5:6])
+    for m in (32, 33):
+        y = _gemm(xd, w, m, fn=nv.matmul_raw)
+        assert torch.equal(bits(y), g[:m]), m
+    check_parity(_gemm(xd, w, 96, torch.float32), x, w, label="gemm 4136x4096 M=96 fp32")
+
+
+def test_gemm_ragged_rows_random_codes():
+    # Partial row tiles (M = 200, 129, 1), columns past N, every code and
+    # scale byte incl. subnormal scales and zero groups, split shapes.
+    for n, k, m in [(333, 1024, 200), (4111, 512, 129), (17, 256, 1), (1000, 2048, 300)]:
+        packed, scales = workload.random_codes(n, k, n + k)
+        scales[:, ::5] = 0
+        w = Weight(packed, scales, 0.0371)
+        x = workload.activations_bf16(m, k, n * 3 + m, outliers=True)
+        xd = upload_bits(x)
+        check_parity(_gemm(xd, w, m), x, w, label="gemm random codes")
+        check_parity(_gemm(xd, w, m, torch.float32), x, w, label="gemm random codes fp32")
+
+
+def test_dequant_bf16_bit_exact():
+    # Expanded weights equal the oracle's, bit for bit: exact e4m3 x e2m1, and
+    # t * e4m3 * e2m1 rounded once (ties to even) with the tensor scale.
+    for n, k, t in [(64, 4096, 3.7e-5), (333, 1024, 0.25), (7, 16, 1.0)]:
+        packed, scales = workload.random_codes(n, k, n * k)
+        scales[0, :] = np.arange(scales.shape[1]) % 8          # subnormal scale bytes
+        w = Weight(packed, scales, float(np.float32(t)))
+        for apply_t in (False, True):
+            got = _expanded(w, apply_t).cpu().numpy().view(np.uint16)
+            want = oracle.dequant_bf16(packed, scales, w.t, apply_t)
+            assert np.array_equal(got, want), (n, k, apply_t)
+
+
+def test_expanded_gemm_equals_gemm():
+    # Expand once (no tensor scale), then the bf16-weight product: the same
+    # bits as the NVFP4 product, at a large M and on ragged shapes.
+    for n, k, m in [(8192, 4096, 1536), (4136, 4096, 70), (333, 1024, 200)]:
+        w = Weight.from_f32(workload.weights_f32(n, k, n + m))
+        x = workload.activations_bf16(m, k, 91 + m)
+        xd = upload_bits(x)
+        ref = bits(_gemm(xd, w, m)).clone()
+        wbf = _expanded(w, False)
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+        st = nv.gemm_expanded_raw(xd.data_ptr(), wbf.data_ptr(), w.t, y.data_ptr(), m, n, k, nv.OUT_BF16, _stream())
+        torch.cuda.synchronize()
+        assert st == nv.OK
+        assert torch.equal(bits(y), ref), (n, k, m)
+
+
+def test_gemm_contract_and_errors():
+    assert nv.gemm_shape_ok(0, 1, 256) and nv.gemm_shape_ok(4096, 8192, 4096)
+    assert not nv.gemm_shape_ok(1, 1, 100) and not nv.gemm_shape_ok(-1, 1, 256)
+    w = Weight.from_f32(workload.weights_f32(64, 256, 3))
+    y = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device=DEV)
+    assert nv.gemm_raw(x.data_ptr(), w.wp.data_ptr(), w.sc.data_ptr(), w.t, y.data_ptr(), 0, 64, 256,
+                       nv.OUT_BF16, _stream()) == nv.OK
+    xr = torch.zeros((3, 256), dtype=torch.bfloat16, device=DEV)
+    y3 = torch.empty((3, 64), dtype=torch.bfloat16, device=DEV)
+    assert nv.gemm_raw(xr.data_ptr() + 2, w.wp.data_ptr(), w.sc.data_ptr(), w.t, y3.data_ptr(), 3, 64, 256,
+                       nv.OUT_BF16, _stream()) == nv.ERR_ALIGN
+    assert nv.gemm_raw(xr.data_ptr(), w.wp.data_ptr(), w.sc.data_ptr(), w.t, y3.data_ptr(), 3, 64, 256,
+                       7, _stream()) == nv.ERR_DTYPE
+    assert nv.gemm_raw(xr.data_ptr(), 0, w.sc.data_ptr(), w.t, y3.data_ptr(), 3, 64, 256,
+                       nv.OUT_BF16, _stream()) == nv.ERR_NULL

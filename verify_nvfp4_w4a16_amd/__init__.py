@@ -28,7 +28,8 @@ K_MULTIPLE = 256
 EXPORTED = ("nvfp4_pack", "nvfp4_check_scales", "nvfp4_linear_shape_ok", "nvfp4_init",
             "nvfp4_linear", "nvfp4_linear_tiled", "nvfp4_tile_info", "nvfp4_strerror",
             "nvfp4_timeout_status", "nvfp4_linear_noalloc", "nvfp4_launch_info",
-            "nvfp4_read_probe")
+            "nvfp4_read_probe", "nvfp4_gemm_shape_ok", "nvfp4_gemm", "nvfp4_matmul",
+            "nvfp4_dequant_bf16", "nvfp4_gemm_expanded")
 
 
 class Tile(ctypes.Structure):
@@ -72,6 +73,11 @@ def _load() -> ctypes.CDLL:
     lib.nvfp4_timeout_status.argtypes = [ctypes.POINTER(ctypes.c_int)]
     lib.nvfp4_launch_info.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.c_char_p, i64]
     lib.nvfp4_read_probe.argtypes = [vp, i64, vp, i64, vp, vp]
+    lib.nvfp4_gemm_shape_ok.argtypes = [i64, i64, i64]
+    lib.nvfp4_gemm.argtypes = [vp, vp, vp, ctypes.c_float, vp, i64, i64, i64, ctypes.c_int, vp]
+    lib.nvfp4_matmul.argtypes = [vp, vp, vp, ctypes.c_float, vp, i64, i64, i64, ctypes.c_int, vp]
+    lib.nvfp4_dequant_bf16.argtypes = [vp, vp, ctypes.c_float, ctypes.c_int, vp, i64, i64, vp]
+    lib.nvfp4_gemm_expanded.argtypes = [vp, vp, ctypes.c_float, vp, i64, i64, i64, ctypes.c_int, vp]
     lib.nvfp4_strerror.argtypes = [ctypes.c_int]
     lib.nvfp4_strerror.restype = ctypes.c_char_p
     for name in EXPORTED:
@@ -177,6 +183,36 @@ def linear_noalloc_raw(x_ptr: int, w_ptr: int, s_ptr: int, tensor_scale: float, 
     """nvfp4_linear_noalloc on raw device addresses; returns the status."""
     return _lib().nvfp4_linear_noalloc(x_ptr, w_ptr, s_ptr, ctypes.c_float(tensor_scale), y_ptr,
                                        m, n, k, y_dtype, stream)
+
+
+def gemm_raw(x_ptr: int, w_ptr: int, s_ptr: int, tensor_scale: float, y_ptr: int,
+             m: int, n: int, k: int, y_dtype: int, stream: int) -> int:
+    """nvfp4_gemm on raw device addresses; returns the status."""
+    return _lib().nvfp4_gemm(x_ptr, w_ptr, s_ptr, ctypes.c_float(tensor_scale), y_ptr, m, n, k, y_dtype, stream)
+
+
+def matmul_raw(x_ptr: int, w_ptr: int, s_ptr: int, tensor_scale: float, y_ptr: int,
+               m: int, n: int, k: int, y_dtype: int, stream: int) -> int:
+    """nvfp4_matmul on raw device addresses; returns the status."""
+    return _lib().nvfp4_matmul(x_ptr, w_ptr, s_ptr, ctypes.c_float(tensor_scale), y_ptr, m, n, k, y_dtype, stream)
+
+
+def dequant_bf16_raw(w_ptr: int, s_ptr: int, tensor_scale: float, apply_tensor_scale: int, dst_ptr: int,
+                     n: int, k: int, stream: int) -> int:
+    """nvfp4_dequant_bf16 on raw device addresses; returns the status."""
+    return _lib().nvfp4_dequant_bf16(w_ptr, s_ptr, ctypes.c_float(tensor_scale), apply_tensor_scale, dst_ptr,
+                                     n, k, stream)
+
+
+def gemm_expanded_raw(x_ptr: int, wbf_ptr: int, tensor_scale: float, y_ptr: int,
+                      m: int, n: int, k: int, y_dtype: int, stream: int) -> int:
+    """nvfp4_gemm_expanded on raw device addresses; returns the status."""
+    return _lib().nvfp4_gemm_expanded(x_ptr, wbf_ptr, ctypes.c_float(tensor_scale), y_ptr, m, n, k, y_dtype,
+                                      stream)
+
+
+def gemm_shape_ok(m: int, n: int, k: int) -> bool:
+    return _lib().nvfp4_gemm_shape_ok(m, n, k) == OK
 
 
 def linear_tiled_raw(x_ptr: int, w_ptr: int, s_ptr: int, tensor_scale: float, y_ptr: int,

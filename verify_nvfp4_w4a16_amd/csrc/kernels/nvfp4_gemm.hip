@@ -1,0 +1,362 @@
+// NVFP4 weight-only product for many rows (the prefill regime of "10 Kernels"
+// 10.2, rows 33 to about 1024, and beyond through the expanded weight):
+//   y[m, n] = t * sum_k x[m, k] * e4m3(s[n, k/16]) * e2m1(q[n, k]),  any M.
+//
+// "Module ops" w4a16_gemm (C = A @ dequant(B), A bf16 [M, K], B NVFP4) is the
+// operation; w4a16_gemm_n128_m128 loads one weight tile for 128 rows.  Here a
+// workgroup owns 128 rows x 64 columns: x comes into LDS one 128-k block at a
+// time (registers -> LDS, double-buffered), and each of the four wavefronts
+// decodes the weights of its 32 columns in registers and multiplies them
+// with 64 rows of x (v_mfma_f32_16x16x32_bf16, 4 x 2 tiles), so one decoded
+// operand serves four MFMAs.  Column tiles are the fastest grid dimension, so
+// the eight XCDs (workgroups dealt round-robin) each keep one eighth of the
+// weight columns in their L2 across the row tiles.
+//
+// The K order is the one of every other kernel of this library, fixed by the
+// (N, K) tile: K cut into `waves` segments, each one MFMA chain in increasing
+// k, added in the two-level order (chains in segment order within a group,
+// group sums in group order).  The MFMA inputs of an output element are the
+// same bf16 values too (x as given, the exactly decoded weight), so every row
+// here has the bits nvfp4_linear gives it at 1..32 rows ("10 Kernels" 10.1),
+// at every M.
+//
+// With BF16W the weight is read as an already expanded bf16 matrix [N, K]
+// holding e2m1 x e4m3 exactly (nvfp4_dequant_bf16 without the tensor scale),
+// the pages' "expand to BF16 once" path for very large M; the tensor scale is
+// still applied once to the fp32 sum, so the bits are the same again.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "nvfp4_w4a16.h"
+#include "nvfp4_common.h"
+#include "setup.h"
+#include "../host/tiles.h"
+
+namespace {
+
+constexpr int kRows = 128;              // rows per workgroup
+constexpr int kCols = 64;               // columns per workgroup
+constexpr int kMT = 4;                  // 16-row tiles per wavefront
+constexpr int kC = 2;                   // 16-column tiles per wavefront
+constexpr int kThreads = 256;
+constexpr int kPitch = kBlockK + 8;     // LDS row pitch of an x block, bf16 elements
+constexpr int kXVec = kRows * kBlockK / 8 / kThreads;   // 16-byte x pieces per thread per block
+constexpr size_t kGemmLds = 2 * size_t(kRows) * kPitch * sizeof(uint16_t);
+constexpr int kMaxGridY = 65535;
+
+struct GemmArgs {
+    const uint16_t* x;      // bf16 [M, K]
+    const uint8_t* wp;      // [N, K/2] packed e2m1 (or bf16 [N, K] with BF16W)
+    const uint8_t* sc;      // [N, K/16] e4m3 (unused with BF16W)
+    void* y;                // [M, N]
+    float t;
+    int m, n, k;
+    int k_per_wave;         // segment length
+    int group;              // segments per segment group
+};
+
+// The B operands of one 128-k block for a lane's kC columns: with NVFP4
+// weights 16 packed bytes (32 k) and the block's 8 scale bytes per column;
+// with bf16 weights the 4 x 8 k of the column.
+template <bool BF16W>
+struct BRegs;
+
+template <>
+struct BRegs<false> {
+    u32x4 w[kC];
+    uint64_t s[kC];
+};
+
+template <>
+struct BRegs<true> {
+    u32x4 w[kC][4];
+};
+
+template <bool BF16W, bool OUT_F32>
+__global__ void __launch_bounds__(kThreads)
+nvfp4_gemm_kernel(GemmArgs a) {
+    extern __shared__ __align__(16) uint16_t xs[];     // [2][kRows][kPitch]
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wave = tid / kWave;
+    const int wm = wave / 2, wn = wave % 2;
+    const int col_lane = lane % 16;
+    const int kq = lane / 16;
+    const int row0 = blockIdx.y * kRows;
+    const int col0 = blockIdx.x * kCols + wn * kC * 16;
+    const int nblocks = a.k / kBlockK;
+    const int seg_blocks = a.k_per_wave / kBlockK;
+
+    // Rows past M and columns past N read the last valid one (never stored).
+    const uint8_t* wrow[kC];
+    const uint8_t* srow[kC];
+#pragma unroll
+    for (int c = 0; c < kC; ++c) {
+        const int n = min(col0 + 16 * c + col_lane, a.n - 1);
+        if constexpr (BF16W) {
+            wrow[c] = a.wp + (int64_t)n * a.k * 2;
+            srow[c] = nullptr;
+        } else {
+            wrow[c] = a.wp + (int64_t)n * (a.k / 2);
+            srow[c] = a.sc + (int64_t)n * (a.k / 16);
+        }
+    }
+    // this thread's 16-byte pieces of an x block: piece v = tid + 256 i is
+    // row v / 16, k 8 (v % 16) of the block
+    const uint16_t* xsrc[kXVec];
+    int xdst[kXVec];
+#pragma unroll
+    for (int i = 0; i < kXVec; ++i) {
+        const int v = tid + kThreads * i;
+        const int r = v / 16, p = v % 16;
+        xsrc[i] = a.x + (int64_t)min(row0 + r, a.m - 1) * a.k + 8 * p;
+        xdst[i] = r * kPitch + 8 * p;
+    }
+
+    auto load_b = [&](BRegs<BF16W>& b, int kb) {
+#pragma unroll
+        for (int c = 0; c < kC; ++c) {
+            if constexpr (BF16W) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    b.w[c][s] = load16_stream(wrow[c] + (int64_t)(kb + 32 * kq + 8 * s) * 2);
+            } else {
+                b.w[c] = load16_stream(wrow[c] + kb / 2 + 16 * kq);
+                b.s[c] = load8_stream(srow[c] + kb / 16);
+            }
+        }
+    };
+    u32x4 xr[kXVec];
+    auto load_x = [&](int kb) {
+#pragma unroll
+        for (int i = 0; i < kXVec; ++i) xr[i] = load16(xsrc[i] + kb);
+    };
+    auto store_x = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < kXVec; ++i)
+            *reinterpret_cast<u32x4*>(xs + buf * kRows * kPitch + xdst[i]) = xr[i];
+    };
+
+    f32x4 acc[kMT][kC], grp[kMT][kC], tot[kMT][kC];
+#pragma unroll
+    for (int t = 0; t < kMT; ++t)
+#pragma unroll
+        for (int c = 0; c < kC; ++c) acc[t][c] = grp[t][c] = tot[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    BRegs<BF16W> bcur, bnext;
+    load_x(0);
+    load_b(bcur, 0);
+    store_x(0);
+    __syncthreads();
+
+    for (int b = 0; b < nblocks; ++b) {
+        const bool more = b + 1 < nblocks;
+        if (more) {
+            load_x((b + 1) * kBlockK);
+            load_b(bnext, (b + 1) * kBlockK);
+        }
+        // multiply block b: per 32-k slice, the wavefront's kC B operands,
+        // then each of its kMT A operands against them
+        const uint16_t* xb = xs + (b & 1) * kRows * kPitch;
+        float g0[kC], g1[kC];
+        if constexpr (!BF16W) {
+#pragma unroll
+            for (int c = 0; c < kC; ++c) {
+                const uint32_t d = static_cast<uint32_t>(bcur.s[c] >> (16 * kq));
+                g0[c] = __builtin_amdgcn_cvt_f32_fp8(d, 0);
+                g1[c] = __builtin_amdgcn_cvt_f32_fp8(d, 1);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            bf16x8 bv[kC];
+#pragma unroll
+            for (int c = 0; c < kC; ++c) {
+                if constexpr (BF16W)
+                    bv[c] = as_bf16x8(bcur.w[c][s]);
+                else
+                    bv[c] = decode8(bcur.w[c][s], s < 2 ? g0[c] : g1[c]);
+            }
+#pragma unroll
+            for (int t = 0; t < kMT; ++t) {
+                const int r = wm * 16 * kMT + 16 * t + col_lane;
+                const bf16x8 xa = as_bf16x8(*reinterpret_cast<const u32x4*>(xb + r * kPitch + 32 * kq + 8 * s));
+#pragma unroll
+                for (int c = 0; c < kC; ++c)
+                    acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bv[c], acc[t][c], 0, 0, 0);
+            }
+        }
+        // end of a segment: its chain joins its group's sum, and at the end
+        // of a group the group sum joins the total (first ones as they are)
+        if ((b + 1) % seg_blocks == 0) {
+            const int seg = (b + 1) / seg_blocks - 1;
+            const bool gfirst_seg = seg % a.group == 0;
+            const bool gend = (seg + 1) % a.group == 0;
+            const bool first_group = seg / a.group == 0;
+#pragma unroll
+            for (int t = 0; t < kMT; ++t)
+#pragma unroll
+                for (int c = 0; c < kC; ++c) {
+                    grp[t][c] = gfirst_seg ? acc[t][c] : grp[t][c] + acc[t][c];
+                    acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (gend) tot[t][c] = first_group ? grp[t][c] : tot[t][c] + grp[t][c];
+                }
+        }
+        if (more) {
+            store_x((b + 1) & 1);
+            bcur = bnext;
+            __syncthreads();
+        }
+    }
+
+#pragma unroll
+    for (int t = 0; t < kMT; ++t)
+#pragma unroll
+        for (int c = 0; c < kC; ++c) {
+            const int n = col0 + 16 * c + col_lane;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int m = row0 + wm * 16 * kMT + 16 * t + 4 * kq + j;
+                if (m < a.m && n < a.n) {
+                    const float r = tot[t][c][j] * a.t;
+                    if (OUT_F32)
+                        static_cast<float*>(a.y)[(int64_t)m * a.n + n] = r;
+                    else
+                        static_cast<uint16_t*>(a.y)[(int64_t)m * a.n + n] = f32_to_bf16_rne(r);
+                }
+            }
+        }
+}
+
+// Expands NVFP4 to bf16 [N, K]: each thread one packed dword (8 k) of one
+// row.  e2m1 x e4m3 is exact in fp32 and in bf16; with APPLY_T it is then
+// multiplied by t in fp32 (one rounding) and rounded to bf16 (a second), which
+// equals one rounding of the exact t * e4m3 * e2m1 to bf16 since fp32 carries
+// more than twice bf16's significand bits plus two.
+template <bool APPLY_T>
+__global__ void __launch_bounds__(256)
+nvfp4_dequant_kernel(const uint8_t* wp, const uint8_t* sc, float t, uint16_t* dst, int64_t n, int64_t k) {
+    const int64_t per_row = k / 8;
+    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= n * per_row) return;
+    const int64_t row = i / per_row, c8 = i % per_row;
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(wp + row * (k / 2) + c8 * 4);
+    const float scale = __builtin_amdgcn_cvt_f32_fp8(static_cast<uint32_t>(sc[row * (k / 16) + c8 / 2]), 0);
+    f32x2 v[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0),
+                  __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1),
+                  __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2),
+                  __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3)};
+    uint16_t out[8];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        float p0 = v[b][0] * scale, p1 = v[b][1] * scale;
+        if (APPLY_T) {
+            p0 = p0 * t;
+            p1 = p1 * t;
+        }
+        out[2 * b] = f32_to_bf16_rne(p0);
+        out[2 * b + 1] = f32_to_bf16_rne(p1);
+    }
+    u32x4 o;
+    __builtin_memcpy(&o, out, sizeof o);
+    *reinterpret_cast<u32x4*>(dst + row * k + c8 * 8) = o;
+}
+
+using GemmFn = void (*)(GemmArgs);
+
+GemmFn pick_gemm(bool bf16w, int y_dtype) {
+    if (bf16w) return y_dtype == NVFP4_OUT_F32 ? nvfp4_gemm_kernel<true, true> : nvfp4_gemm_kernel<true, false>;
+    return y_dtype == NVFP4_OUT_F32 ? nvfp4_gemm_kernel<false, true> : nvfp4_gemm_kernel<false, false>;
+}
+
+int gemm_launch(const void* x, const void* w, const uint8_t* scales, float t, void* y, int64_t m, int64_t n,
+                int64_t k, int y_dtype, void* stream, bool bf16w) {
+    int st = nvfp4_gemm_shape_ok(m, n, k);
+    if (st != NVFP4_OK) return st;
+    if (y_dtype != NVFP4_OUT_BF16 && y_dtype != NVFP4_OUT_F32) return NVFP4_ERR_DTYPE;
+    if (m == 0) return NVFP4_OK;
+    if (!x || !w || (!bf16w && !scales) || !y) return NVFP4_ERR_NULL;
+    auto misaligned = [](const void* p, uintptr_t al) { return (reinterpret_cast<uintptr_t>(p) & (al - 1)) != 0; };
+    if (misaligned(x, 16) || misaligned(w, 16) || (!bf16w && misaligned(scales, 16)) ||
+        misaligned(y, y_dtype == NVFP4_OUT_F32 ? 4 : 2))
+        return NVFP4_ERR_ALIGN;
+    if (nvfp4::load_tile_override() != NVFP4_OK) return NVFP4_ERR_TILEFILE;
+    st = nvfp4::device_setup();
+    if (st != NVFP4_OK) return st;
+    const nvfp4::Tile tile = nvfp4::tile_for(n, k);
+    GemmArgs a;
+    a.x = static_cast<const uint16_t*>(x);
+    a.wp = static_cast<const uint8_t*>(w);
+    a.sc = scales;
+    a.y = y;
+    a.t = t;
+    a.m = static_cast<int>(m);
+    a.n = static_cast<int>(n);
+    a.k = static_cast<int>(k);
+    a.k_per_wave = static_cast<int>(k / tile.waves);
+    a.group = tile.waves / tile.split;
+    const dim3 grid(static_cast<unsigned>((n + kCols - 1) / kCols), static_cast<unsigned>((m + kRows - 1) / kRows));
+    hipLaunchKernelGGL(pick_gemm(bf16w, y_dtype), grid, dim3(kThreads), kGemmLds, static_cast<hipStream_t>(stream), a);
+    return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+}  // namespace
+
+namespace nvfp4 {
+
+int gemm_setup() {
+    for (int bw = 0; bw <= 1; ++bw)
+        for (int od = 0; od <= 1; ++od)
+            if (hipFuncSetAttribute(reinterpret_cast<const void*>(pick_gemm(bw != 0, od)),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    static_cast<int>(kGemmLds)) != hipSuccess)
+                return NVFP4_ERR_HIP;
+    return NVFP4_OK;
+}
+
+}  // namespace nvfp4
+
+extern "C" int nvfp4_gemm_shape_ok(int64_t m, int64_t n, int64_t k) {
+    if (m < 0 || m > int64_t(kMaxGridY) * kRows) return NVFP4_ERR_SHAPE;
+    if (n < 1 || n > (int64_t(1) << 28)) return NVFP4_ERR_SHAPE;
+    if (k < NVFP4_K_MULTIPLE || k > (int64_t(1) << 20) || k % NVFP4_K_MULTIPLE) return NVFP4_ERR_SHAPE;
+    if (m * n > (int64_t(1) << 40)) return NVFP4_ERR_SHAPE;
+    return NVFP4_OK;
+}
+
+extern "C" int nvfp4_gemm(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4m3,
+                          float tensor_scale, void* y, int64_t m, int64_t n, int64_t k, int y_dtype, void* stream) {
+    return gemm_launch(x_bf16, w_packed, scales_e4m3, tensor_scale, y, m, n, k, y_dtype, stream, false);
+}
+
+extern "C" int nvfp4_gemm_expanded(const void* x_bf16, const void* w_bf16, float tensor_scale, void* y,
+                                   int64_t m, int64_t n, int64_t k, int y_dtype, void* stream) {
+    return gemm_launch(x_bf16, w_bf16, nullptr, tensor_scale, y, m, n, k, y_dtype, stream, true);
+}
+
+extern "C" int nvfp4_dequant_bf16(const uint8_t* w_packed, const uint8_t* scales_e4m3, float tensor_scale,
+                                  int apply_tensor_scale, void* w_bf16, int64_t n, int64_t k, void* stream) {
+    if (!w_packed || !scales_e4m3 || !w_bf16) return NVFP4_ERR_NULL;
+    if (n < 1 || n > (int64_t(1) << 28) || k < 16 || k > (int64_t(1) << 20) || k % 16) return NVFP4_ERR_SHAPE;
+    if (apply_tensor_scale != 0 && apply_tensor_scale != 1) return NVFP4_ERR_DTYPE;
+    if ((reinterpret_cast<uintptr_t>(w_packed) & 3) || (reinterpret_cast<uintptr_t>(w_bf16) & 15))
+        return NVFP4_ERR_ALIGN;
+    const int64_t threads = n * (k / 8);
+    const int64_t blocks = (threads + 255) / 256;
+    if (blocks > 0x7fffffff) return NVFP4_ERR_SHAPE;
+    auto fn = apply_tensor_scale ? nvfp4_dequant_kernel<true> : nvfp4_dequant_kernel<false>;
+    hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       w_packed, scales_e4m3, tensor_scale, static_cast<uint16_t*>(w_bf16), n, k);
+    return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+extern "C" int nvfp4_matmul(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4m3,
+                            float tensor_scale, void* y, int64_t m, int64_t n, int64_t k, int y_dtype,
+                            void* stream) {
+    if (m >= 0 && m <= NVFP4_MAX_M)
+        return nvfp4_linear(x_bf16, w_packed, scales_e4m3, tensor_scale, y, m, n, k, y_dtype, stream);
+    return nvfp4_gemm(x_bf16, w_packed, scales_e4m3, tensor_scale, y, m, n, k, y_dtype, stream);
+}

@@ -48,19 +48,11 @@
 #include <type_traits>
 
 #include "nvfp4_w4a16.h"
+#include "nvfp4_common.h"
+#include "setup.h"
 #include "../host/tiles.h"
 
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kWave = 64;
-constexpr int kBlockK = 128;    // k covered by one 16-byte weight load per lane (4 MFMAs)
-constexpr int kMaxLdsBytes = 160 * 1024;
 
 struct Args {
     const uint16_t* x;     // bf16 [M, K]
@@ -89,64 +81,6 @@ __device__ __forceinline__ void fold_segment(f32x4& grp, f32x4& tot, f32x4 v, in
 // before the waits for the current chunk, so two chunks are in flight while
 // one waits (left alone, the scheduler sinks those loads below the waits).
 __device__ __forceinline__ void issue_point() { __builtin_amdgcn_sched_barrier(0); }
-
-__device__ __forceinline__ u32x4 load16(const void* p) {
-    return *reinterpret_cast<const u32x4*>(p);
-}
-
-// Two e2m1 codes of byte `sel` of `w` times the group scale, as a bf16 pair.
-template <int sel>
-__device__ __forceinline__ bf16x2 decode_pair(uint32_t w, float scale) {
-    f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, sel);
-    f32x2 p = {v[0] * scale, v[1] * scale};
-    return __builtin_convertvector(p, bf16x2);
-}
-
-// 8 consecutive k (one dword of packed nibbles) as the B operand.
-__device__ __forceinline__ bf16x8 decode8(uint32_t w, float scale) {
-    bf16x2 a = decode_pair<0>(w, scale);
-    bf16x2 b = decode_pair<1>(w, scale);
-    bf16x2 c = decode_pair<2>(w, scale);
-    bf16x2 d = decode_pair<3>(w, scale);
-    return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
-// fp32 <-> its bits through memcpy: with this compiler, bit-casting a vector
-// element (v[j]) yields element 0 for every j.
-__device__ __forceinline__ uint32_t f32_bits(float f) {
-    uint32_t u;
-    __builtin_memcpy(&u, &f, sizeof u);
-    return u;
-}
-
-__device__ __forceinline__ float bits_f32(uint32_t u) {
-    float f;
-    __builtin_memcpy(&f, &u, sizeof f);
-    return f;
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
-    bf16x8 r;
-    __builtin_memcpy(&r, &v, sizeof r);
-    return r;
-}
-
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-    bf16x2 p = __builtin_convertvector(f32x2{f, 0.0f}, bf16x2);
-    uint16_t out;
-    __builtin_memcpy(&out, &p, sizeof out);
-    return out;
-}
-
-__device__ __forceinline__ u32x4 load16_stream(const void* p) {
-    // Weights are read exactly once: a non-temporal load keeps them from
-    // displacing the activations in the caches.
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
-
-__device__ __forceinline__ uint64_t load8_stream(const void* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const uint64_t*>(p));
-}
 
 // Registers holding the operands of one chunk of U 128-k blocks.  With x in
 // LDS only the weights are held; otherwise the A operands ride along.
@@ -1377,6 +1311,8 @@ int setup_device(int dev) {
                 for (int w = 4; w <= 8; w += 2)
                     if (!allow_full_lds(pick_split(mt, c, w, od))) return NVFP4_ERR_HIP;
         }
+    int st = nvfp4::gemm_setup();
+    if (st != NVFP4_OK) return st;
     // This device's copy of the fixed scratch array, by its device address.
     void* sp = nullptr;
     if (hipGetSymbolAddress(&sp, HIP_SYMBOL(scratch)) != hipSuccess || sp == nullptr) return NVFP4_ERR_HIP;
@@ -1444,6 +1380,15 @@ int setup_current(int* dev) {
 }
 
 }  // namespace
+
+namespace nvfp4 {
+
+int device_setup() {
+    int dev = 0;
+    return setup_current(&dev);
+}
+
+}  // namespace nvfp4
 
 extern "C" int nvfp4_init(void) {
     int dev = 0;

@@ -246,6 +246,74 @@ int nvfp4_linear_tiled(const void* x_bf16, const uint8_t* w_packed,
 int nvfp4_tile_info(int64_t n, int64_t k, char* buf, int64_t buflen);
 
 /*
+ * Device, asynchronous.  Two products over one x in one launch, like
+ * "Module ops" w4a16_gemv_dual (and its 2- and 3-row forms): y0 = x . W0^T and
+ * y1 = x . W1^T, both weights [N, K] (each with its scales and tensor scale),
+ * both outputs [M, N].  Shape contract, layouts and alignment of
+ * nvfp4_linear; every output has the bits nvfp4_linear gives it.
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, HIP, DEVICE, TILEFILE.
+ */
+int nvfp4_linear_dual(const void* x_bf16, const uint8_t* w_packed0, const uint8_t* scales0,
+                      float tensor_scale0, void* y0, const uint8_t* w_packed1, const uint8_t* scales1,
+                      float tensor_scale1, void* y1, int64_t m, int64_t n, int64_t k, int y_dtype,
+                      void* stream);
+
+/*
+ * Device, asynchronous.  "Module ops" w4a16_gemv_silu_input: the product's
+ * activation is silu(gate) * up, formed per element inside the kernel from
+ * the bf16 gate [M, K] and up [M, K] (16-byte aligned): silu(g) = g / (1 +
+ * exp(-g)) and the product with u in fp32, rounded once to bf16, then the
+ * product of nvfp4_linear with that x (same bits as nvfp4_linear on it).
+ * Needs M * (K + 8) * 2 <= 65536 (the activation is formed in LDS), else
+ * SHAPE.  Errors: NULL, SHAPE, ALIGN, DTYPE, HIP, DEVICE, TILEFILE.
+ */
+int nvfp4_linear_silu_input(const void* gate_bf16, const void* up_bf16, const uint8_t* w_packed,
+                            const uint8_t* scales_e4m3, float tensor_scale, void* y, int64_t m,
+                            int64_t n, int64_t k, int y_dtype, void* stream);
+
+/*
+ * Device, asynchronous.  "Module ops" w4a16_gemv_qg / w4a16_gemv_qkvz: the
+ * weight's rows interleave `parts` parts per group (Q and gate per head; Q,
+ * K, V and Z per group), widths[p] rows of part p in each group of
+ * G = sum(widths) rows, N = groups * G; the output is stored de-interleaved,
+ * all groups' part 0, then all groups' part 1, ...: row r of part p of group
+ * g lands in column groups * (widths[0] + .. + widths[p-1]) + g * widths[p] + r.
+ * widths: host array of `parts` (1..4) positive counts, read during the call.
+ * Values and bits are nvfp4_linear's, only the columns move.
+ * Errors: NULL, SHAPE (also N not a multiple of G), ALIGN, DTYPE, HIP, DEVICE,
+ * TILEFILE.
+ */
+int nvfp4_linear_deinterleave(const void* x_bf16, const uint8_t* w_packed,
+                              const uint8_t* scales_e4m3, float tensor_scale, void* y, int64_t m,
+                              int64_t n, int64_t k, int y_dtype, int parts, const int* widths,
+                              void* stream);
+
+/* One product of a grouped launch (nvfp4_linear_grouped): device pointers
+ * with nvfp4_linear's layouts and alignment; m rows (0 skips the entry). */
+typedef struct nvfp4_group {
+    const void* x;                 /* bf16 [m, K] */
+    const uint8_t* w_packed;       /* [N, K/2] */
+    const uint8_t* scales_e4m3;    /* [N, K/16] */
+    void* y;                       /* [m, N], bf16 or fp32 by the launch's y_dtype */
+    float tensor_scale;
+    int32_t m;                     /* 0 <= m <= max_m */
+} nvfp4_group_t;
+
+/*
+ * Device, asynchronous.  "Module ops" moe_w4a16_grouped_gemm_ptrtable: one
+ * launch over `count` products with the same N and K (e.g. the experts of a
+ * MoE layer, each with the rows routed to it), read from `table`, a device
+ * array of count nvfp4_group_t (8-byte aligned) that must stay valid until the
+ * stream passes the call.  max_m (0..32) bounds every entry's m; rows of an
+ * entry past max_m are not computed.  Each output has the bits nvfp4_linear
+ * gives it.  Entry pointers are not checked on the host (they are in device
+ * memory): they must satisfy nvfp4_linear's contract.
+ * Errors: NULL, SHAPE (also count > 65535), ALIGN, DTYPE, HIP, DEVICE, TILEFILE.
+ */
+int nvfp4_linear_grouped(const nvfp4_group_t* table, int64_t count, int64_t max_m, int64_t n,
+                         int64_t k, int y_dtype, void* stream);
+
+/*
  * Host, pure.  The shape contract of nvfp4_gemm and nvfp4_gemm_expanded:
  * 0 <= M <= 65535 * 128, 1 <= N <= 2^28, 256 <= K <= 2^20 with K % 256 == 0,
  * M * N <= 2^40 ("Module ops" w4a16_tc_rows_shape_ok likewise checks a

@@ -4,6 +4,7 @@
 // every host entry point, including the error paths, and prints "host ok".
 // Usage: host_check [expect_tilefile_status]
 #include <cmath>
+#include <cstddef>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -98,6 +99,10 @@ static void tile_cases() {
 }
 
 int main(int argc, char** argv) {
+    // the grouped launch's record as the Python binding lays it out
+    CHECK(sizeof(nvfp4_group_t) == 40 && offsetof(nvfp4_group_t, w_packed) == 8 &&
+          offsetof(nvfp4_group_t, scales_e4m3) == 16 && offsetof(nvfp4_group_t, y) == 24 &&
+          offsetof(nvfp4_group_t, tensor_scale) == 32 && offsetof(nvfp4_group_t, m) == 36);
     pack_cases();
     contract_cases();
     tile_cases();

@@ -321,3 +321,12 @@ def test_read_probe_validates_before_any_hip_call():
     assert lib.nvfp4_read_probe(a16 + 8, 16, None, 0, sink, None) == nv.ERR_ALIGN
     assert lib.nvfp4_read_probe(a16, 16, None, 0, sink + 2, None) == nv.ERR_ALIGN
     assert lib.nvfp4_read_probe(None, 0, None, 0, sink, None) == nv.OK      # nothing to read
+
+
+def test_group_record_layout_matches_the_header():
+    # tests/host_check.cpp checks the C side (sizeof and offsetof) under the
+    # sanitizers; this is the binding's side of the same layout.
+    d = nv.GROUP_DTYPE
+    assert d.itemsize == 40
+    assert [d.fields[f][1] for f in ("x", "w_packed", "scales_e4m3", "y", "tensor_scale", "m")] == \
+        [0, 8, 16, 24, 32, 36]

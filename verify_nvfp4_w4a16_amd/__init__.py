@@ -29,7 +29,8 @@ EXPORTED = ("nvfp4_pack", "nvfp4_check_scales", "nvfp4_linear_shape_ok", "nvfp4_
             "nvfp4_linear", "nvfp4_linear_tiled", "nvfp4_tile_info", "nvfp4_strerror",
             "nvfp4_timeout_status", "nvfp4_linear_noalloc", "nvfp4_launch_info",
             "nvfp4_read_probe", "nvfp4_gemm_shape_ok", "nvfp4_gemm", "nvfp4_matmul",
-            "nvfp4_dequant_bf16", "nvfp4_gemm_expanded")
+            "nvfp4_dequant_bf16", "nvfp4_gemm_expanded", "nvfp4_linear_dual", "nvfp4_linear_silu_input",
+            "nvfp4_linear_deinterleave", "nvfp4_linear_grouped")
 
 
 class Tile(ctypes.Structure):
@@ -77,6 +78,12 @@ def _load() -> ctypes.CDLL:
     lib.nvfp4_gemm.argtypes = [vp, vp, vp, ctypes.c_float, vp, i64, i64, i64, ctypes.c_int, vp]
     lib.nvfp4_matmul.argtypes = [vp, vp, vp, ctypes.c_float, vp, i64, i64, i64, ctypes.c_int, vp]
     lib.nvfp4_dequant_bf16.argtypes = [vp, vp, ctypes.c_float, ctypes.c_int, vp, i64, i64, vp]
+    lib.nvfp4_linear_dual.argtypes = [vp, vp, vp, ctypes.c_float, vp, vp, vp, ctypes.c_float, vp, i64, i64, i64,
+                                      ctypes.c_int, vp]
+    lib.nvfp4_linear_silu_input.argtypes = [vp, vp, vp, vp, ctypes.c_float, vp, i64, i64, i64, ctypes.c_int, vp]
+    lib.nvfp4_linear_deinterleave.argtypes = [vp, vp, vp, ctypes.c_float, vp, i64, i64, i64, ctypes.c_int,
+                                              ctypes.c_int, ctypes.POINTER(ctypes.c_int), vp]
+    lib.nvfp4_linear_grouped.argtypes = [vp, i64, i64, i64, i64, ctypes.c_int, vp]
     lib.nvfp4_gemm_expanded.argtypes = [vp, vp, ctypes.c_float, vp, i64, i64, i64, ctypes.c_int, vp]
     lib.nvfp4_strerror.argtypes = [ctypes.c_int]
     lib.nvfp4_strerror.restype = ctypes.c_char_p
@@ -209,6 +216,38 @@ def gemm_expanded_raw(x_ptr: int, wbf_ptr: int, tensor_scale: float, y_ptr: int,
     """nvfp4_gemm_expanded on raw device addresses; returns the status."""
     return _lib().nvfp4_gemm_expanded(x_ptr, wbf_ptr, ctypes.c_float(tensor_scale), y_ptr, m, n, k, y_dtype,
                                       stream)
+
+
+def linear_dual_raw(x_ptr, w0_ptr, s0_ptr, t0, y0_ptr, w1_ptr, s1_ptr, t1, y1_ptr, m, n, k, y_dtype,
+                    stream) -> int:
+    """nvfp4_linear_dual on raw device addresses; returns the status."""
+    return _lib().nvfp4_linear_dual(x_ptr, w0_ptr, s0_ptr, ctypes.c_float(t0), y0_ptr, w1_ptr, s1_ptr,
+                                    ctypes.c_float(t1), y1_ptr, m, n, k, y_dtype, stream)
+
+
+def linear_silu_input_raw(gate_ptr, up_ptr, w_ptr, s_ptr, tensor_scale, y_ptr, m, n, k, y_dtype,
+                          stream) -> int:
+    """nvfp4_linear_silu_input on raw device addresses; returns the status."""
+    return _lib().nvfp4_linear_silu_input(gate_ptr, up_ptr, w_ptr, s_ptr, ctypes.c_float(tensor_scale), y_ptr,
+                                          m, n, k, y_dtype, stream)
+
+
+def linear_deinterleave_raw(x_ptr, w_ptr, s_ptr, tensor_scale, y_ptr, m, n, k, y_dtype, widths,
+                            stream) -> int:
+    """nvfp4_linear_deinterleave on raw device addresses; `widths` a list of part widths."""
+    arr = (ctypes.c_int * len(widths))(*widths) if widths is not None else None
+    return _lib().nvfp4_linear_deinterleave(x_ptr, w_ptr, s_ptr, ctypes.c_float(tensor_scale), y_ptr, m, n, k,
+                                            y_dtype, len(widths) if widths is not None else 0, arr, stream)
+
+
+# nvfp4_group_t: four device pointers, the fp32 tensor scale, the int32 row count
+GROUP_DTYPE = np.dtype([("x", "<u8"), ("w_packed", "<u8"), ("scales_e4m3", "<u8"), ("y", "<u8"),
+                        ("tensor_scale", "<f4"), ("m", "<i4")])
+
+
+def linear_grouped_raw(table_ptr, count, max_m, n, k, y_dtype, stream) -> int:
+    """nvfp4_linear_grouped on a device table of GROUP_DTYPE records; returns the status."""
+    return _lib().nvfp4_linear_grouped(table_ptr, count, max_m, n, k, y_dtype, stream)
 
 
 def gemm_shape_ok(m: int, n: int, k: int) -> bool:

@@ -10,4 +10,7 @@ int device_setup();
 // Kernel attributes of the many-row GEMM kernels (their LDS beyond 64 KB).
 int gemm_setup();
 
+// Kernel attributes of the fused and grouped kernels.
+int fused_setup();
+
 }  // namespace nvfp4

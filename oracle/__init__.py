@@ -28,8 +28,10 @@ from .linear import (unpack_codes, dequant, linear_ref, bound, accept,
 from .quant import quantize_ref, e4m3_round, e2m1_round
 from .expand import round_to_bf16, dequant_bf16
 from .fused import silu, silu_mul_bf16, deinterleave_columns, deinterleave
+from .fp8 import dequant_fp8, linear_fp8_ref, bound_fp8, quantize_fp8_ref
 
 __all__ = ["E2M1", "E4M3", "e2m1_value", "e4m3_value", "unpack_codes",
            "dequant", "linear_ref", "bound", "accept", "max_violation", "tolerance",
            "bf16_bits_to_f64", "quantize_ref", "e4m3_round", "e2m1_round", "round_to_bf16",
-           "dequant_bf16", "silu", "silu_mul_bf16", "deinterleave_columns", "deinterleave"]
+           "dequant_bf16", "silu", "silu_mul_bf16", "deinterleave_columns", "deinterleave",
+           "dequant_fp8", "linear_fp8_ref", "bound_fp8", "quantize_fp8_ref"]

@@ -314,6 +314,47 @@ int nvfp4_linear_grouped(const nvfp4_group_t* table, int64_t count, int64_t max_
                          int64_t k, int y_dtype, void* stream);
 
 /*
+ * FP8 block-scaled weights (W8A16), the pages' second weight format ("10
+ * Kernels" 10.3; "Module ops" w8a16_gemm / w8a16_tc_rows): a weight [N, K] of
+ * e4m3 codes (OCP "fn": bias 7, max 448, NaN = 0x7F/0xFF) and one fp32 scale
+ * per 128 x 128 block, [N/128, K/128] row-major:
+ *   y[m, n] = sum over 128-k blocks b of S[n/128, b] * sum_{k in b} x[m, k] * e4m3(W[n, k]).
+ */
+
+/*
+ * Host.  Quantise a row-major fp32 w[N, K] (N, K multiples of 128) into e4m3
+ * codes w_e4m3[N * K] and block scales block_scales[(N/128) * (K/128)], host
+ * buffers owned by the caller.  Rule (IEEE binary64, in this order): per block
+ * S = fp32(max|w| / 448), 1 when that is 0; code = e4m3 of w / S rounded to
+ * nearest, ties to even, saturating at 448, sign kept except for a zero code.
+ * The layout is the one "10 Kernels" 10.3 reads as stored (and 448 is
+ * "Module ops" E4M3_MAX); the pages' checkpoints come quantised, so the rule
+ * for choosing S is this library's reading.  Errors: NULL, SHAPE, NONFINITE.
+ */
+int fp8_w8a16_pack(const float* w, int64_t n, int64_t k, uint8_t* w_e4m3, float* block_scales);
+
+/*
+ * Host, pure.  The shape contract of fp8_w8a16_linear, like "Module ops"
+ * w8a16_tc_rows_shape_ok: 0 <= M <= 32, N and K positive multiples of 128,
+ * N <= 2^28, K <= 2^20.  Returns NVFP4_OK or NVFP4_ERR_SHAPE.
+ */
+int fp8_w8a16_shape_ok(int64_t m, int64_t n, int64_t k);
+
+/*
+ * Device, asynchronous on `stream`.  The W8A16 product above at 1..32 rows:
+ * x bf16 [M, K] (16-byte aligned), w_e4m3 [N, K] (16-byte aligned),
+ * block_scales fp32 [N/128, K/128] (4-byte aligned), y [M, N] bf16 or fp32,
+ * all device memory owned by the caller.  Each 128-k block's partial sum
+ * starts from zero and joins the row's chain as one fused multiply-add by its
+ * scale, blocks in increasing k; K is cut into segments (a function of N and
+ * K) added in a fixed order, so a row's bits do not depend on M ("10 Kernels"
+ * 10.1).  M == 0 launches nothing; no allocation, no host sync.
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, HIP, DEVICE, TILEFILE.
+ */
+int fp8_w8a16_linear(const void* x_bf16, const uint8_t* w_e4m3, const float* block_scales, void* y,
+                     int64_t m, int64_t n, int64_t k, int y_dtype, void* stream);
+
+/*
  * Host, pure.  The shape contract of nvfp4_gemm and nvfp4_gemm_expanded:
  * 0 <= M <= 65535 * 128, 1 <= N <= 2^28, 256 <= K <= 2^20 with K % 256 == 0,
  * M * N <= 2^40 ("Module ops" w4a16_tc_rows_shape_ok likewise checks a

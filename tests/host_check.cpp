@@ -54,6 +54,19 @@ static void pack_cases() {
     CHECK(nvfp4_pack(nullptr, 64, 32, p.data(), sc.data(), &t) == NVFP4_ERR_NULL);
     CHECK(nvfp4_pack(z.data(), 0, 32, p.data(), sc.data(), &t) == NVFP4_ERR_SHAPE);
     CHECK(nvfp4_pack(z.data(), 4, 24, p.data(), sc.data(), &t) == NVFP4_ERR_SHAPE);
+    // FP8 block-scaled packer
+    {
+        std::vector<float> w8(256 * 384);
+        for (auto& v : w8) v = nd(gen);
+        std::vector<uint8_t> c8(w8.size());
+        std::vector<float> s8(2 * 3);
+        CHECK(fp8_w8a16_pack(w8.data(), 256, 384, c8.data(), s8.data()) == NVFP4_OK);
+        CHECK(fp8_w8a16_pack(w8.data(), 100, 384, c8.data(), s8.data()) == NVFP4_ERR_SHAPE);
+        CHECK(fp8_w8a16_pack(nullptr, 256, 384, c8.data(), s8.data()) == NVFP4_ERR_NULL);
+        w8[77] = std::numeric_limits<float>::infinity();
+        CHECK(fp8_w8a16_pack(w8.data(), 256, 384, c8.data(), s8.data()) == NVFP4_ERR_NONFINITE);
+        CHECK(fp8_w8a16_shape_ok(32, 128, 128) == NVFP4_OK && fp8_w8a16_shape_ok(1, 128, 64) == NVFP4_ERR_SHAPE);
+    }
     // scale check
     std::vector<uint8_t> s2(32, 0x38);
     CHECK(nvfp4_check_scales(s2.data(), 2, 256) == NVFP4_OK);
@@ -75,6 +88,8 @@ static void contract_cases() {
     CHECK(nvfp4_linear_shape_ok(1, 1, 128) == NVFP4_ERR_SHAPE);
     CHECK(nvfp4_linear_shape_ok(1, 1, 384) == NVFP4_ERR_SHAPE);
     CHECK(nvfp4_linear_shape_ok(1, 1, (int64_t(1) << 20) + 256) == NVFP4_ERR_SHAPE);
+    CHECK(nvfp4_gemm_shape_ok(4096, 8192, 4096) == NVFP4_OK && nvfp4_gemm_shape_ok(65535 * 128 + 1, 1, 256) != 0);
+    CHECK(nvfp4_gemm_shape_ok(1, 1, 100) == NVFP4_ERR_SHAPE && nvfp4_gemm_shape_ok(-1, 1, 256) == NVFP4_ERR_SHAPE);
     for (int st = 1; st >= -40; --st) CHECK(nvfp4_strerror(st) != nullptr);
 }
 

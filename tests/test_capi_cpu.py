@@ -16,7 +16,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "nv
 
 def _declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(nvfp4_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+((?:nvfp4|fp8)_\w+)\s*\(", text, re.M)))
 
 
 PAGES = ('"10 Kernels"', '"CUDA Kernel Engineering"', '"Module ops"')
@@ -26,7 +26,7 @@ def _declaration_comments():
     """{function: the comment block right above its declaration}."""
     text = open(HEADER).read()
     out = {}
-    for m in re.finditer(r"/\*(?:(?!\*/).)*\*/\s*(?:(?:int|const char\*)\s+)(nvfp4_\w+)\s*\(", text, re.S):
+    for m in re.finditer(r"/\*(?:(?!\*/).)*\*/\s*(?:(?:int|const char\*)\s+)((?:nvfp4|fp8)_\w+)\s*\(", text, re.S):
         out[m.group(1)] = m.group(0)
     return out
 
@@ -330,3 +330,23 @@ def test_group_record_layout_matches_the_header():
     assert d.itemsize == 40
     assert [d.fields[f][1] for f in ("x", "w_packed", "scales_e4m3", "y", "tensor_scale", "m")] == \
         [0, 8, 16, 24, 32, 36]
+
+
+def test_fp8_pack_matches_oracle():
+    g = workload.rng(8)
+    for n, k in [(128, 128), (256, 384), (384, 1024)]:
+        w = workload.weights_f32(n, k, n + k)
+        w[:128, :128] *= np.float32(1e-30)                  # a block of tiny values
+        w[128:256, 128:256] = 0.0 if n > 128 and k > 128 else w[128:256, 128:256]
+        w[5, 7] = np.float32(3.0e4)                           # a dominant value in one block
+        codes, scales = nv.fp8_pack(w)
+        c2, s2 = oracle.quantize_fp8_ref(w)
+        assert np.array_equal(scales, s2) and np.array_equal(codes, c2), (n, k)
+    bad = np.zeros((128, 128), np.float32)
+    bad[3, 3] = np.inf
+    with pytest.raises(nv.Nvfp4Error):
+        nv.fp8_pack(bad)
+    with pytest.raises(nv.Nvfp4Error):
+        nv.fp8_pack(np.zeros((100, 128), np.float32))
+    assert nv.fp8_shape_ok(32, 128, 128) and not nv.fp8_shape_ok(33, 128, 128)
+    assert not nv.fp8_shape_ok(1, 100, 128) and not nv.fp8_shape_ok(1, 128, 64)

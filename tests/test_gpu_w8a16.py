@@ -1,0 +1,86 @@
+"""The FP8 block-scaled product (W8A16) on the GPU (gpu): parity with the fp64
+oracle, exact decode of every e4m3 code, and each row's bits independent of M
+and of the other rows."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import verify_nvfp4_w4a16_amd as nv
+import workload
+from tests._gpu import DEV, bits, to_f64, upload_bits, upload_u8
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(xd, wd, sd, m, n, k, out_dtype=torch.bfloat16):
+    y = torch.empty((m, n), dtype=out_dtype, device=DEV)
+    od = nv.OUT_F32 if out_dtype == torch.float32 else nv.OUT_BF16
+    st = nv.fp8_linear_raw(xd.data_ptr(), wd.data_ptr(), sd.data_ptr(), y.data_ptr(), m, n, k, od,
+                           torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == nv.OK, st
+    return y
+
+
+def _parity(y, x, codes, scales, cols=None, label=""):
+    y64 = to_f64(y)
+    if cols is not None:
+        y64 = y64[:, cols]
+    ref = oracle.linear_fp8_ref(x, codes, scales, cols)
+    bnd = oracle.bound_fp8(x, codes, scales, cols)
+    out = "bf16" if y.dtype == torch.bfloat16 else "f32"
+    viol = oracle.max_violation(y64, ref, bnd, out)
+    print(f"[parity] {label} {out} M={x.shape[0]} max err/tol = {viol:.3g}", flush=True)
+    assert viol <= 1.0, label
+
+
+def test_w8a16_parity_and_row_invariance():
+    for n, k in [(4096, 4096), (8192, 4096), (4096, 12288), (384, 1152)]:
+        codes, scales = nv.fp8_pack(workload.weights_f32(n, k, 100 + n // 128))
+        wd, sd = upload_u8(codes), torch.from_numpy(scales).to(DEV)
+        x = workload.activations_bf16(32, k, 200 + k, outliers=True)
+        xd = upload_bits(x)
+        full = _run(xd, wd, sd, 32, n, k)
+        cols = np.unique(np.concatenate([np.arange(32), np.arange(n - 32, n),
+                                         workload.rng(n).integers(0, n, 256)]))
+        _parity(full, x, codes, scales, cols, f"w8a16 {n}x{k} M=32")
+        ref = bits(full).clone()
+        for m in (1, 2, 5, 7, 8, 16, 17, 31):
+            y = _run(xd, wd, sd, m, n, k)
+            assert torch.equal(bits(y), ref[:m]), (n, k, m)     # x in LDS (small M) or read per chunk
+        alone = _run(upload_bits(x[9:10]), wd, sd, 1, n, k)
+        assert torch.equal(bits(alone), ref[9:10])
+        _parity(_run(xd, wd, sd, 3, n, k, torch.float32), x[:3], codes, scales, cols, f"w8a16 {n}x{k} fp32")
+
+
+def test_w8a16_every_code_decoded_exactly():
+    # One-hot x picks single weights: y[m, n] = e4m3(code) * S exactly, for
+    # all 256 codes (0x7F and 0xFF give NaN) at two scales.
+    n, k = 256, 256
+    codes = np.zeros((n, k), np.uint8)
+    codes[:, 3] = np.arange(256, dtype=np.uint8)
+    scales = np.array([[2.0 ** -3, 1.0], [3.0, 0.5]], np.float32)
+    x = np.zeros((1, k), np.uint16)
+    x[0, 3] = 0x3F80
+    y = _run(upload_bits(x), upload_u8(codes), torch.from_numpy(scales).to(DEV), 1, n, k, torch.float32)
+    got = y.cpu().numpy()[0].astype(np.float64)
+    want = oracle.E4M3[np.arange(256)] * np.where(np.arange(256) < 128, 2.0 ** -3, 3.0)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+
+
+def test_w8a16_errors():
+    codes, scales = nv.fp8_pack(workload.weights_f32(128, 256, 5))
+    wd, sd = upload_u8(codes), torch.from_numpy(scales).to(DEV)
+    x = upload_bits(workload.activations_bf16(2, 256, 6))
+    y = torch.empty((2, 128), dtype=torch.bfloat16, device=DEV)
+    s = torch.cuda.current_stream().cuda_stream
+    assert nv.fp8_linear_raw(x.data_ptr(), wd.data_ptr(), sd.data_ptr(), y.data_ptr(), 33, 128, 256, 0, s) == \
+        nv.ERR_SHAPE
+    assert nv.fp8_linear_raw(x.data_ptr(), wd.data_ptr(), sd.data_ptr(), y.data_ptr(), 2, 100, 256, 0, s) == \
+        nv.ERR_SHAPE
+    assert nv.fp8_linear_raw(x.data_ptr() + 8, wd.data_ptr(), sd.data_ptr(), y.data_ptr(), 2, 128, 256, 0, s) == \
+        nv.ERR_ALIGN
+    assert nv.fp8_linear_raw(x.data_ptr(), wd.data_ptr(), sd.data_ptr(), y.data_ptr(), 0, 128, 256, 0, s) == nv.OK

@@ -30,7 +30,8 @@ EXPORTED = ("nvfp4_pack", "nvfp4_check_scales", "nvfp4_linear_shape_ok", "nvfp4_
             "nvfp4_timeout_status", "nvfp4_linear_noalloc", "nvfp4_launch_info",
             "nvfp4_read_probe", "nvfp4_gemm_shape_ok", "nvfp4_gemm", "nvfp4_matmul",
             "nvfp4_dequant_bf16", "nvfp4_gemm_expanded", "nvfp4_linear_dual", "nvfp4_linear_silu_input",
-            "nvfp4_linear_deinterleave", "nvfp4_linear_grouped")
+            "nvfp4_linear_deinterleave", "nvfp4_linear_grouped", "fp8_w8a16_pack", "fp8_w8a16_shape_ok",
+            "fp8_w8a16_linear")
 
 
 class Tile(ctypes.Structure):
@@ -84,6 +85,9 @@ def _load() -> ctypes.CDLL:
     lib.nvfp4_linear_deinterleave.argtypes = [vp, vp, vp, ctypes.c_float, vp, i64, i64, i64, ctypes.c_int,
                                               ctypes.c_int, ctypes.POINTER(ctypes.c_int), vp]
     lib.nvfp4_linear_grouped.argtypes = [vp, i64, i64, i64, i64, ctypes.c_int, vp]
+    lib.fp8_w8a16_pack.argtypes = [vp, i64, i64, vp, vp]
+    lib.fp8_w8a16_shape_ok.argtypes = [i64, i64, i64]
+    lib.fp8_w8a16_linear.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
     lib.nvfp4_gemm_expanded.argtypes = [vp, vp, ctypes.c_float, vp, i64, i64, i64, ctypes.c_int, vp]
     lib.nvfp4_strerror.argtypes = [ctypes.c_int]
     lib.nvfp4_strerror.restype = ctypes.c_char_p
@@ -248,6 +252,27 @@ GROUP_DTYPE = np.dtype([("x", "<u8"), ("w_packed", "<u8"), ("scales_e4m3", "<u8"
 def linear_grouped_raw(table_ptr, count, max_m, n, k, y_dtype, stream) -> int:
     """nvfp4_linear_grouped on a device table of GROUP_DTYPE records; returns the status."""
     return _lib().nvfp4_linear_grouped(table_ptr, count, max_m, n, k, y_dtype, stream)
+
+
+def fp8_pack(w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """fp32 W[N, K] -> (e4m3 codes [N, K] uint8, fp32 block scales [N/128, K/128])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    if w.ndim != 2:
+        raise ValueError("w must be 2-D [N, K]")
+    n, k = w.shape
+    codes = np.empty((n, k), np.uint8)
+    scales = np.empty((max(n // 128, 0), max(k // 128, 0)), np.float32)
+    _check(_lib().fp8_w8a16_pack(w.ctypes.data, n, k, codes.ctypes.data, scales.ctypes.data), "fp8_w8a16_pack")
+    return codes, scales
+
+
+def fp8_shape_ok(m: int, n: int, k: int) -> bool:
+    return _lib().fp8_w8a16_shape_ok(m, n, k) == OK
+
+
+def fp8_linear_raw(x_ptr, w_ptr, s_ptr, y_ptr, m, n, k, y_dtype, stream) -> int:
+    """fp8_w8a16_linear on raw device addresses; returns the status."""
+    return _lib().fp8_w8a16_linear(x_ptr, w_ptr, s_ptr, y_ptr, m, n, k, y_dtype, stream)
 
 
 def gemm_shape_ok(m: int, n: int, k: int) -> bool:

@@ -22,7 +22,7 @@ ARCH = "gfx950"
 
 HOST_SOURCES = ["host/pack.cpp", "host/tiles.cpp"]
 HIP_SOURCES = ["kernels/nvfp4_linear.hip", "kernels/nvfp4_gemm.hip", "kernels/nvfp4_fused.hip",
-               "kernels/read_probe.hip"]
+               "kernels/w8a16.hip", "kernels/read_probe.hip"]
 
 # -ffp-contract=off keeps the packer's float64 steps unfused (bit-exact rule).
 HOST_FLAGS = ["-std=c++17", "-O3", "-fPIC", "-ffp-contract=off", "-Wall", "-Wextra",

@@ -159,6 +159,37 @@ extern "C" int nvfp4_pack(const float* w, int64_t n, int64_t k, uint8_t* w_packe
     return NVFP4_OK;
 }
 
+extern "C" int fp8_w8a16_pack(const float* w, int64_t n, int64_t k, uint8_t* w_e4m3, float* block_scales) {
+    constexpr int64_t kB = 128;
+    if (!w || !w_e4m3 || !block_scales) return NVFP4_ERR_NULL;
+    if (n < kB || k < kB || n % kB || k % kB) return NVFP4_ERR_SHAPE;
+    for (int64_t i = 0; i < n * k; ++i)
+        if (!std::isfinite(w[i])) return NVFP4_ERR_NONFINITE;
+    const int64_t kb = k / kB;
+    const int workers = worker_count(n / kB, kB * k);
+    const int64_t rows_per = (n / kB + workers - 1) / workers;     // 128-row block rows per thread
+    run_parallel(workers, [&](int t) {
+        for (int64_t br = t * rows_per; br < std::min(n / kB, (t + 1) * rows_per); ++br)
+            for (int64_t bc = 0; bc < kb; ++bc) {
+                double amax = 0.0;
+                for (int64_t r = 0; r < kB; ++r)
+                    for (int64_t c = 0; c < kB; ++c)
+                        amax = std::max(amax, std::fabs(double(w[(br * kB + r) * k + bc * kB + c])));
+                float s = static_cast<float>(amax / kE4m3Max);
+                if (amax == 0.0 || s == 0.0f) s = 1.0f;
+                block_scales[br * kb + bc] = s;
+                for (int64_t r = 0; r < kB; ++r)
+                    for (int64_t c = 0; c < kB; ++c) {
+                        const int64_t i = (br * kB + r) * k + bc * kB + c;
+                        const double v = double(w[i]) / double(s);
+                        const uint8_t mag = e4m3_encode(std::fabs(v));
+                        w_e4m3[i] = static_cast<uint8_t>(mag | ((v < 0.0 && mag != 0) ? 0x80 : 0));
+                    }
+            }
+    });
+    return NVFP4_OK;
+}
+
 extern "C" int nvfp4_check_scales(const uint8_t* scales_e4m3, int64_t n, int64_t k) {
     if (!scales_e4m3) return NVFP4_ERR_NULL;
     if (n < 1 || k < kGroup || k % kGroup) return NVFP4_ERR_SHAPE;
@@ -174,6 +205,23 @@ extern "C" int nvfp4_linear_shape_ok(int64_t m, int64_t n, int64_t k) {
     if (m < 0 || m > NVFP4_MAX_M) return NVFP4_ERR_SHAPE;
     if (n < 1 || n > (int64_t(1) << 28)) return NVFP4_ERR_SHAPE;
     if (k < NVFP4_K_MULTIPLE || k > (int64_t(1) << 20) || k % NVFP4_K_MULTIPLE) return NVFP4_ERR_SHAPE;
+    return NVFP4_OK;
+}
+
+extern "C" int nvfp4_gemm_shape_ok(int64_t m, int64_t n, int64_t k) {
+    // rows: at most 65535 workgroup rows (the grid's y limit) of 128
+    if (m < 0 || m > int64_t(65535) * 128) return NVFP4_ERR_SHAPE;
+    if (n < 1 || n > (int64_t(1) << 28)) return NVFP4_ERR_SHAPE;
+    if (k < NVFP4_K_MULTIPLE || k > (int64_t(1) << 20) || k % NVFP4_K_MULTIPLE) return NVFP4_ERR_SHAPE;
+    if (m * n > (int64_t(1) << 40)) return NVFP4_ERR_SHAPE;
+    return NVFP4_OK;
+}
+
+extern "C" int fp8_w8a16_shape_ok(int64_t m, int64_t n, int64_t k) {
+    constexpr int64_t kB = 128;
+    if (m < 0 || m > NVFP4_MAX_M) return NVFP4_ERR_SHAPE;
+    if (n < kB || n > (int64_t(1) << 28) || n % kB) return NVFP4_ERR_SHAPE;
+    if (k < kB || k > (int64_t(1) << 20) || k % kB) return NVFP4_ERR_SHAPE;
     return NVFP4_OK;
 }
 

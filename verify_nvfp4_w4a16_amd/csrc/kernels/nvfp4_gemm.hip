@@ -45,7 +45,6 @@ constexpr int kThreads = 256;
 constexpr int kPitch = kBlockK + 8;     // LDS row pitch of an x block, bf16 elements
 constexpr int kXVec = kRows * kBlockK / 8 / kThreads;   // 16-byte x pieces per thread per block
 constexpr size_t kGemmLds = 2 * size_t(kRows) * kPitch * sizeof(uint16_t);
-constexpr int kMaxGridY = 65535;
 
 struct GemmArgs {
     const uint16_t* x;      // bf16 [M, K]
@@ -318,14 +317,6 @@ int gemm_setup() {
 }
 
 }  // namespace nvfp4
-
-extern "C" int nvfp4_gemm_shape_ok(int64_t m, int64_t n, int64_t k) {
-    if (m < 0 || m > int64_t(kMaxGridY) * kRows) return NVFP4_ERR_SHAPE;
-    if (n < 1 || n > (int64_t(1) << 28)) return NVFP4_ERR_SHAPE;
-    if (k < NVFP4_K_MULTIPLE || k > (int64_t(1) << 20) || k % NVFP4_K_MULTIPLE) return NVFP4_ERR_SHAPE;
-    if (m * n > (int64_t(1) << 40)) return NVFP4_ERR_SHAPE;
-    return NVFP4_OK;
-}
 
 extern "C" int nvfp4_gemm(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4m3,
                           float tensor_scale, void* y, int64_t m, int64_t n, int64_t k, int y_dtype, void* stream) {

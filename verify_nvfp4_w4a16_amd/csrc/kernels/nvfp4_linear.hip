@@ -1313,6 +1313,7 @@ int setup_device(int dev) {
         }
     int st = nvfp4::gemm_setup();
     if (st == NVFP4_OK) st = nvfp4::fused_setup();
+    if (st == NVFP4_OK) st = nvfp4::w8a16_setup();
     if (st != NVFP4_OK) return st;
     // This device's copy of the fixed scratch array, by its device address.
     void* sp = nullptr;

@@ -13,4 +13,7 @@ int gemm_setup();
 // Kernel attributes of the fused and grouped kernels.
 int fused_setup();
 
+// Kernel attributes of the FP8 (W8A16) kernels.
+int w8a16_setup();
+
 }  // namespace nvfp4

@@ -1,0 +1,266 @@
+// FP8 block-scaled weight-only product (W8A16) for 1..32 rows:
+//   y[m, n] = sum over 128-k blocks b of S[n / 128, b] * (sum_{k in b} x[m, k] * e4m3(B[n, k]))
+// "10 Kernels" 10.3: the checkpoint's block-scaled FP8 read as stored, a tile
+// 128 wide along K so that each step covers one scale block, the scale one
+// number applied to the fp32 sum; "Module ops" w8a16_gemm / w8a16_tc_rows
+// (weight [N, K] e4m3, block scale [N/128, K/128] fp32, N and K multiples of
+// 128).
+//
+// Same machine layout as the NVFP4 kernels' register path: a workgroup per
+// 16 output columns, its wavefronts one K segment each, weights loaded into
+// registers (two 16-byte loads per lane per 128-k block, 64 contiguous bytes
+// of a row per load instruction) and converted exactly to the bf16 B operand
+// of v_mfma_f32_16x16x32_bf16 by v_cvt_scalef32_pk_bf16_fp8 at scale 1 (e4m3
+// has 4 significant bits).  Each block's four MFMAs start from zero; the block
+// sum joins the segment's chain as fma(S, block, chain), blocks in increasing
+// k; the segment chains are added in the two-level order of the (N, K) tile,
+// so a row's bits do not depend on M or on the other rows ("10 Kernels" 10.1).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "nvfp4_w4a16.h"
+#include "nvfp4_common.h"
+#include "setup.h"
+#include "../host/tiles.h"
+
+namespace {
+
+constexpr int kFp8Block = 128;
+
+struct W8Args {
+    const uint16_t* x;     // bf16 [M, K]
+    const uint8_t* w;      // e4m3 [N, K]
+    const float* s;        // fp32 [N/128, K/128]
+    void* y;               // [M, N]
+    int m, n, k;
+    int k_per_wave;        // segment length, a multiple of 128
+    int group;             // segments per segment group
+};
+
+// Eight e4m3 codes (two dwords) as the bf16 B operand, exactly.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+    return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+template <int MT, bool XLDS>
+struct W8Chunk {
+    u32x4 w[2];            // bytes 16 kq .. +15 and 64 + 16 kq .. +15 of the lane's row in the block
+    float s;               // the block's scale for the lane's rows
+    u32x4 x[XLDS ? 1 : MT][XLDS ? 1 : 4];
+};
+
+// MFMA s of a block takes, in lane quarter kq, k = 64 (s / 2) + 16 kq + 8 (s % 2) .. + 7
+// of the block, for the weight and the activation alike.
+__device__ __forceinline__ int slot_k(int s, int kq) { return 64 * (s / 2) + 16 * kq + 8 * (s % 2); }
+
+template <int MT, bool XLDS, bool OUT_F32>
+__global__ void __launch_bounds__(512)
+fp8_w8a16_kernel(W8Args a) {
+    extern __shared__ __align__(16) uint16_t lds[];
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    const int waves = blockDim.x / kWave;
+    const int col_lane = lane % 16;
+    const int kq = lane / 16;
+    const int col_base = blockIdx.x * 16;
+    const int n = col_base + col_lane;          // N is a multiple of 128: no column past N
+    const int pitch = a.k + 8;
+    const int kblocks = a.k / kFp8Block;
+    const uint8_t* wrow = a.w + (int64_t)n * a.k;
+    const float* srow = a.s + (int64_t)(col_base / kFp8Block) * kblocks;
+    int xr[MT];
+    const uint16_t* xrow[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        xr[t] = min(16 * t + col_lane, a.m - 1);
+        xrow[t] = a.x + (int64_t)xr[t] * a.k;
+    }
+    if constexpr (XLDS) {
+        const int vec_per_row = a.k / 8;
+        const int total = a.m * vec_per_row;
+        for (int v = threadIdx.x; v < total; v += blockDim.x) {
+            const int r = v / vec_per_row, c = v % vec_per_row;
+            *reinterpret_cast<u32x4*>(lds + r * pitch + 8 * c) = load16(a.x + (int64_t)r * a.k + 8 * c);
+        }
+        __syncthreads();
+    }
+
+    auto load = [&](W8Chunk<MT, XLDS>& ch, int kb) {
+        ch.w[0] = load16_stream(wrow + kb + 16 * kq);
+        ch.w[1] = load16_stream(wrow + kb + 64 + 16 * kq);
+        ch.s = srow[kb / kFp8Block];
+        if constexpr (!XLDS) {
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) ch.x[t][s] = load16(xrow[t] + kb + slot_k(s, kq));
+        }
+    };
+
+    f32x4 acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const W8Chunk<MT, XLDS>& ch, int kb) {
+        f32x4 blk[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) blk[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const u32x4 p = ch.w[s / 2];
+            const bf16x8 b = fp8x8_to_bf16(p[2 * (s % 2)], p[2 * (s % 2) + 1]);
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                u32x4 xa;
+                if constexpr (XLDS)
+                    xa = *reinterpret_cast<const u32x4*>(lds + xr[t] * pitch + kb + slot_k(s, kq));
+                else
+                    xa = ch.x[t][s];
+                blk[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), b, blk[t], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[t][j] = __builtin_fmaf(ch.s, blk[t][j], acc[t][j]);
+    };
+
+    const int k0 = wave * a.k_per_wave;
+    const int nchunks = a.k_per_wave / kFp8Block;
+    W8Chunk<MT, XLDS> A, B;
+    load(A, k0);
+    int i = 0;
+    for (; i + 2 <= nchunks; i += 2) {
+        load(B, k0 + (i + 1) * kFp8Block);
+        compute(A, k0 + i * kFp8Block);
+        if (i + 2 < nchunks) load(A, k0 + (i + 2) * kFp8Block);
+        compute(B, k0 + (i + 1) * kFp8Block);
+    }
+    if (i < nchunks) compute(A, k0 + i * kFp8Block);
+
+    // segment chains in the two-level order, through the LDS that held x
+    if (waves > 1) {
+        f32x4 tot[MT];
+        float* partials = reinterpret_cast<float*>(lds);
+        __syncthreads();
+        if (wave != 0) {
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) partials[((wave * MT + t) * 4 + j) * kWave + lane] = acc[t][j];
+        }
+        __syncthreads();
+        if (wave != 0) return;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) tot[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int w2 = 1; w2 < waves; ++w2) {
+            const bool starts = w2 % a.group == 0;
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const float* p = partials + (w2 * MT + t) * 4 * kWave + lane;
+                const f32x4 v = f32x4{p[0], p[kWave], p[2 * kWave], p[3 * kWave]};
+                const f32x4 closed = w2 == a.group ? acc[t] : tot[t] + acc[t];
+                tot[t] = starts ? closed : tot[t];
+                acc[t] = starts ? v : acc[t] + v;
+            }
+        }
+        if (a.group < waves) {
+#pragma unroll
+            for (int t = 0; t < MT; ++t) acc[t] = tot[t] + acc[t];
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int m = 16 * t + 4 * kq + j;
+            if (m < a.m) {
+                if (OUT_F32)
+                    static_cast<float*>(a.y)[(int64_t)m * a.n + n] = acc[t][j];
+                else
+                    static_cast<uint16_t*>(a.y)[(int64_t)m * a.n + n] = f32_to_bf16_rne(acc[t][j]);
+            }
+        }
+}
+
+using W8Fn = void (*)(W8Args);
+
+W8Fn pick_w8(int mt, bool xlds, int y_dtype) {
+    const bool f = y_dtype == NVFP4_OUT_F32;
+    if (mt == 1) {
+        if (xlds) return f ? fp8_w8a16_kernel<1, true, true> : fp8_w8a16_kernel<1, true, false>;
+        return f ? fp8_w8a16_kernel<1, false, true> : fp8_w8a16_kernel<1, false, false>;
+    }
+    if (xlds) return f ? fp8_w8a16_kernel<2, true, true> : fp8_w8a16_kernel<2, true, false>;
+    return f ? fp8_w8a16_kernel<2, false, true> : fp8_w8a16_kernel<2, false, false>;
+}
+
+constexpr size_t kXLdsMax = 64 * 1024;
+
+// Segments of the FP8 tile: K cut into the most of 8, 4, 2, 1 equal parts of
+// whole 128-k blocks; groups of them by the NVFP4 table's default rule.  A
+// function of (N, K) only.
+void fp8_tile(int64_t n, int64_t k, int* waves, int* group) {
+    const int64_t blocks = k / kFp8Block;
+    int w = 8;
+    while (w > 1 && blocks % w != 0) w /= 2;
+    *waves = w;
+    *group = w / nvfp4::default_split(n, w);
+}
+
+}  // namespace
+
+namespace nvfp4 {
+
+int w8a16_setup() {
+    for (int mt = 1; mt <= 2; ++mt)
+        for (int xl = 0; xl <= 1; ++xl)
+            for (int od = 0; od <= 1; ++od)
+                if (hipFuncSetAttribute(reinterpret_cast<const void*>(pick_w8(mt, xl != 0, od)),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        static_cast<int>(kXLdsMax)) != hipSuccess)
+                    return NVFP4_ERR_HIP;
+    return NVFP4_OK;
+}
+
+}  // namespace nvfp4
+
+extern "C" int fp8_w8a16_linear(const void* x_bf16, const uint8_t* w_e4m3, const float* block_scales, void* y,
+                                int64_t m, int64_t n, int64_t k, int y_dtype, void* stream) {
+    int st = fp8_w8a16_shape_ok(m, n, k);
+    if (st != NVFP4_OK) return st;
+    if (y_dtype != NVFP4_OUT_BF16 && y_dtype != NVFP4_OUT_F32) return NVFP4_ERR_DTYPE;
+    if (m == 0) return NVFP4_OK;
+    if (!x_bf16 || !w_e4m3 || !block_scales || !y) return NVFP4_ERR_NULL;
+    auto misaligned = [](const void* p, uintptr_t al) { return (reinterpret_cast<uintptr_t>(p) & (al - 1)) != 0; };
+    if (misaligned(x_bf16, 16) || misaligned(w_e4m3, 16) || misaligned(block_scales, 4) ||
+        misaligned(y, y_dtype == NVFP4_OUT_F32 ? 4 : 2))
+        return NVFP4_ERR_ALIGN;
+    st = nvfp4::device_setup();
+    if (st != NVFP4_OK) return st;
+    W8Args a;
+    a.x = static_cast<const uint16_t*>(x_bf16);
+    a.w = w_e4m3;
+    a.s = block_scales;
+    a.y = y;
+    a.m = static_cast<int>(m);
+    a.n = static_cast<int>(n);
+    a.k = static_cast<int>(k);
+    int waves = 1, group = 1;
+    fp8_tile(n, k, &waves, &group);
+    a.k_per_wave = static_cast<int>(k / waves);
+    a.group = group;
+    const int mt = m <= 16 ? 1 : 2;
+    const size_t x_bytes = size_t(m) * (k + 8) * sizeof(uint16_t);
+    const bool xlds = x_bytes <= kXLdsMax;
+    const size_t part_bytes = waves > 1 ? size_t(waves) * mt * 4 * kWave * sizeof(float) : 0;
+    const size_t lds = xlds && x_bytes > part_bytes ? x_bytes : part_bytes;
+    hipLaunchKernelGGL(pick_w8(mt, xlds, y_dtype), dim3(static_cast<unsigned>(n / 16)),
+                       dim3(static_cast<unsigned>(kWave * waves)), lds, static_cast<hipStream_t>(stream), a);
+    return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}

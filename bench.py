@@ -46,7 +46,7 @@ CPU_BASELINE_MAX_S = 30.0           # ... and stops starting new ones past this
 CPU_BASELINE_LAYERS = 8             # layers whose packed bytes stay on the host for it
 COLD_BYTES = 512 << 20              # weight copies rotated per timed launch sequence
 KERNEL_SOURCES = [os.path.join(ROOT, "verify_nvfp4_w4a16_amd", "csrc", "kernels", f)
-                  for f in ("nvfp4_linear.hip",)]
+                  for f in ("nvfp4_common.h", "nvfp4_linear.hip", "nvfp4_gemm.hip", "nvfp4_fused.hip", "w8a16.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_round.json")
 
 
@@ -313,6 +313,149 @@ def config_timings(torch, dev, stream) -> dict:
     return out
 
 
+def next_rows(torch, dev, stream) -> dict:
+    """The other regimes and forms of the product, timed cold like the
+    workloads above: the many-row GEMM (M = 64, 256, 1024) and the expand path
+    (M = 4096) on the decode round's shapes, the fused forms (two projections
+    over one x, the silu(gate) * up input, de-interleaved Q|K|V|Z output, a
+    grouped launch over 128 experts) and the FP8 block-scaled product."""
+    import verify_nvfp4_w4a16_amd as nv
+    out = {}
+    def rotate(make, nbytes):
+        return [make() for _ in range(max(2, -(-COLD_BYTES // nbytes)))]
+
+    def xs(m, k, seed):
+        xb = workload.activations_bf16(m, k, seed)
+        return torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def nvfp4_weight(n, k, seed):
+        packed, scales, t = nv.pack(workload.weights_f32(n, k, seed))
+        return torch.from_numpy(packed).to(dev), torch.from_numpy(scales).to(dev), t, packed.nbytes + scales.nbytes
+
+    def call(fn, *args):
+        st = fn(*args)
+        if st != nv.OK:
+            raise nv.Nvfp4Error(st, getattr(fn, "__name__", "call"))
+
+    gemm = {}
+    for s in workload.ROUND_SHAPES:
+        wp0, sc0, t, wb = nvfp4_weight(s.n, s.k, 7)
+        ws = rotate(lambda: (wp0.clone(), sc0.clone()), wb)
+        for m in (64, 256, 1024):
+            x = xs(m, s.k, 8)
+            y = torch.empty((m, s.n), dtype=torch.bfloat16, device=dev)
+            def run(h):
+                for wp, sc in ws:
+                    call(nv.gemm_raw, x.data_ptr(), wp.data_ptr(), sc.data_ptr(), t, y.data_ptr(), m, s.n, s.k,
+                         nv.OUT_BF16, h)
+            us = timed_graph(torch, stream, run) * 1e3 / len(ws)
+            def run_mm(h):
+                for wp, sc in ws:
+                    call(nv.matmul_raw, x.data_ptr(), wp.data_ptr(), sc.data_ptr(), t, y.data_ptr(), m, s.n, s.k,
+                         nv.OUT_BF16, h)
+            us_mm = timed_graph(torch, stream, run_mm) * 1e3 / len(ws)
+            tf = 2.0 * m * s.n * s.k / (us * 1e-6) / 1e12
+            gemm[f"{s.n}x{s.k}_M{m}"] = {"us": us, "TFLOPs": tf, "frac_of_bf16_mfma_peak": tf / PEAK_BF16_MFMA_TFLOPS,
+                                        "weight_GBps": wb / (us * 1e-6) / 1e9, "matmul_dispatch_us": us_mm}
+        del ws
+    out["gemm_regime"] = gemm
+
+    n, k, m = 8192, 4096, 4096
+    wp0, sc0, t, wb = nvfp4_weight(n, k, 9)
+    x = xs(m, k, 10)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    wbf = torch.empty((n, k), dtype=torch.bfloat16, device=dev)
+    us_expand = timed_graph(torch, stream, lambda h: call(nv.dequant_bf16_raw, wp0.data_ptr(), sc0.data_ptr(), t, 0,
+                                                          wbf.data_ptr(), n, k, h)) * 1e3
+    us_exp_gemm = timed_graph(torch, stream, lambda h: call(nv.gemm_expanded_raw, x.data_ptr(), wbf.data_ptr(), t,
+                                                            y.data_ptr(), m, n, k, nv.OUT_BF16, h)) * 1e3
+    us_gemm = timed_graph(torch, stream, lambda h: call(nv.gemm_raw, x.data_ptr(), wp0.data_ptr(), sc0.data_ptr(), t,
+                                                        y.data_ptr(), m, n, k, nv.OUT_BF16, h)) * 1e3
+    out["expand_8192x4096_M4096"] = {"expand_us": us_expand, "expand_GBps_read_plus_write":
+                                     (wb + 2 * n * k) / (us_expand * 1e-6) / 1e9,
+                                     "gemm_expanded_us": us_exp_gemm, "gemm_nvfp4_us": us_gemm,
+                                     "gemm_expanded_TFLOPs": 2.0 * m * n * k / (us_exp_gemm * 1e-6) / 1e12}
+    del wbf
+
+    fused = {}
+    n, k = 12288, 4096
+    a = nvfp4_weight(n, k, 11)
+    b = nvfp4_weight(n, k, 12)
+    pairs = rotate(lambda: (a[0].clone(), a[1].clone(), b[0].clone(), b[1].clone()), 2 * a[3])
+    for m in (1, 8):
+        x = xs(m, k, 13)
+        y0 = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        y1 = torch.empty_like(y0)
+        def run(h):
+            for wa, sa, wb_, sb in pairs:
+                call(nv.linear_dual_raw, x.data_ptr(), wa.data_ptr(), sa.data_ptr(), a[2], y0.data_ptr(),
+                     wb_.data_ptr(), sb.data_ptr(), b[2], y1.data_ptr(), m, n, k, nv.OUT_BF16, h)
+        us = timed_graph(torch, stream, run) * 1e3 / len(pairs)
+        fused[f"dual_2x{n}x{k}_M{m}"] = {"us": us, "weight_GBps": 2 * a[3] / (us * 1e-6) / 1e9}
+    del pairs
+    n, k = 4096, 12288
+    wp0, sc0, t, wb = nvfp4_weight(n, k, 14)
+    ws = rotate(lambda: (wp0.clone(), sc0.clone()), wb)
+    for m in (1, 2):
+        g, u = xs(m, k, 15), xs(m, k, 16)
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        def run(h):
+            for wp, sc in ws:
+                call(nv.linear_silu_input_raw, g.data_ptr(), u.data_ptr(), wp.data_ptr(), sc.data_ptr(), t,
+                     y.data_ptr(), m, n, k, nv.OUT_BF16, h)
+        us = timed_graph(torch, stream, run) * 1e3 / len(ws)
+        fused[f"silu_input_{n}x{k}_M{m}"] = {"us": us, "weight_GBps": wb / (us * 1e-6) / 1e9}
+    del ws
+    n, k, widths = 12288, 4096, [256, 128, 128, 256]
+    wp0, sc0, t, wb = nvfp4_weight(n, k, 17)
+    ws = rotate(lambda: (wp0.clone(), sc0.clone()), wb)
+    for m in (1, 8):
+        x = xs(m, k, 18)
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        def run(h):
+            for wp, sc in ws:
+                call(nv.linear_deinterleave_raw, x.data_ptr(), wp.data_ptr(), sc.data_ptr(), t, y.data_ptr(),
+                     m, n, k, nv.OUT_BF16, widths, h)
+        us = timed_graph(torch, stream, run) * 1e3 / len(ws)
+        fused[f"qkvz_{n}x{k}_M{m}"] = {"us": us, "weight_GBps": wb / (us * 1e-6) / 1e9}
+    del ws
+    experts, n, k, m = 128, 1536, 4096, 2
+    wp0, sc0, t, wb = nvfp4_weight(n, k, 19)
+    ews = [(wp0.clone(), sc0.clone()) for _ in range(experts)]
+    xe = [xs(m, k, 20 + e % 4) for e in range(experts)]
+    ye = [torch.empty((m, n), dtype=torch.bfloat16, device=dev) for _ in range(experts)]
+    rec = np.zeros(experts, dtype=nv.GROUP_DTYPE)
+    for e in range(experts):
+        rec[e] = (xe[e].data_ptr(), ews[e][0].data_ptr(), ews[e][1].data_ptr(), ye[e].data_ptr(), t, m)
+    table = torch.from_numpy(rec.view(np.uint8)).to(dev)
+    us = timed_graph(torch, stream, lambda h: call(nv.linear_grouped_raw, table.data_ptr(), experts, m, n, k,
+                                                   nv.OUT_BF16, h)) * 1e3
+    fused[f"grouped_{experts}x{n}x{k}_M{m}"] = {"us": us, "weight_GBps": experts * wb / (us * 1e-6) / 1e9}
+    del ews
+    out["fused"] = fused
+
+    fp8 = {}
+    for s in workload.ROUND_SHAPES:
+        codes, scales = nv.fp8_pack(workload.weights_f32(s.n, s.k, 21))
+        c0, s0 = torch.from_numpy(codes).to(dev), torch.from_numpy(scales).to(dev)
+        wb = codes.nbytes + scales.nbytes
+        ws = rotate(lambda: (c0.clone(), s0.clone()), wb)
+        for m in (1, 16, 32):
+            x = xs(m, s.k, 22)
+            y = torch.empty((m, s.n), dtype=torch.bfloat16, device=dev)
+            def run(h):
+                for c, sc in ws:
+                    call(nv.fp8_linear_raw, x.data_ptr(), c.data_ptr(), sc.data_ptr(), y.data_ptr(), m, s.n, s.k,
+                         nv.OUT_BF16, h)
+            us = timed_graph(torch, stream, run) * 1e3 / len(ws)
+            gbps = wb / (us * 1e-6) / 1e9
+            fp8[f"{s.n}x{s.k}_M{m}"] = {"us": us, "weight_GBps": gbps, "frac_of_peak": gbps / PEAK_HBM_GBPS}
+        del ws
+    out["fp8_w8a16"] = fp8
+    torch.cuda.synchronize()
+    return out
+
+
 def cpu_baseline(torch, dev, rnd: Round, launches: dict, ms_list) -> dict:
     """The oracle on this host's cores over a bounded sample of the same
     workload: the decode round's products of its first layers, in round order
@@ -505,6 +648,7 @@ def main() -> int:
                     "mfma_frac_of_bf16_peak": dom["mfma_TFLOPs"] / PEAK_BF16_MFMA_TFLOPS}
         ceiling = read_ceiling(torch, stream, rnd)
         configs = config_timings(torch, dev, stream)
+        configs["next"] = next_rows(torch, dev, stream)
 
     base = None
     if not args.no_cpu_baseline:

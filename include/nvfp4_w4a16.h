@@ -105,8 +105,8 @@ int nvfp4_linear_shape_ok(int64_t m, int64_t n, int64_t k);
  * code objects and the (N, K) tile table once per process (the table may be
  * overridden by the file named in the environment variable NVFP4_TILES, read
  * here only), and sets up the current device's workspace once per device: 32
- * MiB of tagged partial sums plus 16 KiB of generation words in uncached
- * device memory, zeroed once and kept until the process ends (the many-row
+ * MiB of tagged partial sums plus 16 KiB of generation words in device
+ * memory, zeroed once and kept until the process ends (the many-row
  * kernel exchanges segment-group sums through it; generations only advance,
  * so it is never cleared again).  Call on every device before capturing
  * nvfp4_linear into a HIP graph; the first nvfp4_linear call on a device runs
@@ -380,8 +380,11 @@ int nvfp4_gemm(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scale
 /*
  * Device, asynchronous.  Picks the kernel by row count over one stored
  * format, as "10 Kernels" 10.2's table does: nvfp4_linear for M <= 32,
- * nvfp4_gemm above.  Both give every row the same bits.  Errors: those of the
- * call it makes.
+ * nvfp4_linear on 32-row slices up to 128 rows (one launch per slice; the
+ * 128-row GEMM tile would leave most CUs idle there), nvfp4_gemm above.  All
+ * give every row the same bits.  Shape contract: nvfp4_gemm's.  A slice that
+ * fails stops the call with its status, earlier slices having been launched.
+ * Errors: those of the calls it makes.
  */
 int nvfp4_matmul(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4m3,
                  float tensor_scale, void* y, int64_t m, int64_t n, int64_t k, int y_dtype,

@@ -58,6 +58,8 @@ def test_gemm_parity_and_rows_across_m(shape):
     cols = np.unique(np.concatenate([np.arange(16), np.arange(shape.n - 16, shape.n),
                                      workload.rng(71).integers(0, shape.n, 96)]))
     full = bits(_gemm(xd, w, 1024)).clone()
+    assert torch.equal(bits(_gemm(xd, w, 1024, fn=nv.matmul_raw)), full)
+    assert torch.equal(bits(_gemm(xd, w, 100, fn=nv.matmul_raw)), full[:100])
     rows = np.unique(np.concatenate([np.arange(8), workload.rng(72).integers(0, 1024, 56)]))
     check_parity(_gemm(xd, w, 1024)[torch.from_numpy(rows).to(DEV)], x[rows], w, cols=cols,
                  label=f"gemm {shape.n}x{shape.k} M=1024 sampled rows")
@@ -81,8 +83,8 @@ def test_gemm_rows_equal_linear_rows():
         lin = bits(_linear(upload_bits(x[r0:r0 + 32]), w, 32))
         assert torch.equal(lin, g[r0:r0 + 32]), r0
     assert torch.equal(bits(_linear(upload_bits(x[5:6]), w, 1)), g[5:6])
-    for m in (32, 33):
-        y = _gemm(xd, w, m, fn=nv.matmul_raw)
+    for m in (32, 33, 64, 96):
+        y = _gemm(xd, w, m, fn=nv.matmul_raw)                # slices of 32 up to 128 rows
         assert torch.equal(bits(y), g[:m]), m
     check_parity(_gemm(xd, w, 96, torch.float32), x, w, label="gemm 4136x4096 M=96 fp32")
 

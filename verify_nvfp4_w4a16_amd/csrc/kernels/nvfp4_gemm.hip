@@ -27,6 +27,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 
@@ -45,6 +46,7 @@ constexpr int kThreads = 256;
 constexpr int kPitch = kBlockK + 8;     // LDS row pitch of an x block, bf16 elements
 constexpr int kXVec = kRows * kBlockK / 8 / kThreads;   // 16-byte x pieces per thread per block
 constexpr size_t kGemmLds = 2 * size_t(kRows) * kPitch * sizeof(uint16_t);
+constexpr int64_t kChunkedMaxM = 128;   // nvfp4_matmul: 32-row slices of the skinny product up to here
 
 struct GemmArgs {
     const uint16_t* x;      // bf16 [M, K]
@@ -75,7 +77,7 @@ struct BRegs<true> {
 };
 
 template <bool BF16W, bool OUT_F32>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads, 2)
 nvfp4_gemm_kernel(GemmArgs a) {
     extern __shared__ __align__(16) uint16_t xs[];     // [2][kRows][kPitch]
     const int tid = threadIdx.x;
@@ -104,16 +106,13 @@ nvfp4_gemm_kernel(GemmArgs a) {
         }
     }
     // this thread's 16-byte pieces of an x block: piece v = tid + 256 i is
-    // row v / 16, k 8 (v % 16) of the block
-    const uint16_t* xsrc[kXVec];
-    int xdst[kXVec];
-#pragma unroll
-    for (int i = 0; i < kXVec; ++i) {
-        const int v = tid + kThreads * i;
-        const int r = v / 16, p = v % 16;
-        xsrc[i] = a.x + (int64_t)min(row0 + r, a.m - 1) * a.k + 8 * p;
-        xdst[i] = r * kPitch + 8 * p;
-    }
+    // row tid / 16 + 16 i, k 8 (tid % 16) of the block (rows past M read row
+    // M - 1, never stored)
+    const int xr0 = tid / 16, xp = tid % 16;
+    const uint16_t* xsrc0 = a.x + 8 * xp;
+    const int xdst0 = xr0 * kPitch + 8 * xp;
+    const bool xfull = row0 + kRows <= a.m;
+    auto xrow_of = [&](int i) { return (int64_t)(xfull ? row0 + xr0 + 16 * i : min(row0 + xr0 + 16 * i, a.m - 1)); };
 
     auto load_b = [&](BRegs<BF16W>& b, int kb) {
 #pragma unroll
@@ -131,12 +130,12 @@ nvfp4_gemm_kernel(GemmArgs a) {
     u32x4 xr[kXVec];
     auto load_x = [&](int kb) {
 #pragma unroll
-        for (int i = 0; i < kXVec; ++i) xr[i] = load16(xsrc[i] + kb);
+        for (int i = 0; i < kXVec; ++i) xr[i] = load16(xsrc0 + xrow_of(i) * a.k + kb);
     };
     auto store_x = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < kXVec; ++i)
-            *reinterpret_cast<u32x4*>(xs + buf * kRows * kPitch + xdst[i]) = xr[i];
+            *reinterpret_cast<u32x4*>(xs + buf * kRows * kPitch + xdst0 + 16 * kPitch * i) = xr[i];
     };
 
     f32x4 acc[kMT][kC], grp[kMT][kC], tot[kMT][kC];
@@ -349,5 +348,22 @@ extern "C" int nvfp4_matmul(const void* x_bf16, const uint8_t* w_packed, const u
                             void* stream) {
     if (m >= 0 && m <= NVFP4_MAX_M)
         return nvfp4_linear(x_bf16, w_packed, scales_e4m3, tensor_scale, y, m, n, k, y_dtype, stream);
-    return nvfp4_gemm(x_bf16, w_packed, scales_e4m3, tensor_scale, y, m, n, k, y_dtype, stream);
+    int st = nvfp4_gemm_shape_ok(m, n, k);
+    if (st != NVFP4_OK) return st;
+    if (m > kChunkedMaxM)
+        return nvfp4_gemm(x_bf16, w_packed, scales_e4m3, tensor_scale, y, m, n, k, y_dtype, stream);
+    // 33..128 rows: the skinny product on 32-row slices (same bits), which
+    // streams the weight at a few TB/s per slice where the 128-row GEMM tile
+    // would leave most CUs idle (measured on MI355X at 64 rows: 24-44 us
+    // against 66-187 us on the decode round's shapes).
+    if (y_dtype != NVFP4_OUT_BF16 && y_dtype != NVFP4_OUT_F32) return NVFP4_ERR_DTYPE;
+    if (!x_bf16 || !y) return NVFP4_ERR_NULL;
+    const size_t ysize = y_dtype == NVFP4_OUT_F32 ? 4 : 2;
+    for (int64_t r0 = 0; r0 < m; r0 += NVFP4_MAX_M) {
+        const int64_t rows = std::min<int64_t>(NVFP4_MAX_M, m - r0);
+        st = nvfp4_linear(static_cast<const uint16_t*>(x_bf16) + r0 * k, w_packed, scales_e4m3, tensor_scale,
+                          static_cast<uint8_t*>(y) + r0 * n * ysize, rows, n, k, y_dtype, stream);
+        if (st != NVFP4_OK) return st;
+    }
+    return NVFP4_OK;
 }

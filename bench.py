@@ -43,7 +43,7 @@ PEAK_BF16_MFMA_TFLOPS = 2500.0
 BYTES_PER_WEIGHT = 0.5625          # 4-bit code + one e4m3 byte per 16 weights
 CPU_BASELINE_MIN_S = 10.0           # the oracle runs products until this much CPU time has passed ...
 CPU_BASELINE_MAX_S = 30.0           # ... and stops starting new ones past this
-CPU_BASELINE_LAYERS = 8             # layers whose packed bytes stay on the host for it
+CPU_BASELINE_LAYERS = 32            # layers whose packed bytes stay on the host for it
 COLD_BYTES = 512 << 20              # weight copies rotated per timed launch sequence
 KERNEL_SOURCES = [os.path.join(ROOT, "verify_nvfp4_w4a16_amd", "csrc", "kernels", f)
                   for f in ("nvfp4_common.h", "nvfp4_linear.hip", "nvfp4_gemm.hip", "nvfp4_fused.hip", "w8a16.hip")]
@@ -497,12 +497,14 @@ def cpu_baseline(torch, dev, rnd: Round, launches: dict, ms_list) -> dict:
                                  axis=1)
             y64 = y.float().cpu().numpy().astype(np.float64)
             worst = max(worst, oracle.max_violation(y64, y_ref, bnd, "bf16"))
-            done.append(f"L{l}P{p}M{m}")
+            done.append((l, p, m))
     return {"value": weight_bytes / total_s / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
             "cpu_model": cpu_model(),
-            "sample": f"{len(done)} decode-round products ({', '.join(done)}; {weight_bytes} weight-stream "
-                      f"bytes) in {total_s:.1f} s of oracle time: fp64 decode and dgemm, columns split over "
-                      f"{cores} worker threads, BLAS single-threaded per worker",
+            "sample": f"{len(done)} decode-round products in round order (layers {done[0][0]}..{done[-1][0]}, "
+                      f"every projection, M = {', '.join(str(m) for m in ms_list)} each; last "
+                      f"L{done[-1][0]} P{done[-1][1]} M{done[-1][2]}; {weight_bytes} weight-stream bytes) in "
+                      f"{total_s:.1f} s of oracle time: fp64 decode and dgemm, columns split over {cores} "
+                      f"worker threads, BLAS single-threaded per worker",
             "seconds": total_s, "parity_max_err_over_tol": worst}
 
 
@@ -537,6 +539,8 @@ def main() -> int:
                     help="time eager launches instead of graph replays (for counter collection)")
     ap.add_argument("--copy-only", action="store_true",
                     help="only run a 1 GiB device copy 5 times (counter calibration) and exit")
+    ap.add_argument("--next-only", action="store_true",
+                    help="only time the other regimes and forms (GEMM, expand, fused, grouped, FP8) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -559,6 +563,11 @@ def main() -> int:
                           "dispatches": 5}), flush=True)
         return 0
     nv.init()
+    if args.next_only:
+        stream = torch.cuda.Stream(device=dev)
+        print(json.dumps({"next": next_rows(torch, dev, stream),
+                          "kernel_source_sha256_16": kernel_source_hash()}), flush=True)
+        return 0
     ms_list = [int(v) for v in args.m.split(",") if v]
     extra_m = [int(v) for v in args.extra_m.split(",") if v]
 

@@ -108,7 +108,8 @@ int nvfp4_linear_shape_ok(int64_t m, int64_t n, int64_t k);
  * MiB of tagged partial sums plus 16 KiB of generation words in device
  * memory, zeroed once and kept until the process ends (the many-row
  * kernel exchanges segment-group sums through it; generations only advance,
- * so it is never cleared again).  Call on every device before capturing
+ * so it is never cleared again), and 64 MiB for the group sums of a K-split
+ * nvfp4_gemm (written in full before they are read).  Call on every device before capturing
  * nvfp4_linear into a HIP graph; the first nvfp4_linear call on a device runs
  * it otherwise.  Safe to call more than once.  If the workspace cannot be
  * allocated, nvfp4_linear still works (with kernels that do not need it) and
@@ -369,8 +370,13 @@ int nvfp4_gemm_shape_ok(int64_t m, int64_t n, int64_t k);
  * operation C = A @ dequant(B).  Arguments, layouts, alignment and ownership
  * as nvfp4_linear; M == 0 launches nothing.  The K order is the (N, K) tile's
  * (as nvfp4_linear), so each row's bits are those nvfp4_linear gives it, for
- * every M ("10 Kernels" 10.1).  No allocation, no host sync.  Workgroups own
- * 128 rows x 64 columns.
+ * every M ("10 Kernels" 10.1).  No allocation (the first call on a device
+ * runs nvfp4_init's set-up unless it has run), no host sync.  Workgroups own
+ * 128 rows x 64 columns; when that gives no more workgroups than CUs and the
+ * tile has split > 1, each workgroup takes one segment group and a second
+ * kernel adds the group sums in order through the device buffer nvfp4_init
+ * allocates (same bits): such calls on one device must not overlap in time
+ * (calls on one stream, or on streams ordered by events, never do).
  * Errors: NULL, SHAPE, ALIGN, DTYPE, HIP, DEVICE, TILEFILE.
  */
 int nvfp4_gemm(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4m3,
@@ -380,9 +386,10 @@ int nvfp4_gemm(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scale
 /*
  * Device, asynchronous.  Picks the kernel by row count over one stored
  * format, as "10 Kernels" 10.2's table does: nvfp4_linear for M <= 32,
- * nvfp4_linear on 32-row slices up to 128 rows (one launch per slice; the
- * 128-row GEMM tile would leave most CUs idle there), nvfp4_gemm above.  All
- * give every row the same bits.  Shape contract: nvfp4_gemm's.  A slice that
+ * nvfp4_linear on 32-row slices up to 96 rows (one launch per slice; the
+ * 128-row GEMM tile leaves most CUs idle there), nvfp4_gemm above.  All
+ * give every row the same bits.  Like those calls, calls that use the
+ * device workspace must not overlap in time on one device.  Shape contract: nvfp4_gemm's.  A slice that
  * fails stops the call with its status, earlier slices having been launched.
  * Errors: those of the calls it makes.
  */

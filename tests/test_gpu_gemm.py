@@ -84,9 +84,27 @@ def test_gemm_rows_equal_linear_rows():
         assert torch.equal(lin, g[r0:r0 + 32]), r0
     assert torch.equal(bits(_linear(upload_bits(x[5:6]), w, 1)), g[5:6])
     for m in (32, 33, 64, 96):
-        y = _gemm(xd, w, m, fn=nv.matmul_raw)                # slices of 32 up to 128 rows
+        y = _gemm(xd, w, m, fn=nv.matmul_raw)                # slices of 32 up to 96 rows
         assert torch.equal(bits(y), g[:m]), m
     check_parity(_gemm(xd, w, 96, torch.float32), x, w, label="gemm 4136x4096 M=96 fp32")
+
+
+def test_gemm_k_split_rows_equal_unsplit():
+    # No more 128 x 64 tiles than CUs: each workgroup takes one segment group
+    # and a second kernel adds the group sums in order.  Every row's bits
+    # equal those of a product with enough rows to run unsplit (bf16 and fp32
+    # outputs, ragged columns), and the split product is within the oracle's
+    # tolerance.
+    for n, k in [(4096, 8192), (4100, 4096)]:
+        w = Weight.from_f32(workload.weights_f32(n, k, n + 5))
+        x = workload.activations_bf16(1536, k, k + 6)
+        xd = upload_bits(x)
+        for dt in (torch.bfloat16, torch.float32):
+            full = bits(_gemm(xd, w, 1536, dt)).clone()
+            for m in (1, 40, 200, 255):
+                assert torch.equal(bits(_gemm(xd, w, m, dt)), full[:m]), (n, k, m, dt)
+        cols = np.unique(np.concatenate([np.arange(8), np.arange(n - 8, n), workload.rng(n).integers(0, n, 48)]))
+        check_parity(_gemm(xd, w, 200, torch.float32), x[:200], w, cols=cols, label=f"k-split gemm {n}x{k} M=200")
 
 
 def test_gemm_ragged_rows_random_codes():

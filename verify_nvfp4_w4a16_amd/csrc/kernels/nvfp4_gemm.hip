@@ -46,7 +46,7 @@ constexpr int kThreads = 256;
 constexpr int kPitch = kBlockK + 8;     // LDS row pitch of an x block, bf16 elements
 constexpr int kXVec = kRows * kBlockK / 8 / kThreads;   // 16-byte x pieces per thread per block
 constexpr size_t kGemmLds = 2 * size_t(kRows) * kPitch * sizeof(uint16_t);
-constexpr int64_t kChunkedMaxM = 128;   // nvfp4_matmul: 32-row slices of the skinny product up to here
+constexpr int64_t kChunkedMaxM = 96;    // nvfp4_matmul: 32-row slices of the skinny product up to here
 
 struct GemmArgs {
     const uint16_t* x;      // bf16 [M, K]
@@ -57,6 +57,8 @@ struct GemmArgs {
     int m, n, k;
     int k_per_wave;         // segment length
     int group;              // segments per segment group
+    float* part;            // parts > 1: group sums [parts][M][N] (fp32, t not applied)
+    int parts;              // workgroups along K (blockIdx.z): 1, or one per segment group
 };
 
 // The B operands of one 128-k block for a lane's kC columns: with NVFP4
@@ -88,7 +90,9 @@ nvfp4_gemm_kernel(GemmArgs a) {
     const int kq = lane / 16;
     const int row0 = blockIdx.y * kRows;
     const int col0 = blockIdx.x * kCols + wn * kC * 16;
-    const int nblocks = a.k / kBlockK;
+    // K blocks of this workgroup: all of K, or one segment group's
+    const int nblocks = a.k / kBlockK / a.parts;
+    const int kbase = static_cast<int>(blockIdx.z) * nblocks * kBlockK;
     const int seg_blocks = a.k_per_wave / kBlockK;
 
     // Rows past M and columns past N read the last valid one (never stored).
@@ -114,7 +118,8 @@ nvfp4_gemm_kernel(GemmArgs a) {
     const bool xfull = row0 + kRows <= a.m;
     auto xrow_of = [&](int i) { return (int64_t)(xfull ? row0 + xr0 + 16 * i : min(row0 + xr0 + 16 * i, a.m - 1)); };
 
-    auto load_b = [&](BRegs<BF16W>& b, int kb) {
+    auto load_b = [&](BRegs<BF16W>& b, int kl) {
+        const int kb = kbase + kl;
 #pragma unroll
         for (int c = 0; c < kC; ++c) {
             if constexpr (BF16W) {
@@ -128,9 +133,9 @@ nvfp4_gemm_kernel(GemmArgs a) {
         }
     };
     u32x4 xr[kXVec];
-    auto load_x = [&](int kb) {
+    auto load_x = [&](int kl) {
 #pragma unroll
-        for (int i = 0; i < kXVec; ++i) xr[i] = load16(xsrc0 + xrow_of(i) * a.k + kb);
+        for (int i = 0; i < kXVec; ++i) xr[i] = load16(xsrc0 + xrow_of(i) * a.k + kbase + kl);
     };
     auto store_x = [&](int buf) {
 #pragma unroll
@@ -188,7 +193,9 @@ nvfp4_gemm_kernel(GemmArgs a) {
             }
         }
         // end of a segment: its chain joins its group's sum, and at the end
-        // of a group the group sum joins the total (first ones as they are)
+        // of a group the group sum joins the total (first ones as they are);
+        // segments are numbered within this workgroup's K range, which is
+        // all of K or exactly one group
         if ((b + 1) % seg_blocks == 0) {
             const int seg = (b + 1) / seg_blocks - 1;
             const bool gfirst_seg = seg % a.group == 0;
@@ -210,6 +217,22 @@ nvfp4_gemm_kernel(GemmArgs a) {
         }
     }
 
+    if (a.parts > 1) {
+        // one group's sum per output; nvfp4_gemm_reduce adds the groups in order
+        float* dst = a.part + (int64_t)blockIdx.z * a.m * a.n;
+#pragma unroll
+        for (int t = 0; t < kMT; ++t)
+#pragma unroll
+            for (int c = 0; c < kC; ++c) {
+                const int n = col0 + 16 * c + col_lane;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int m = row0 + wm * 16 * kMT + 16 * t + 4 * kq + j;
+                    if (m < a.m && n < a.n) dst[(int64_t)m * a.n + n] = grp[t][c][j];
+                }
+            }
+        return;
+    }
 #pragma unroll
     for (int t = 0; t < kMT; ++t)
 #pragma unroll
@@ -227,6 +250,28 @@ nvfp4_gemm_kernel(GemmArgs a) {
                 }
             }
         }
+}
+
+// The group sums of a K-split GEMM [parts][M][N] added in group order (the
+// second level of the tile's order), times t, one rounding: each thread four
+// consecutive outputs of the flattened [M][N].
+template <bool OUT_F32>
+__global__ void __launch_bounds__(256)
+nvfp4_gemm_reduce(const float* part, int parts, int64_t mn, float t, void* y) {
+    const int64_t i0 = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
+    if (i0 >= mn) return;
+    const int cnt = mn - i0 < 4 ? static_cast<int>(mn - i0) : 4;
+    float tot[4];
+    for (int j = 0; j < cnt; ++j) tot[j] = part[i0 + j];
+    for (int q = 1; q < parts; ++q)
+        for (int j = 0; j < cnt; ++j) tot[j] = tot[j] + part[(int64_t)q * mn + i0 + j];
+    for (int j = 0; j < cnt; ++j) {
+        const float r = tot[j] * t;
+        if (OUT_F32)
+            static_cast<float*>(y)[i0 + j] = r;
+        else
+            static_cast<uint16_t*>(y)[i0 + j] = f32_to_bf16_rne(r);
+    }
 }
 
 // Expands NVFP4 to bf16 [N, K]: each thread one packed dword (8 k) of one
@@ -296,9 +341,40 @@ int gemm_launch(const void* x, const void* w, const uint8_t* scales, float t, vo
     a.k = static_cast<int>(k);
     a.k_per_wave = static_cast<int>(k / tile.waves);
     a.group = tile.waves / tile.split;
-    const dim3 grid(static_cast<unsigned>((n + kCols - 1) / kCols), static_cast<unsigned>((m + kRows - 1) / kRows));
+    a.part = nullptr;
+    a.parts = 1;
+    const int64_t col_tiles = (n + kCols - 1) / kCols, row_tiles = (m + kRows - 1) / kRows;
+    // No more tiles than CUs: one workgroup per segment group instead (the
+    // tile's split), the group sums added in order by a second kernel, so
+    // the bits do not change.  Needs the partial-sum buffer nvfp4_init
+    // allocates.  (Measured on MI355X: 1.1-2.7x faster at 128..512 rows on
+    // the decode round's products; with more tiles than CUs the extra
+    // partial-sum traffic costs more than the split gains.)
+    if (tile.split > 1) {
+        float* part = nullptr;
+        size_t bytes = 0;
+        int cus = 256;
+        st = nvfp4::gemm_partials(&part, &bytes, &cus);
+        if (st != NVFP4_OK) return st;
+        if (part && row_tiles * col_tiles <= int64_t(cus) &&
+            size_t(tile.split) * size_t(m) * size_t(n) * sizeof(float) <= bytes) {
+            a.part = part;
+            a.parts = tile.split;
+        }
+    }
+    const dim3 grid(static_cast<unsigned>(col_tiles), static_cast<unsigned>(row_tiles),
+                    static_cast<unsigned>(a.parts));
     hipLaunchKernelGGL(pick_gemm(bf16w, y_dtype), grid, dim3(kThreads), kGemmLds, static_cast<hipStream_t>(stream), a);
-    return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+    if (hipGetLastError() != hipSuccess) return NVFP4_ERR_HIP;
+    if (a.parts > 1) {
+        const int64_t mn = m * n;
+        const int64_t blocks = (mn + 1023) / 1024;
+        auto red = y_dtype == NVFP4_OUT_F32 ? nvfp4_gemm_reduce<true> : nvfp4_gemm_reduce<false>;
+        hipLaunchKernelGGL(red, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                           static_cast<const float*>(a.part), a.parts, mn, t, y);
+        if (hipGetLastError() != hipSuccess) return NVFP4_ERR_HIP;
+    }
+    return NVFP4_OK;
 }
 
 }  // namespace
@@ -352,10 +428,11 @@ extern "C" int nvfp4_matmul(const void* x_bf16, const uint8_t* w_packed, const u
     if (st != NVFP4_OK) return st;
     if (m > kChunkedMaxM)
         return nvfp4_gemm(x_bf16, w_packed, scales_e4m3, tensor_scale, y, m, n, k, y_dtype, stream);
-    // 33..128 rows: the skinny product on 32-row slices (same bits), which
+    // 33..96 rows: the skinny product on 32-row slices (same bits), which
     // streams the weight at a few TB/s per slice where the 128-row GEMM tile
-    // would leave most CUs idle (measured on MI355X at 64 rows: 24-44 us
-    // against 66-187 us on the decode round's shapes).
+    // leaves most CUs idle (measured on MI355X at 64 rows: 22-42 us against
+    // 31-72 us for the K-split GEMM on the decode round's shapes; at 128 rows
+    // the two are within 10 %).
     if (y_dtype != NVFP4_OUT_BF16 && y_dtype != NVFP4_OUT_F32) return NVFP4_ERR_DTYPE;
     if (!x_bf16 || !y) return NVFP4_ERR_NULL;
     const size_t ysize = y_dtype == NVFP4_OUT_F32 ? 4 : 2;

@@ -1236,6 +1236,7 @@ constexpr int kMaxDevices = 64;
 constexpr size_t kWorkBytes = size_t(32) << 20;      // tagged group sums of the many-row kernel
 constexpr size_t kGenWords = kWorkBytes / sizeof(uint64_t) / kGenBlock;   // one per block of them
 constexpr size_t kStatusWords = 64;                  // the time-out word, on its own 256 bytes
+constexpr size_t kGemmPartBytes = size_t(64) << 20;  // per-group partial sums of the many-row GEMM
 
 // Fixed scratch of nvfp4_linear_noalloc, in 32-bit words: 8 MiB of tagged
 // group sums, their generation words, then the time-out word.
@@ -1271,6 +1272,7 @@ struct DeviceState {
     int setup_status = NVFP4_OK;
     int cus = 0;
     Workspace heap;                 // device memory, never freed
+    float* gemm_part = nullptr;     // device memory, never freed: the GEMM's group partial sums
     Workspace fixed;                // this device's `scratch` array
 };
 DeviceState g_dev[kMaxDevices];
@@ -1348,6 +1350,13 @@ void alloc_workspace(int dev) {
     } else {
         (void)hipGetLastError();   // clear the failure; the memory (if any) stays unused
     }
+    // The many-row GEMM's per-group partial sums: written in full before they
+    // are read by every call that uses them, so never cleared.
+    void* part = nullptr;
+    if (hipMalloc(&part, kGemmPartBytes) == hipSuccess)
+        d.gemm_part = static_cast<float*>(part);
+    else
+        (void)hipGetLastError();   // the GEMM then runs every group in one workgroup
 }
 
 std::once_flag g_init_once;
@@ -1401,6 +1410,25 @@ extern "C" int nvfp4_init(void) {
     std::call_once(d.alloc_once, [&] { alloc_workspace(dev); });
     return NVFP4_OK;
 }
+
+namespace nvfp4 {
+
+int gemm_partials(float** part, size_t* bytes, int* cus) {
+    *part = nullptr;
+    *bytes = 0;
+    const int st = nvfp4_init();
+    if (st != NVFP4_OK) return st;
+    int dev = 0;
+    if (current_device(&dev) != NVFP4_OK) return NVFP4_ERR_HIP;
+    *cus = g_dev[dev].cus > 0 ? g_dev[dev].cus : 256;
+    if (g_dev[dev].gemm_part) {
+        *part = g_dev[dev].gemm_part;
+        *bytes = kGemmPartBytes;
+    }
+    return NVFP4_OK;
+}
+
+}  // namespace nvfp4
 
 extern "C" int nvfp4_timeout_status(int* timed_out) {
     if (!timed_out) return NVFP4_ERR_NULL;

@@ -1400,6 +1400,12 @@ int device_setup() {
     return setup_current(&dev);
 }
 
+int device_cus() {
+    int dev = 0;
+    if (current_device(&dev) != NVFP4_OK || g_dev[dev].cus <= 0) return 256;
+    return g_dev[dev].cus;
+}
+
 }  // namespace nvfp4
 
 extern "C" int nvfp4_init(void) {

@@ -18,6 +18,9 @@ int fused_setup();
 // Kernel attributes of the FP8 (W8A16) kernels.
 int w8a16_setup();
 
+// The current device's CU count (after device_setup; 256 if unknown).
+int device_cus();
+
 // nvfp4_init's set-up (allocating the device workspace once per device), then
 // the current device's buffer for the many-row GEMM's per-group partial sums
 // (*part = NULL and *bytes = 0 when it could not be allocated) and its CU count.

@@ -251,7 +251,9 @@ int nvfp4_tile_info(int64_t n, int64_t k, char* buf, int64_t buflen);
  * "Module ops" w4a16_gemv_dual (and its 2- and 3-row forms): y0 = x . W0^T and
  * y1 = x . W1^T, both weights [N, K] (each with its scales and tensor scale),
  * both outputs [M, N].  Shape contract, layouts and alignment of
- * nvfp4_linear; every output has the bits nvfp4_linear gives it.
+ * nvfp4_linear; every output has the bits nvfp4_linear gives it.  It runs
+ * nvfp4_linear's kernels with the weight picked per workgroup, so like
+ * nvfp4_linear it may use the device workspace (same rule on overlap).
  * Errors: NULL, SHAPE, ALIGN, DTYPE, HIP, DEVICE, TILEFILE.
  */
 int nvfp4_linear_dual(const void* x_bf16, const uint8_t* w_packed0, const uint8_t* scales0,
@@ -280,7 +282,8 @@ int nvfp4_linear_silu_input(const void* gate_bf16, const void* up_bf16, const ui
  * all groups' part 0, then all groups' part 1, ...: row r of part p of group
  * g lands in column groups * (widths[0] + .. + widths[p-1]) + g * widths[p] + r.
  * widths: host array of `parts` (1..4) positive counts, read during the call.
- * Values and bits are nvfp4_linear's, only the columns move.
+ * Values and bits are nvfp4_linear's, only the columns move (nvfp4_linear's
+ * kernels with the map on the store; same workspace rule).
  * Errors: NULL, SHAPE (also N not a multiple of G), ALIGN, DTYPE, HIP, DEVICE,
  * TILEFILE.
  */
@@ -307,8 +310,10 @@ typedef struct nvfp4_group {
  * array of count nvfp4_group_t (8-byte aligned) that must stay valid until the
  * stream passes the call.  max_m (0..32) bounds every entry's m; rows of an
  * entry past max_m are not computed.  Each output has the bits nvfp4_linear
- * gives it.  Entry pointers are not checked on the host (they are in device
- * memory): they must satisfy nvfp4_linear's contract.
+ * gives it: nvfp4_linear's kernels, sized for max_m, run with the entry
+ * picked per workgroup (same workspace rule).  Entry pointers are not checked
+ * on the host (they are in device memory): they must satisfy nvfp4_linear's
+ * contract.
  * Errors: NULL, SHAPE (also count > 65535), ALIGN, DTYPE, HIP, DEVICE, TILEFILE.
  */
 int nvfp4_linear_grouped(const nvfp4_group_t* table, int64_t count, int64_t max_m, int64_t n,

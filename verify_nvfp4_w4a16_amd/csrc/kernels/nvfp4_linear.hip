@@ -63,7 +63,60 @@ struct Args {
     int m, n, k;
     int k_per_wave;        // segment length
     int group;             // segments per segment group
+    // Several products of one (N, K) in one launch, blockIdx.y picking one:
+    // rows of a device table (m above is then the largest m of an entry),
+    // or, without a table, a second weight over the same x (product 1).
+    const nvfp4_group_t* table;
+    const uint8_t* wp1;
+    const uint8_t* sc1;
+    void* y1;
+    float t1;
+    // De-interleaved store (omap_parts > 0): weight row r of part p of group
+    // g goes to output column ngroups * (widths of parts before p) + g *
+    // width[p] + r.
+    int omap_parts;
+    int omap_width[4];
+    int omap_gwidth;
+    int omap_ngroups;
 };
+
+// The product of this workgroup (blockIdx.y) in a several-product launch;
+// m <= 0 means there is nothing to do (uniform over the workgroup).
+__device__ __forceinline__ Args entry_args(const Args& in) {
+    Args a = in;
+    if (in.table) {
+        const nvfp4_group_t& g = in.table[blockIdx.y];
+        a.x = static_cast<const uint16_t*>(g.x);
+        a.wp = g.w_packed;
+        a.sc = g.scales_e4m3;
+        a.y = g.y;
+        a.t = g.tensor_scale;
+        a.m = min(g.m, in.m);
+    } else if (blockIdx.y == 1) {
+        a.wp = in.wp1;
+        a.sc = in.sc1;
+        a.y = in.y1;
+        a.t = in.t1;
+    }
+    return a;
+}
+
+// Output column of weight row n (the de-interleaving map, or n itself).
+__device__ __forceinline__ int out_col(const Args& a, int n) {
+    if (a.omap_parts == 0) return n;
+    const int g = n / a.omap_gwidth;
+    int r = n - g * a.omap_gwidth;
+    int before = 0;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        if (p < a.omap_parts) {
+            if (r < a.omap_width[p]) return a.omap_ngroups * before + g * a.omap_width[p] + r;
+            r -= a.omap_width[p];
+            before += a.omap_width[p];
+        }
+    }
+    return n;   // unreachable for a valid map
+}
 
 // Folds segment sum `v` of segment `w` (w >= 1) into the running sums of the
 // two-level order: `grp` is the sum of the current group so far, `tot` the
@@ -122,9 +175,11 @@ __device__ __forceinline__ int xpiece(int u, int r) {
 // outputs are never stored), so the weight pipeline holds only weights in
 // registers.
 // Otherwise (x too large for LDS) each chunk also fetches its A operands.
-template <int C, int MT, int U, bool XLDS, bool OUT_F32>
+template <int C, int MT, int U, bool XLDS, bool OUT_F32, bool MULTI>
 __global__ void __launch_bounds__(512)
-nvfp4_skinny(Args a) {
+nvfp4_skinny(Args a_in) {
+    const Args a = MULTI ? entry_args(a_in) : a_in;
+    if (MULTI && a.m <= 0) return;                // an empty entry (uniform over the workgroup)
     extern __shared__ __align__(16) uint16_t lds[];   // x rows, then reused for segment partials
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
@@ -308,9 +363,9 @@ nvfp4_skinny(Args a) {
                 if (m < a.m && n < a.n) {
                     float r = acc[c][t][j] * a.t;
                     if (OUT_F32)
-                        static_cast<float*>(a.y)[(int64_t)m * a.n + n] = r;
+                        static_cast<float*>(a.y)[(int64_t)m * a.n + (MULTI ? out_col(a, n) : n)] = r;
                     else
-                        static_cast<uint16_t*>(a.y)[(int64_t)m * a.n + n] = f32_to_bf16_rne(r);
+                        static_cast<uint16_t*>(a.y)[(int64_t)m * a.n + (MULTI ? out_col(a, n) : n)] = f32_to_bf16_rne(r);
                 }
             }
     }
@@ -561,9 +616,11 @@ __device__ __forceinline__ void mma_chunk(f32x4 (&acc)[C][MT], const uint8_t* ws
 // single workgroup fits a CU's LDS.
 //
 // LDS: x [M][K + 8] bf16 | 2 x segment partials | per wavefront NB chunk buffers.
-template <int C, int MT, int NB, bool OUT_F32>
+template <int C, int MT, int NB, bool OUT_F32, bool MULTI>
 __global__ void __launch_bounds__(512)
-nvfp4_skinny_persistent(Args a) {
+nvfp4_skinny_persistent(Args a_in) {
+    const Args a = MULTI ? entry_args(a_in) : a_in;
+    if (MULTI && a.m <= 0) return;                         // an empty entry (uniform over the workgroup)
     extern __shared__ __align__(16) uint16_t lds[];
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
@@ -668,9 +725,9 @@ nvfp4_skinny_persistent(Args a) {
                         if (m < a.m && n < a.n) {
                             float r = acc[c][t][jj] * a.t;
                             if (OUT_F32)
-                                static_cast<float*>(a.y)[(int64_t)m * a.n + n] = r;
+                                static_cast<float*>(a.y)[(int64_t)m * a.n + (MULTI ? out_col(a, n) : n)] = r;
                             else
-                                static_cast<uint16_t*>(a.y)[(int64_t)m * a.n + n] = f32_to_bf16_rne(r);
+                                static_cast<uint16_t*>(a.y)[(int64_t)m * a.n + (MULTI ? out_col(a, n) : n)] = f32_to_bf16_rne(r);
                         }
                     }
             }
@@ -716,9 +773,11 @@ size_t persistent_lds_bytes(int64_t m, int64_t k, int waves, int c, int mt, int 
 // small, several share a CU and one's reduction overlaps the others' loads.
 //
 // LDS per wavefront: x slice [M][k_per_wave + 8] bf16 | NB chunk buffers.
-template <int C, int MT, int NB, bool OUT_F32>
+template <int C, int MT, int NB, bool OUT_F32, bool MULTI>
 __global__ void __launch_bounds__(512)
-nvfp4_skinny_tile(Args a) {
+nvfp4_skinny_tile(Args a_in) {
+    const Args a = MULTI ? entry_args(a_in) : a_in;
+    if (MULTI && a.m <= 0) return;                         // an empty entry (uniform over the workgroup)
     extern __shared__ __align__(16) uint8_t ldsb[];
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
@@ -805,9 +864,9 @@ nvfp4_skinny_tile(Args a) {
                 if (m < a.m && n < a.n) {
                     float r = acc[c][t][jj] * a.t;
                     if (OUT_F32)
-                        static_cast<float*>(a.y)[(int64_t)m * a.n + n] = r;
+                        static_cast<float*>(a.y)[(int64_t)m * a.n + (MULTI ? out_col(a, n) : n)] = r;
                     else
-                        static_cast<uint16_t*>(a.y)[(int64_t)m * a.n + n] = f32_to_bf16_rne(r);
+                        static_cast<uint16_t*>(a.y)[(int64_t)m * a.n + (MULTI ? out_col(a, n) : n)] = f32_to_bf16_rne(r);
                 }
             }
     }
@@ -870,12 +929,15 @@ constexpr int kXPitch = kChunkK + 8;        // LDS row pitch of an x window (bf1
 constexpr int kGenBlock = 1024;             // workspace words per generation word
 constexpr int kMaxParts = 8;                // largest split
 
-template <int C, int MT, int W, bool OUT_F32>
+template <int C, int MT, int W, bool OUT_F32, bool MULTI>
 __global__ void __launch_bounds__(64 * W)
 nvfp4_skinny_split(SplitArgs sa) {
     constexpr int kXLoads = (16 * MT + W - 1) / W;      // x rows one wavefront loads per window
     extern __shared__ __align__(16) uint16_t lds[];    // x windows [2][M][kXPitch] | chunk buffers
-    const Args& a = sa.a;
+    Args a_entry;
+    if constexpr (MULTI) a_entry = entry_args(sa.a);
+    const Args& a = MULTI ? a_entry : sa.a;
+    if (MULTI && a.m <= 0) return;                     // an empty entry: no part of it runs
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
     const int col_lane = lane % 16;
@@ -897,7 +959,7 @@ nvfp4_skinny_split(SplitArgs sa) {
     // block of its region per lane, the ones it advances at the end.
     constexpr int kSlot = W * C * MT * 4 * kWave;
     constexpr int kVals = C * MT * 4;
-    const int64_t region0 = (int64_t)cgroup * sa.region;
+    const int64_t region0 = ((MULTI ? (int64_t)blockIdx.y * sa.groups : 0) + cgroup) * sa.region;
     const int lrow = wave * kVals * kWave;
     auto blk = [&](int q, int i) { return (region0 + (int64_t)q * kSlot + lrow + i * kWave) / kGenBlock; };
     uint32_t glo[kMaxParts - 1] = {}, ghi[kMaxParts - 1] = {};
@@ -1129,9 +1191,9 @@ nvfp4_skinny_split(SplitArgs sa) {
                 if (m < a.m && n < a.n) {
                     float r = grp[c][t][j] * a.t;
                     if (OUT_F32)
-                        static_cast<float*>(a.y)[(int64_t)m * a.n + n] = r;
+                        static_cast<float*>(a.y)[(int64_t)m * a.n + (MULTI ? out_col(a, n) : n)] = r;
                     else
-                        static_cast<uint16_t*>(a.y)[(int64_t)m * a.n + n] = f32_to_bf16_rne(r);
+                        static_cast<uint16_t*>(a.y)[(int64_t)m * a.n + (MULTI ? out_col(a, n) : n)] = f32_to_bf16_rne(r);
                 }
             }
     }
@@ -1145,9 +1207,14 @@ size_t split_lds_bytes(int64_t m, int w, int c) {
 using KernelFn = void (*)(Args);
 using SplitFn = void (*)(SplitArgs);
 
+// y_dtype may carry kMulti: the instantiation of a several-product launch.
+constexpr int kMulti = 0x100;
+
 template <int C, int MT, int U, bool XLDS>
 KernelFn pick_out(int y_dtype) {
-    return y_dtype == NVFP4_OUT_F32 ? nvfp4_skinny<C, MT, U, XLDS, true> : nvfp4_skinny<C, MT, U, XLDS, false>;
+    const bool f = (y_dtype & 0xff) == NVFP4_OUT_F32;
+    if (y_dtype & kMulti) return f ? nvfp4_skinny<C, MT, U, XLDS, true, true> : nvfp4_skinny<C, MT, U, XLDS, false, true>;
+    return f ? nvfp4_skinny<C, MT, U, XLDS, true, false> : nvfp4_skinny<C, MT, U, XLDS, false, false>;
 }
 
 // Pipeline depth of the generic kernel, capped where deeper steps would spill
@@ -1184,8 +1251,10 @@ KernelFn pick_kernel(int mt, int cols, int unroll, bool xlds, int y_dtype) {
 
 template <int C, int MT, int NB>
 KernelFn pick_p_out(int y_dtype) {
-    return y_dtype == NVFP4_OUT_F32 ? nvfp4_skinny_persistent<C, MT, NB, true>
-                                    : nvfp4_skinny_persistent<C, MT, NB, false>;
+    const bool f = (y_dtype & 0xff) == NVFP4_OUT_F32;
+    if (y_dtype & kMulti)
+        return f ? nvfp4_skinny_persistent<C, MT, NB, true, true> : nvfp4_skinny_persistent<C, MT, NB, false, true>;
+    return f ? nvfp4_skinny_persistent<C, MT, NB, true, false> : nvfp4_skinny_persistent<C, MT, NB, false, false>;
 }
 
 template <int NB>
@@ -1201,7 +1270,9 @@ KernelFn pick_persistent(int mt, int c, int nb, int y_dtype) {
 
 template <int C, int MT, int NB>
 KernelFn pick_t_out(int y_dtype) {
-    return y_dtype == NVFP4_OUT_F32 ? nvfp4_skinny_tile<C, MT, NB, true> : nvfp4_skinny_tile<C, MT, NB, false>;
+    const bool f = (y_dtype & 0xff) == NVFP4_OUT_F32;
+    if (y_dtype & kMulti) return f ? nvfp4_skinny_tile<C, MT, NB, true, true> : nvfp4_skinny_tile<C, MT, NB, false, true>;
+    return f ? nvfp4_skinny_tile<C, MT, NB, true, false> : nvfp4_skinny_tile<C, MT, NB, false, false>;
 }
 
 template <int NB>
@@ -1217,7 +1288,9 @@ KernelFn pick_tile(int mt, int c, int nb, int y_dtype) {
 
 template <int C, int MT, int W>
 SplitFn pick_s_out(int y_dtype) {
-    return y_dtype == NVFP4_OUT_F32 ? nvfp4_skinny_split<C, MT, W, true> : nvfp4_skinny_split<C, MT, W, false>;
+    const bool f = (y_dtype & 0xff) == NVFP4_OUT_F32;
+    if (y_dtype & kMulti) return f ? nvfp4_skinny_split<C, MT, W, true, true> : nvfp4_skinny_split<C, MT, W, false, true>;
+    return f ? nvfp4_skinny_split<C, MT, W, true, false> : nvfp4_skinny_split<C, MT, W, false, false>;
 }
 
 template <int MT>
@@ -1298,7 +1371,7 @@ int setup_device(int dev) {
     // capture, and let each use the whole LDS.
     const int cols[3] = {16, 32, 64};
     for (int mt = 1; mt <= 2; ++mt)
-        for (int od = 0; od <= 1; ++od) {
+        for (int od : {int(NVFP4_OUT_BF16), int(NVFP4_OUT_F32), NVFP4_OUT_BF16 | kMulti, NVFP4_OUT_F32 | kMulti}) {
             for (int ci = 0; ci < 3; ++ci)
                 for (int un = 1; un <= 4; un *= 2)
                     for (int xl = 0; xl <= 1; ++xl)
@@ -1483,7 +1556,7 @@ struct SplitPlan {
 };
 
 bool plan_split(const nvfp4::Tile& tile, int64_t m, int64_t n, int64_t k, const Workspace* ws, bool whole,
-                SplitPlan* p) {
+                SplitPlan* p, int64_t count = 1) {
     const int64_t seg = k / tile.waves;
     if (seg % kChunkK != 0) return false;
     p->c = tile.cols == 16 ? 1 : 2;
@@ -1500,9 +1573,10 @@ bool plan_split(const nvfp4::Tile& tile, int64_t m, int64_t n, int64_t k, const 
         const int64_t slot = int64_t(p->w) * p->c * mt * 4 * kWave;     // words of one workgroup
         p->region = ((tile.split - 1) * slot + kGenBlock - 1) / kGenBlock * kGenBlock;
         if (!ws || !ws->sums) return false;
-        // the words, and one generation word per block of them
-        if (size_t(p->groups) * size_t(p->region) * sizeof(uint64_t) > ws->sum_bytes ||
-            size_t(p->groups) * size_t(p->region) / kGenBlock > ws->gen_words) {
+        // the words, and one generation word per block of them (regions of
+        // their own for each product of a several-product launch)
+        const size_t words = size_t(count) * size_t(p->groups) * size_t(p->region);
+        if (words * sizeof(uint64_t) > ws->sum_bytes || words / kGenBlock > ws->gen_words) {
             p->scratch_short = true;
             return false;
         }
@@ -1522,11 +1596,14 @@ std::string kernel_text(const char* fn, std::initializer_list<int> params, int y
     return s;
 }
 
-// Validates and launches one product; with `describe` set it launches
-// nothing and writes there the kernel it would run (pointers unchecked).
+// Validates and launches one product (or, with `ml`, the products of a
+// several-product launch, m then bounding every product's rows); with
+// `describe` set it launches nothing and writes there the kernel it would
+// run (pointers unchecked).  The pointers a device table holds are the
+// caller's to check.
 int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4m3, float tensor_scale,
            void* y, int64_t m, int64_t n, int64_t k, int y_dtype, void* stream, const nvfp4::Tile& tile,
-           int kernel, bool noalloc, std::string* describe = nullptr) {
+           int kernel, bool noalloc, std::string* describe = nullptr, const nvfp4::MultiLaunch* ml = nullptr) {
     int st = nvfp4_linear_shape_ok(m, n, k);
     if (st != NVFP4_OK) return st;
     if (y_dtype != NVFP4_OUT_BF16 && y_dtype != NVFP4_OUT_F32) return NVFP4_ERR_DTYPE;
@@ -1534,7 +1611,8 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
         if (describe) *describe = "none";
         return NVFP4_OK;
     }
-    if (!describe) {
+    const bool tabled = ml && ml->table;
+    if (!describe && !tabled) {
         if (!x_bf16 || !w_packed || !scales_e4m3 || !y) return NVFP4_ERR_NULL;
         auto misaligned = [](const void* p, uintptr_t al) { return (reinterpret_cast<uintptr_t>(p) & (al - 1)) != 0; };
         if (misaligned(x_bf16, 16) || misaligned(w_packed, 16) || misaligned(scales_e4m3, 16) ||
@@ -1553,7 +1631,7 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
     const Workspace* ws = noalloc ? &d.fixed : &d.heap;
 
     const int mt = m <= 16 ? 1 : 2;
-    Args a;
+    Args a{};
     a.x = static_cast<const uint16_t*>(x_bf16);
     a.wp = w_packed;
     a.sc = scales_e4m3;
@@ -1564,6 +1642,19 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
     a.k = static_cast<int>(k);
     a.k_per_wave = static_cast<int>(k / tile.waves);
     a.group = tile.waves / tile.split;
+    const unsigned count = ml ? static_cast<unsigned>(ml->count) : 1u;
+    const int yd = y_dtype | (ml ? kMulti : 0);   // the kernels' instantiation
+    if (ml) {
+        a.table = ml->table;
+        a.wp1 = ml->wp1;
+        a.sc1 = ml->sc1;
+        a.y1 = ml->y1;
+        a.t1 = ml->t1;
+        a.omap_parts = ml->omap_parts;
+        for (int i = 0; i < 4; ++i) a.omap_width[i] = ml->omap_width[i];
+        a.omap_gwidth = ml->omap_gwidth;
+        a.omap_ngroups = ml->omap_ngroups;
+    }
     const int c = tile.cols / 16;
     const hipStream_t hs = static_cast<hipStream_t>(stream);
 
@@ -1579,7 +1670,7 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
                          pers_bytes + 256 <= size_t(kMaxLdsBytes) && x_bytes <= size_t(64 * 1024);
     SplitPlan plan;
     const bool whole = kernel == NVFP4_KERNEL_WHOLE;
-    const bool split_ok = plan_split(tile, m, n, k, ws, whole, &plan);
+    const bool split_ok = plan_split(tile, m, n, k, ws, whole, &plan, count);
     if (whole) kernel = NVFP4_KERNEL_SPLIT;
     // The per-tile kernel: each wavefront's x slice and chunk buffers (up to
     // three, at most one per chunk of its segment) within the LDS: the most
@@ -1633,12 +1724,12 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
         const int64_t tiles = (n + tile.cols - 1) / tile.cols;
         const int per_cu = std::max(1, std::min(64 / tile.waves, int(kMaxLdsBytes / (pers_bytes + 256))));
         const int64_t grid_p = tiles < int64_t(per_cu) * cus ? tiles : int64_t(per_cu) * cus;
-        const dim3 grid(static_cast<unsigned>(grid_p)), block(static_cast<unsigned>(kWave * tile.waves));
+        const dim3 grid(static_cast<unsigned>(grid_p), count), block(static_cast<unsigned>(kWave * tile.waves));
         if (describe) {
             *describe = kernel_text("nvfp4_skinny_persistent", {pc, mt, pnb}, y_dtype, grid, block, pers_bytes);
             return NVFP4_OK;
         }
-        hipLaunchKernelGGL(pick_persistent(mt, pc, pnb, y_dtype), grid, block, pers_bytes, hs, a);
+        hipLaunchKernelGGL(pick_persistent(mt, pc, pnb, yd), grid, block, pers_bytes, hs, a);
     } else if (kernel == NVFP4_KERNEL_SPLIT) {
         SplitArgs sa;
         sa.a = a;
@@ -1651,21 +1742,22 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
         sa.spin_limit = g_test_split_timeout ? kTestSpinLimit : kSpinLimit;
         sa.test_mode = g_test_split_timeout;
         sa.groups = static_cast<int>(plan.groups);
-        const dim3 grid(static_cast<unsigned>(plan.groups * plan.parts)), block(static_cast<unsigned>(kWave * plan.w));
+        const dim3 grid(static_cast<unsigned>(plan.groups * plan.parts), count),
+            block(static_cast<unsigned>(kWave * plan.w));
         if (describe) {
             *describe = kernel_text("nvfp4_skinny_split", {plan.c, mt, plan.w}, y_dtype, grid, block, plan.lds) +
                         " parts=" + std::to_string(plan.parts);
             return NVFP4_OK;
         }
-        hipLaunchKernelGGL(pick_split(mt, plan.c, plan.w, y_dtype), grid, block, plan.lds, hs, sa);
+        hipLaunchKernelGGL(pick_split(mt, plan.c, plan.w, yd), grid, block, plan.lds, hs, sa);
     } else if (kernel == NVFP4_KERNEL_TILE) {
-        const dim3 grid(static_cast<unsigned>((n + 16 * pc - 1) / (16 * pc))),
+        const dim3 grid(static_cast<unsigned>((n + 16 * pc - 1) / (16 * pc)), count),
             block(static_cast<unsigned>(kWave * tile.waves));
         if (describe) {
             *describe = kernel_text("nvfp4_skinny_tile", {pc, mt, tnb}, y_dtype, grid, block, tile_bytes);
             return NVFP4_OK;
         }
-        hipLaunchKernelGGL(pick_tile(mt, pc, tnb, y_dtype), grid, block, tile_bytes, hs, a);
+        hipLaunchKernelGGL(pick_tile(mt, pc, tnb, yd), grid, block, tile_bytes, hs, a);
     } else {
         // The generic per-tile kernel (register loads, any shape); x goes
         // through LDS when it fits in 64 KB.  pick_kernel caps the pipeline
@@ -1673,14 +1765,14 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
         const bool xlds = x_bytes <= size_t(64 * 1024);
         const size_t part_bytes = tile.waves > 1 ? size_t(tile.waves) * c * mt * 4 * kWave * sizeof(float) : 0;
         const size_t lds = xlds && x_bytes > part_bytes ? x_bytes : part_bytes;
-        const dim3 grid(static_cast<unsigned>((n + tile.cols - 1) / tile.cols));
+        const dim3 grid(static_cast<unsigned>((n + tile.cols - 1) / tile.cols), count);
         const dim3 block(static_cast<unsigned>(kWave * tile.waves));
         if (describe) {
             *describe = kernel_text("nvfp4_skinny", {c, mt, generic_unroll(tile.unroll, c, xlds), xlds ? 1 : 0},
                                     y_dtype, grid, block, lds);
             return NVFP4_OK;
         }
-        hipLaunchKernelGGL(pick_kernel(mt, tile.cols, tile.unroll, xlds, y_dtype), grid, block, lds, hs, a);
+        hipLaunchKernelGGL(pick_kernel(mt, tile.cols, tile.unroll, xlds, yd), grid, block, lds, hs, a);
     }
     if (hipGetLastError() != hipSuccess) return NVFP4_ERR_HIP;
     return NVFP4_OK;
@@ -1707,6 +1799,17 @@ extern "C" int nvfp4_linear_noalloc(const void* x_bf16, const uint8_t* w_packed,
     return launch(x_bf16, w_packed, scales_e4m3, tensor_scale, y, m, n, k, y_dtype, stream,
                   nvfp4::tile_for(n, k), NVFP4_KERNEL_AUTO, true);
 }
+
+namespace nvfp4 {
+
+int launch_multi(const void* x, const uint8_t* wp, const uint8_t* sc, float t, void* y, int64_t m, int64_t n,
+                 int64_t k, int y_dtype, void* stream, const MultiLaunch& ml) {
+    if (load_tile_override() != NVFP4_OK) return NVFP4_ERR_TILEFILE;
+    return launch(x, wp, sc, t, y, m, n, k, y_dtype, stream, tile_for(n, k), NVFP4_KERNEL_AUTO, false, nullptr,
+                  &ml);
+}
+
+}  // namespace nvfp4
 
 extern "C" int nvfp4_launch_info(int64_t m, int64_t n, int64_t k, int y_dtype, char* buf, int64_t buflen) {
     if (!buf) return NVFP4_ERR_NULL;

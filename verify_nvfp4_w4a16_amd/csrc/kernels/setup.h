@@ -2,6 +2,9 @@
 #pragma once
 
 #include <cstddef>
+#include <cstdint>
+
+#include "nvfp4_w4a16.h"
 
 namespace nvfp4 {
 
@@ -25,5 +28,26 @@ int device_cus();
 // the current device's buffer for the many-row GEMM's per-group partial sums
 // (*part = NULL and *bytes = 0 when it could not be allocated) and its CU count.
 int gemm_partials(float** part, size_t* bytes, int* cus);
+
+// Several products of one (N, K) in one launch of the skinny kernels
+// (blockIdx.y picks one) and the de-interleaved store.
+struct MultiLaunch {
+    const nvfp4_group_t* table = nullptr;   // device table of `count` products, or NULL
+    int count = 1;                          // products in the launch
+    const uint8_t* wp1 = nullptr;           // without a table: product 1's weight over the same x
+    const uint8_t* sc1 = nullptr;
+    void* y1 = nullptr;
+    float t1 = 0.0f;
+    int omap_parts = 0;                     // de-interleaving parts per group (0: none)
+    int omap_width[4] = {0, 0, 0, 0};
+    int omap_gwidth = 0;
+    int omap_ngroups = 0;
+};
+
+// nvfp4_linear's dispatch and kernels for such a launch; m bounds every
+// product's rows.  Arguments are validated as nvfp4_linear does, except the
+// pointers inside a table.
+int launch_multi(const void* x, const uint8_t* wp, const uint8_t* sc, float t, void* y, int64_t m, int64_t n,
+                 int64_t k, int y_dtype, void* stream, const MultiLaunch& ml);
 
 }  // namespace nvfp4

@@ -263,12 +263,16 @@ int nvfp4_linear_dual(const void* x_bf16, const uint8_t* w_packed0, const uint8_
 
 /*
  * Device, asynchronous.  "Module ops" w4a16_gemv_silu_input: the product's
- * activation is silu(gate) * up, formed per element inside the kernel from
- * the bf16 gate [M, K] and up [M, K] (16-byte aligned): silu(g) = g / (1 +
- * exp(-g)) and the product with u in fp32, rounded once to bf16, then the
- * product of nvfp4_linear with that x (same bits as nvfp4_linear on it).
- * Needs M * (K + 8) * 2 <= 65536 (the activation is formed in LDS), else
- * SHAPE.  Errors: NULL, SHAPE, ALIGN, DTYPE, HIP, DEVICE, TILEFILE.
+ * activation is silu(gate) * up, formed per element from the bf16 gate
+ * [M, K] and up [M, K] (16-byte aligned): silu(g) = g / (1 + exp(-g)) and
+ * the product with u in fp32, rounded once to bf16, then the product of
+ * nvfp4_linear with that x (same bits as nvfp4_linear on it).  One call, two
+ * launches: a small kernel writes the activation (M * K * 2 bytes) to the
+ * device buffer nvfp4_init allocates, then nvfp4_linear runs on it; calls
+ * that use the device workspace must not overlap in time on one device.  If
+ * that buffer could not be allocated, one kernel forms the activation in its
+ * LDS instead, which needs M * (K + 8) * 2 <= 65536, else SHAPE.
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, HIP, DEVICE, TILEFILE.
  */
 int nvfp4_linear_silu_input(const void* gate_bf16, const void* up_bf16, const uint8_t* w_packed,
                             const uint8_t* scales_e4m3, float tensor_scale, void* y, int64_t m,

@@ -68,7 +68,7 @@ def _silu(gd, ud, w, m, out_dtype=torch.bfloat16):
 
 def test_silu_input_forms_the_activation_once_and_multiplies_it():
     k, n = 4096, 4096
-    m = 7                                            # the most rows whose activation fits the LDS at K = 4096
+    m = 32                                           # every row count of the contract
     g = workload.activations_bf16(m, k, 21)
     u = workload.activations_bf16(m, k, 22, outliers=True)
     gd, ud = upload_bits(g), upload_bits(u)
@@ -84,13 +84,14 @@ def test_silu_input_forms_the_activation_once_and_multiplies_it():
     assert np.all(np.abs(h_bits.astype(np.int32)[off] - h_ref.astype(np.int32)[off]) == 1)
     # the fused product equals nvfp4_linear on that activation, bit for bit
     w = Weight.from_f32(workload.weights_f32(n, k, 23))
-    for mm in (1, 3, 7):
+    for mm in (1, 3, 7, 8, 17, 32):
         y = _silu(gd, ud, w, mm)
         assert torch.equal(bits(y), bits(_linear(upload_bits(h_bits[:mm]), w, mm))), mm
-    check_parity(_silu(gd, ud, w, m), h_ref, w, label="silu input M=7")
-    # more rows than the LDS holds is refused
+    check_parity(_silu(gd, ud, w, m), h_ref, w, label="silu input M=32")
+    check_parity(_silu(gd, ud, w, 5, torch.float32), h_ref[:5], w, label="silu input M=5 fp32")
+    # more rows than the contract allows is refused
     st = nv.linear_silu_input_raw(gd.data_ptr(), ud.data_ptr(), w.wp.data_ptr(), w.sc.data_ptr(), w.t,
-                                  gd.data_ptr(), 8, n, k, nv.OUT_BF16, _s())
+                                  gd.data_ptr(), 33, n, k, nv.OUT_BF16, _s())
     assert st == nv.ERR_SHAPE
 
 

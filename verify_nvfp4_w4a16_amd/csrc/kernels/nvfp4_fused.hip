@@ -49,6 +49,23 @@ __device__ __forceinline__ uint16_t silu_mul(uint16_t g, uint16_t u) {
     return f32_to_bf16_rne(s * bf16_to_f32(u));
 }
 
+// The activation alone: h = bf16(silu(gate) * up), eight elements a thread.
+__global__ void __launch_bounds__(256)
+nvfp4_silu_mul_kernel(const uint16_t* gate, const uint16_t* up, uint16_t* h, int64_t vecs) {
+    const int64_t v = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (v >= vecs) return;
+    const u32x4 g = load16(gate + 8 * v);
+    const u32x4 u = load16(up + 8 * v);
+    uint16_t gv[8], uv[8], hv[8];
+    __builtin_memcpy(gv, &g, 16);
+    __builtin_memcpy(uv, &u, 16);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) hv[i] = silu_mul(gv[i], uv[i]);
+    u32x4 o;
+    __builtin_memcpy(&o, hv, 16);
+    *reinterpret_cast<u32x4*>(h + 8 * v) = o;
+}
+
 template <int U>
 struct FChunk {
     u32x4 w[U];
@@ -264,12 +281,30 @@ extern "C" int nvfp4_linear_silu_input(const void* gate_bf16, const void* up_bf1
                                        int64_t k, int y_dtype, void* stream) {
     int st = check_common(m, n, k, y_dtype);
     if (st != NVFP4_OK) return st;
-    if (size_t(m) * (k + 8) * sizeof(uint16_t) > kXLdsMax) return NVFP4_ERR_SHAPE;
     if (m == 0) return NVFP4_OK;
     if ((st = check_entry(gate_bf16, w_packed, scales_e4m3, y, y_dtype)) != NVFP4_OK) return st;
     if (!up_bf16) return NVFP4_ERR_NULL;
     if (misaligned(up_bf16, 16)) return NVFP4_ERR_ALIGN;
     if (nvfp4::load_tile_override() != NVFP4_OK) return NVFP4_ERR_TILEFILE;
+    // The activation first, into the device buffer nvfp4_init allocates
+    // (M * K * 2 bytes, at most its 64 MiB), then nvfp4_linear on it: the
+    // product's weights then stream through its direct-to-LDS kernels, which
+    // cannot form the activation themselves (an LDS store drains their loads).
+    float* buf = nullptr;
+    size_t bytes = 0;
+    int cus = 256;
+    if ((st = nvfp4::gemm_partials(&buf, &bytes, &cus)) != NVFP4_OK) return st;
+    if (buf && size_t(m) * size_t(k) * sizeof(uint16_t) <= bytes) {
+        uint16_t* h = reinterpret_cast<uint16_t*>(buf);
+        const int64_t vecs = m * k / 8;
+        hipLaunchKernelGGL(nvfp4_silu_mul_kernel, dim3(static_cast<unsigned>((vecs + 255) / 256)), dim3(256), 0,
+                           static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(gate_bf16),
+                           static_cast<const uint16_t*>(up_bf16), h, vecs);
+        if (hipGetLastError() != hipSuccess) return NVFP4_ERR_HIP;
+        return nvfp4_linear(h, w_packed, scales_e4m3, tensor_scale, y, m, n, k, y_dtype, stream);
+    }
+    // Without that buffer: one kernel forming the activation in its LDS.
+    if (size_t(m) * (k + 8) * sizeof(uint16_t) > kXLdsMax) return NVFP4_ERR_SHAPE;
     if ((st = nvfp4::device_setup()) != NVFP4_OK) return st;
     const nvfp4::Tile tile = nvfp4::tile_for(n, k);
     FusedArgs fa;

@@ -269,10 +269,9 @@ int nvfp4_linear_dual(const void* x_bf16, const uint8_t* w_packed0, const uint8_
  * nvfp4_linear with that x (same bits as nvfp4_linear on it).  One call, two
  * launches: a small kernel writes the activation (M * K * 2 bytes) to the
  * device buffer nvfp4_init allocates, then nvfp4_linear runs on it; calls
- * that use the device workspace must not overlap in time on one device.  If
- * that buffer could not be allocated, one kernel forms the activation in its
- * LDS instead, which needs M * (K + 8) * 2 <= 65536, else SHAPE.
- * Errors: NULL, SHAPE, ALIGN, DTYPE, HIP, DEVICE, TILEFILE.
+ * that use the device workspace must not overlap in time on one device.
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, HIP (also: the device buffer could not
+ * be allocated), DEVICE, TILEFILE.
  */
 int nvfp4_linear_silu_input(const void* gate_bf16, const void* up_bf16, const uint8_t* w_packed,
                             const uint8_t* scales_e4m3, float tensor_scale, void* y, int64_t m,

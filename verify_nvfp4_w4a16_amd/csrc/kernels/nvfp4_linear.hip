@@ -1387,7 +1387,6 @@ int setup_device(int dev) {
                     if (!allow_full_lds(pick_split(mt, c, w, od))) return NVFP4_ERR_HIP;
         }
     int st = nvfp4::gemm_setup();
-    if (st == NVFP4_OK) st = nvfp4::fused_setup();
     if (st == NVFP4_OK) st = nvfp4::w8a16_setup();
     if (st != NVFP4_OK) return st;
     // This device's copy of the fixed scratch array, by its device address.

@@ -15,9 +15,6 @@ int device_setup();
 // Kernel attributes of the many-row GEMM kernels (their LDS beyond 64 KB).
 int gemm_setup();
 
-// Kernel attributes of the fused and grouped kernels.
-int fused_setup();
-
 // Kernel attributes of the FP8 (W8A16) kernels.
 int w8a16_setup();
 

@@ -23,13 +23,14 @@ def test_init_reports_gfx950():
 def test_launch_info_names_the_dispatched_kernel():
     # The per-tile kernel at one row, the many-row kernel at 16 and 32 rows on
     # the decode round's shapes; the trace name carries the template
-    # arguments (column tiles, row tiles, buffers or wavefronts, output type).
+    # arguments (column tiles, row tiles, buffers or wavefronts, output type,
+    # several-product launch).
     for n, k in ((8192, 4096), (4096, 8192), (24576, 4096), (4096, 12288)):
         assert nv.kernel_name(1, n, k).startswith("nvfp4_skinny_tile<1, 1, ")
         assert nv.kernel_name(16, n, k).startswith("nvfp4_skinny_split<1, 1, ")
         assert nv.kernel_name(32, n, k).startswith("nvfp4_skinny_split<1, 2, ")
-        assert nv.kernel_name(32, n, k).endswith(", false>")
-    assert nv.kernel_name(1, 151552, 4096, nv.OUT_F32).endswith(", true>")
+        assert nv.kernel_name(32, n, k).endswith(", false, false>")
+    assert nv.kernel_name(1, 151552, 4096, nv.OUT_F32).endswith(", true, false>")
     assert nv.launch_info(0, 8192, 4096) == "none"
     info = nv.launch_info(32, 8192, 4096)
     assert " grid=" in info and " block=" in info and " parts=4" in info

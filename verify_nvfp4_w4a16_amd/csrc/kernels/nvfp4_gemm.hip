@@ -114,7 +114,11 @@ nvfp4_gemm_kernel(GemmArgs a) {
     // M - 1, never stored)
     const int xr0 = tid / 16, xp = tid % 16;
     const uint16_t* xsrc0 = a.x + 8 * xp;
-    const int xdst0 = xr0 * kPitch + 8 * xp;
+    // The 32-k quarter q of row r sits at slot (q + r / 4) % 4 of the row:
+    // with the row pitch 4 banks apart, the A reads of 16 rows x 4 quarters
+    // would otherwise meet in the same banks (same rotation as the skinny
+    // kernels' x windows).
+    const int xdst0 = xr0 * kPitch + 32 * ((xp / 4 + xr0 / 4) % 4) + 8 * (xp % 4);
     const bool xfull = row0 + kRows <= a.m;
     auto xrow_of = [&](int i) { return (int64_t)(xfull ? row0 + xr0 + 16 * i : min(row0 + xr0 + 16 * i, a.m - 1)); };
 
@@ -186,7 +190,8 @@ nvfp4_gemm_kernel(GemmArgs a) {
 #pragma unroll
             for (int t = 0; t < kMT; ++t) {
                 const int r = wm * 16 * kMT + 16 * t + col_lane;
-                const bf16x8 xa = as_bf16x8(*reinterpret_cast<const u32x4*>(xb + r * kPitch + 32 * kq + 8 * s));
+                const bf16x8 xa = as_bf16x8(
+                    *reinterpret_cast<const u32x4*>(xb + r * kPitch + 32 * ((kq + col_lane / 4) % 4) + 8 * s));
 #pragma unroll
                 for (int c = 0; c < kC; ++c)
                     acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bv[c], acc[t][c], 0, 0, 0);

@@ -1590,7 +1590,7 @@ std::string kernel_text(const char* fn, std::initializer_list<int> params, int y
     std::string s = fn;
     s += "<";
     for (int v : params) s += std::to_string(v) + ", ";
-    s += y_dtype == NVFP4_OUT_F32 ? "true>" : "false>";
+    s += y_dtype == NVFP4_OUT_F32 ? "true, false>" : "false, false>";   // output type; not a several-product launch
     s += " grid=" + std::to_string(grid.x) + " block=" + std::to_string(block.x) + " lds=" + std::to_string(lds);
     return s;
 }

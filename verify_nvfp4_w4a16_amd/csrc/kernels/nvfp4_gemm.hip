@@ -223,7 +223,7 @@ nvfp4_gemm_kernel(GemmArgs a) {
     }
 
     if (a.parts > 1) {
-        // one group's sum per output; nvfp4_gemm_reduce adds the groups in order
+        // one group's sum per output; launch_ordered_sum adds the groups in order
         float* dst = a.part + (int64_t)blockIdx.z * a.m * a.n;
 #pragma unroll
         for (int t = 0; t < kMT; ++t)
@@ -257,9 +257,9 @@ nvfp4_gemm_kernel(GemmArgs a) {
         }
 }
 
-// The group sums of a K-split GEMM [parts][M][N] added in group order (the
-// second level of the tile's order), times t, one rounding: each thread four
-// consecutive outputs of the flattened [M][N].
+// The group sums of a K-split product [parts][M][N] added in group order
+// (the second level of the tile's order), times t, one rounding: each thread
+// four consecutive outputs of the flattened [M][N].
 template <bool OUT_F32>
 __global__ void __launch_bounds__(256)
 nvfp4_gemm_reduce(const float* part, int parts, int64_t mn, float t, void* y) {
@@ -371,20 +371,21 @@ int gemm_launch(const void* x, const void* w, const uint8_t* scales, float t, vo
                     static_cast<unsigned>(a.parts));
     hipLaunchKernelGGL(pick_gemm(bf16w, y_dtype), grid, dim3(kThreads), kGemmLds, static_cast<hipStream_t>(stream), a);
     if (hipGetLastError() != hipSuccess) return NVFP4_ERR_HIP;
-    if (a.parts > 1) {
-        const int64_t mn = m * n;
-        const int64_t blocks = (mn + 1023) / 1024;
-        auto red = y_dtype == NVFP4_OUT_F32 ? nvfp4_gemm_reduce<true> : nvfp4_gemm_reduce<false>;
-        hipLaunchKernelGGL(red, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream),
-                           static_cast<const float*>(a.part), a.parts, mn, t, y);
-        if (hipGetLastError() != hipSuccess) return NVFP4_ERR_HIP;
-    }
+    if (a.parts > 1) return nvfp4::launch_ordered_sum(a.part, a.parts, m * n, t, y, y_dtype, stream);
     return NVFP4_OK;
 }
 
 }  // namespace
 
 namespace nvfp4 {
+
+int launch_ordered_sum(const float* part, int parts, int64_t mn, float t, void* y, int y_dtype, void* stream) {
+    const int64_t blocks = (mn + 1023) / 1024;
+    auto red = y_dtype == NVFP4_OUT_F32 ? nvfp4_gemm_reduce<true> : nvfp4_gemm_reduce<false>;
+    hipLaunchKernelGGL(red, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       part, parts, mn, t, y);
+    return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
 
 int gemm_setup() {
     for (int bw = 0; bw <= 1; ++bw)

@@ -26,6 +26,10 @@ int device_cus();
 // (*part = NULL and *bytes = 0 when it could not be allocated) and its CU count.
 int gemm_partials(float** part, size_t* bytes, int* cus);
 
+// y[i] = t * (((part[0][i] + part[1][i]) + part[2][i]) + ...), i < mn, rounded
+// once to y_dtype: the group sums of a K-split product added in group order.
+int launch_ordered_sum(const float* part, int parts, int64_t mn, float t, void* y, int y_dtype, void* stream);
+
 // Several products of one (N, K) in one launch of the skinny kernels
 // (blockIdx.y picks one) and the de-interleaved store.
 struct MultiLaunch {

@@ -36,6 +36,8 @@ struct W8Args {
     int m, n, k;
     int k_per_wave;        // segment length, a multiple of 128
     int group;             // segments per segment group
+    float* part;           // parts > 1: group sums [parts][M][N]; workgroup (x, y) runs group y
+    int parts;
 };
 
 // Eight e4m3 codes (two dwords) as the bf16 B operand, exactly.
@@ -148,7 +150,7 @@ fp8_w8a16_kernel(W8Args a) {
                 for (int j = 0; j < 4; ++j) acc[c][t][j] = __builtin_fmaf(ch.s, blk[c][t][j], acc[c][t][j]);
     };
 
-    const int k0 = wave * a.k_per_wave;
+    const int k0 = ((int)blockIdx.y * waves + wave) * a.k_per_wave;   // blockIdx.y > 0 only when K is split
     const int nchunks = a.k_per_wave / kFp8Block;
     W8Chunk<MT, C, XLDS> A, B;
     load(A, k0);
@@ -201,6 +203,10 @@ fp8_w8a16_kernel(W8Args a) {
                 for (int t = 0; t < MT; ++t) acc[c][t] = tot[c][t] + acc[c][t];
         }
     }
+    // this workgroup's group sum, when the groups are added by a second kernel
+    void* out = a.y;
+    const bool part_out = a.parts > 1;
+    if (part_out) out = a.part + (int64_t)blockIdx.y * a.m * a.n;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
         const int n = col_base + 16 * c + col_lane;
@@ -209,7 +215,9 @@ fp8_w8a16_kernel(W8Args a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int m = 16 * t + 4 * kq + j;
-                if (m < a.m) {
+                if (m < a.m && part_out) {
+                    static_cast<float*>(out)[(int64_t)m * a.n + n] = acc[c][t][j];
+                } else if (m < a.m) {
                     if (OUT_F32)
                         static_cast<float*>(a.y)[(int64_t)m * a.n + n] = acc[c][t][j];
                     else
@@ -290,17 +298,49 @@ extern "C" int fp8_w8a16_linear(const void* x_bf16, const uint8_t* w_e4m3, const
     fp8_tile(n, k, &waves, &group);
     a.k_per_wave = static_cast<int>(k / waves);
     a.group = group;
+    a.part = nullptr;
+    a.parts = 1;
     const int mt = m <= 16 ? 1 : 2;
     const size_t x_bytes = size_t(m) * (k + 8) * sizeof(uint16_t);
     const bool xlds = x_bytes <= kXLdsMax;
-    // Where x is read from memory, two column tiles per wavefront halve its
-    // reads, if that still leaves a workgroup for every CU (measured on
-    // MI355X at 16 and 32 rows: 1.1-1.3x faster on 8192 and 24576 columns;
-    // four tiles were 2-9 % slower than two on 24576 columns).
-    const int c = !xlds && n / 32 >= nvfp4::device_cus() ? 2 : 1;
-    const size_t part_bytes = waves > 1 ? size_t(waves) * c * mt * 4 * kWave * sizeof(float) : 0;
+    // Where x is read from memory each workgroup reads its x slice once for
+    // its 16 c columns: two column tiles per wavefront halve those reads
+    // where 32-column workgroups still cover the CUs.  Where they do not and
+    // there are two row tiles (x reads largest), K is split into the tile's
+    // segment groups instead, one per workgroup, their sums added in order
+    // by a second kernel through the buffer nvfp4_init allocates (same bits).
+    // Measured on MI355X at 16 and 32 rows on the decode round's shapes:
+    // two tiles 1.1-1.3x faster on 8192 and 24576 columns; the split with two
+    // tiles 1.04-1.14x faster on 4096 columns at 32 rows and no faster
+    // elsewhere; four tiles never faster than two.
+    int c = 1, parts = 1;
+    float* buf = nullptr;
+    if (!xlds) {
+        const int cus = nvfp4::device_cus();
+        const int split = waves / group;
+        if (n / 32 >= cus) {
+            c = 2;
+        } else if (mt == 2 && split > 1 && (n / 32) * split >= cus) {
+            size_t bytes = 0;
+            int cus2 = cus;
+            st = nvfp4::gemm_partials(&buf, &bytes, &cus2);
+            if (st != NVFP4_OK) return st;
+            if (buf && size_t(split) * size_t(m) * size_t(n) * 4 <= bytes) {
+                c = 2;
+                parts = split;
+            }
+        }
+    }
+    const int wg_waves = waves / parts;
+    if (parts > 1) {
+        a.part = buf;
+        a.parts = parts;
+    }
+    const size_t part_bytes = wg_waves > 1 ? size_t(wg_waves) * c * mt * 4 * kWave * sizeof(float) : 0;
     const size_t lds = xlds && x_bytes > part_bytes ? x_bytes : part_bytes;
-    hipLaunchKernelGGL(pick_w8(mt, c, xlds, y_dtype), dim3(static_cast<unsigned>(n / (16 * c))),
-                       dim3(static_cast<unsigned>(kWave * waves)), lds, static_cast<hipStream_t>(stream), a);
-    return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+    hipLaunchKernelGGL(pick_w8(mt, c, xlds, y_dtype), dim3(static_cast<unsigned>(n / (16 * c)), parts),
+                       dim3(static_cast<unsigned>(kWave * wg_waves)), lds, static_cast<hipStream_t>(stream), a);
+    if (hipGetLastError() != hipSuccess) return NVFP4_ERR_HIP;
+    if (parts > 1) return nvfp4::launch_ordered_sum(buf, parts, m * n, 1.0f, y, y_dtype, stream);
+    return NVFP4_OK;
 }

@@ -314,7 +314,9 @@ typedef struct nvfp4_group {
  * stream passes the call.  max_m (0..32) bounds every entry's m; rows of an
  * entry past max_m are not computed.  Each output has the bits nvfp4_linear
  * gives it: nvfp4_linear's kernels, sized for max_m, run with the entry
- * picked per workgroup (same workspace rule).  Entry pointers are not checked
+ * picked per workgroup (same workspace rule; where the many-row kernel's
+ * exchange for every entry would not fit the workspace, another kernel of
+ * the same tile runs).  Entry pointers are not checked
  * on the host (they are in device memory): they must satisfy nvfp4_linear's
  * contract.
  * Errors: NULL, SHAPE (also count > 65535), ALIGN, DTYPE, HIP, DEVICE, TILEFILE.

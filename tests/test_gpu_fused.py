@@ -140,3 +140,24 @@ def test_grouped_launch_over_a_device_table():
             continue
         assert torch.equal(bits(ys[e]), bits(_linear(xs[e], ws[e], m, torch.float32))), e
     check_parity(ys[-1], workload.activations_bf16(32, k, 50 + len(rows) - 1), ws[-1], label="grouped expert M=32")
+
+
+def test_grouped_launch_beyond_the_exchange_workspace():
+    # Forty experts at up to 17 rows: the many-row kernel's exchange regions
+    # for every expert would not fit the device workspace, so the launch runs
+    # another kernel of the same tile; each expert's rows still have the bits
+    # nvfp4_linear gives them alone (where the exchange fits).
+    n, k, count = 1536, 4096, 40
+    w = Weight.from_f32(workload.weights_f32(n, k, 60))
+    rows = [17 - (e % 17) for e in range(count)]
+    xs = [upload_bits(workload.activations_bf16(m, k, 61 + e)) for e, m in enumerate(rows)]
+    ys = [torch.empty((m, n), dtype=torch.bfloat16, device=DEV) for m in rows]
+    rec = np.zeros(count, dtype=nv.GROUP_DTYPE)
+    for e, m in enumerate(rows):
+        rec[e] = (xs[e].data_ptr(), w.wp.data_ptr(), w.sc.data_ptr(), ys[e].data_ptr(), w.t, m)
+    table = upload_u8(rec.view(np.uint8))
+    st = nv.linear_grouped_raw(table.data_ptr(), count, max(rows), n, k, nv.OUT_BF16, _s())
+    torch.cuda.synchronize()
+    assert st == nv.OK
+    for e in (0, 1, 16, 17, 39):
+        assert torch.equal(bits(ys[e]), bits(_linear(xs[e], w, rows[e]))), e

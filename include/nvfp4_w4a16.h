@@ -108,12 +108,15 @@ int nvfp4_linear_shape_ok(int64_t m, int64_t n, int64_t k);
  * MiB of tagged partial sums plus 16 KiB of generation words in device
  * memory, zeroed once and kept until the process ends (the many-row
  * kernel exchanges segment-group sums through it; generations only advance,
- * so it is never cleared again), and 64 MiB for the group sums of a K-split
- * nvfp4_gemm (written in full before they are read).  Call on every device before capturing
- * nvfp4_linear into a HIP graph; the first nvfp4_linear call on a device runs
+ * so it is never cleared again), and a 64 MiB buffer, written in full before
+ * it is read by every call that uses it: the group sums of a K-split
+ * nvfp4_gemm or fp8_w8a16_linear, the activation of nvfp4_linear_silu_input.
+ * Call on every device before capturing any of this library's device calls
+ * into a HIP graph; the first call on a device that needs the workspace runs
  * it otherwise.  Safe to call more than once.  If the workspace cannot be
- * allocated, nvfp4_linear still works (with kernels that do not need it) and
- * gives the same bits.
+ * allocated, nvfp4_linear, nvfp4_gemm and fp8_w8a16_linear still work (with
+ * kernels that do not need it) and give the same bits; the silu input then
+ * fails with HIP.
  * Test hook, read once per process: NVFP4_TEST_SPLIT_TIMEOUT=1 makes the
  * many-row kernel's producer workgroups store no partial sums, =2 makes them
  * store them only after a long bounded delay; with either, its consumers give

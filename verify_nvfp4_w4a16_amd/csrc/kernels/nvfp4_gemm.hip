@@ -46,7 +46,7 @@ constexpr int kThreads = 256;
 constexpr int kPitch = kBlockK + 8;     // LDS row pitch of an x block, bf16 elements
 constexpr int kXVec = kRows * kBlockK / 8 / kThreads;   // 16-byte x pieces per thread per block
 constexpr size_t kGemmLds = 2 * size_t(kRows) * kPitch * sizeof(uint16_t);
-constexpr int64_t kChunkedMaxM = 96;    // nvfp4_matmul: 32-row slices of the skinny product up to here
+constexpr int64_t kChunkedMaxM = 128;   // nvfp4_matmul: 32-row slices of the skinny product up to here
 
 struct GemmArgs {
     const uint16_t* x;      // bf16 [M, K]
@@ -434,19 +434,16 @@ extern "C" int nvfp4_matmul(const void* x_bf16, const uint8_t* w_packed, const u
     if (st != NVFP4_OK) return st;
     if (m > kChunkedMaxM)
         return nvfp4_gemm(x_bf16, w_packed, scales_e4m3, tensor_scale, y, m, n, k, y_dtype, stream);
-    // 33..96 rows: the skinny product on 32-row slices (same bits), which
-    // streams the weight at a few TB/s per slice where the 128-row GEMM tile
-    // leaves most CUs idle (measured on MI355X at 64 rows: 22-42 us against
-    // 31-72 us for the K-split GEMM on the decode round's shapes; at 128 rows
-    // the two are within 10 %).
-    if (y_dtype != NVFP4_OUT_BF16 && y_dtype != NVFP4_OUT_F32) return NVFP4_ERR_DTYPE;
-    if (!x_bf16 || !y) return NVFP4_ERR_NULL;
-    const size_t ysize = y_dtype == NVFP4_OUT_F32 ? 4 : 2;
-    for (int64_t r0 = 0; r0 < m; r0 += NVFP4_MAX_M) {
-        const int64_t rows = std::min<int64_t>(NVFP4_MAX_M, m - r0);
-        st = nvfp4_linear(static_cast<const uint16_t*>(x_bf16) + r0 * k, w_packed, scales_e4m3, tensor_scale,
-                          static_cast<uint8_t*>(y) + r0 * n * ysize, rows, n, k, y_dtype, stream);
-        if (st != NVFP4_OK) return st;
-    }
-    return NVFP4_OK;
+    // 33..128 rows: the skinny product's kernels on 32-row slices, all slices
+    // in one launch (blockIdx.y picks the slice; same bits), which stream the
+    // weight at a few TB/s where the 128-row GEMM tile leaves most CUs idle
+    // (measured on MI355X on the decode round's shapes: 21-41 us at 64 rows
+    // against 30-73 us for the GEMM; even at 128 rows; the GEMM ahead from
+    // 192 rows on three of the four).
+    nvfp4::MultiLaunch ml;
+    ml.slice_rows = NVFP4_MAX_M;
+    ml.rows_total = static_cast<int>(m);
+    ml.count = static_cast<int>((m + NVFP4_MAX_M - 1) / NVFP4_MAX_M);
+    return nvfp4::launch_multi(x_bf16, w_packed, scales_e4m3, tensor_scale, y, NVFP4_MAX_M, n, k, y_dtype, stream,
+                               ml);
 }

@@ -78,6 +78,11 @@ struct Args {
     int omap_width[4];
     int omap_gwidth;
     int omap_ngroups;
+    // Row slices of one product (slice_rows > 0): product e is rows
+    // [e * slice_rows, e * slice_rows + slice_rows) of x and y, of rows_total.
+    int slice_rows;
+    int rows_total;
+    int y_bytes;           // bytes per output element (2 or 4)
 };
 
 // The product of this workgroup (blockIdx.y) in a several-product launch;
@@ -92,6 +97,11 @@ __device__ __forceinline__ Args entry_args(const Args& in) {
         a.y = g.y;
         a.t = g.tensor_scale;
         a.m = min(g.m, in.m);
+    } else if (in.slice_rows > 0) {
+        const int r0 = static_cast<int>(blockIdx.y) * in.slice_rows;
+        a.x = in.x + (int64_t)r0 * in.k;
+        a.y = static_cast<uint8_t*>(in.y) + (int64_t)r0 * in.n * in.y_bytes;
+        a.m = min(in.slice_rows, in.rows_total - r0);
     } else if (blockIdx.y == 1) {
         a.wp = in.wp1;
         a.sc = in.sc1;
@@ -1653,6 +1663,9 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
         for (int i = 0; i < 4; ++i) a.omap_width[i] = ml->omap_width[i];
         a.omap_gwidth = ml->omap_gwidth;
         a.omap_ngroups = ml->omap_ngroups;
+        a.slice_rows = ml->slice_rows;
+        a.rows_total = ml->rows_total;
+        a.y_bytes = y_dtype == NVFP4_OUT_F32 ? 4 : 2;
     }
     const int c = tile.cols / 16;
     const hipStream_t hs = static_cast<hipStream_t>(stream);

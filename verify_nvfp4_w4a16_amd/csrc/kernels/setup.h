@@ -31,7 +31,8 @@ int gemm_partials(float** part, size_t* bytes, int* cus);
 int launch_ordered_sum(const float* part, int parts, int64_t mn, float t, void* y, int y_dtype, void* stream);
 
 // Several products of one (N, K) in one launch of the skinny kernels
-// (blockIdx.y picks one) and the de-interleaved store.
+// (blockIdx.y picks one: a table row, a second weight over the same x, or a
+// slice of rows of one product) and the de-interleaved store.
 struct MultiLaunch {
     const nvfp4_group_t* table = nullptr;   // device table of `count` products, or NULL
     int count = 1;                          // products in the launch
@@ -43,6 +44,8 @@ struct MultiLaunch {
     int omap_width[4] = {0, 0, 0, 0};
     int omap_gwidth = 0;
     int omap_ngroups = 0;
+    int slice_rows = 0;                     // row slices of one product: count slices of x and y
+    int rows_total = 0;                     // rows of that product (m is then the slice's rows)
 };
 
 // nvfp4_linear's dispatch and kernels for such a launch; m bounds every

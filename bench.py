@@ -371,10 +371,43 @@ def next_rows(torch, dev, stream) -> dict:
                                                             y.data_ptr(), m, n, k, nv.OUT_BF16, h)) * 1e3
     us_gemm = timed_graph(torch, stream, lambda h: call(nv.gemm_raw, x.data_ptr(), wp0.data_ptr(), sc0.data_ptr(), t,
                                                         y.data_ptr(), m, n, k, nv.OUT_BF16, h)) * 1e3
+    # the library GEMM: its first call (handle, workspace, plan) outside capture
+    call(nv.gemm_library_raw, x.data_ptr(), wbf.data_ptr(), t, y.data_ptr(), m, n, k, nv.OUT_BF16,
+         stream.cuda_stream)
+    torch.cuda.synchronize()
+    us_lib = timed_graph(torch, stream, lambda h: call(nv.gemm_library_raw, x.data_ptr(), wbf.data_ptr(), t,
+                                                       y.data_ptr(), m, n, k, nv.OUT_BF16, h)) * 1e3
     out["expand_8192x4096_M4096"] = {"expand_us": us_expand, "expand_GBps_read_plus_write":
                                      (wb + 2 * n * k) / (us_expand * 1e-6) / 1e9,
                                      "gemm_expanded_us": us_exp_gemm, "gemm_nvfp4_us": us_gemm,
-                                     "gemm_expanded_TFLOPs": 2.0 * m * n * k / (us_exp_gemm * 1e-6) / 1e12}
+                                     "gemm_expanded_TFLOPs": 2.0 * m * n * k / (us_exp_gemm * 1e-6) / 1e12,
+                                     "gemm_library_us": us_lib,
+                                     "gemm_library_TFLOPs": 2.0 * m * n * k / (us_lib * 1e-6) / 1e12}
+    # the library GEMM on the decode round's shapes at 1024 and 4096 rows
+    # against nvfp4_gemm (one weight, warm: both reread it per row tile)
+    lib_rows = {}
+    for s in workload.ROUND_SHAPES:
+        wp1, sc1, t1, _ = nvfp4_weight(s.n, s.k, 11)
+        wbf1 = torch.empty((s.n, s.k), dtype=torch.bfloat16, device=dev)
+        call(nv.dequant_bf16_raw, wp1.data_ptr(), sc1.data_ptr(), t1, 0, wbf1.data_ptr(), s.n, s.k,
+             stream.cuda_stream)
+        for mm in (1024, 4096):
+            x1 = xs(mm, s.k, 12)
+            y1 = torch.empty((mm, s.n), dtype=torch.bfloat16, device=dev)
+            call(nv.gemm_library_raw, x1.data_ptr(), wbf1.data_ptr(), t1, y1.data_ptr(), mm, s.n, s.k,
+                 nv.OUT_BF16, stream.cuda_stream)
+            torch.cuda.synchronize()
+            ul = timed_graph(torch, stream, lambda h: call(nv.gemm_library_raw, x1.data_ptr(), wbf1.data_ptr(), t1,
+                                                           y1.data_ptr(), mm, s.n, s.k, nv.OUT_BF16, h)) * 1e3
+            ug = timed_graph(torch, stream, lambda h: call(nv.gemm_raw, x1.data_ptr(), wp1.data_ptr(),
+                                                           sc1.data_ptr(), t1, y1.data_ptr(), mm, s.n, s.k,
+                                                           nv.OUT_BF16, h)) * 1e3
+            fl = 2.0 * mm * s.n * s.k
+            lib_rows[f"{s.n}x{s.k}_M{mm}"] = {"library_us": ul, "nvfp4_gemm_us": ug,
+                                               "library_TFLOPs": fl / (ul * 1e-6) / 1e12,
+                                               "nvfp4_gemm_TFLOPs": fl / (ug * 1e-6) / 1e12}
+        del wbf1
+    out["library_gemm"] = lib_rows
     del wbf
 
     fused = {}

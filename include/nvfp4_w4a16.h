@@ -53,7 +53,8 @@ enum {
     NVFP4_ERR_TILEFILE = -9,  /* the NVFP4_TILES override file is unreadable or invalid */
     NVFP4_ERR_BUFFER = -10,   /* nvfp4_tile_info: the text buffer is too small */
     NVFP4_ERR_TILE = -11,     /* nvfp4_linear_tiled: the tile does not fit the shape */
-    NVFP4_ERR_SCRATCH = -12   /* nvfp4_linear_noalloc: the call needs more than the fixed scratch */
+    NVFP4_ERR_SCRATCH = -12,  /* nvfp4_linear_noalloc: the call needs more than the fixed scratch */
+    NVFP4_ERR_LIBRARY = -13   /* nvfp4_gemm_library: the GEMM library reported an error */
 };
 
 /* Largest row count of one nvfp4_linear call. */
@@ -439,6 +440,26 @@ int nvfp4_dequant_bf16(const uint8_t* w_packed, const uint8_t* scales_e4m3, floa
  */
 int nvfp4_gemm_expanded(const void* x_bf16, const void* w_bf16, float tensor_scale, void* y,
                         int64_t m, int64_t n, int64_t k, int y_dtype, void* stream);
+
+/*
+ * Device, asynchronous on `stream`.  The third regime of "10 Kernels" 10.2 as
+ * the pages run it (expand to BF16 once, then the platform's library GEMM):
+ * y = t * x @ w_bf16^T through hipBLASLt, bf16 operands, fp32 accumulation,
+ * t applied to the fp32 sum, one rounding to y's type.  Arguments, layouts
+ * and the shape contract as nvfp4_gemm_expanded (w_bf16 from
+ * nvfp4_dequant_bf16 with apply_tensor_scale = 0).  The library picks its own
+ * kernel and K order per shape, so the bits are not nvfp4_gemm's and a row
+ * may differ in its last bits between row counts (within the same error
+ * bound); repeated calls of one shape give the same bits.  The first call on
+ * a device creates the library handle and a 32 MiB workspace (hipMalloc), the
+ * first call of each (M, N, K, y_dtype) builds its plan (host only); both are
+ * kept until the process ends, so make those calls before capturing a graph.
+ * Calls on one device that overlap in time share the workspace: keep them on
+ * one stream.
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, HIP, DEVICE, LIBRARY.
+ */
+int nvfp4_gemm_library(const void* x_bf16, const void* w_bf16, float tensor_scale, void* y,
+                       int64_t m, int64_t n, int64_t k, int y_dtype, void* stream);
 
 /*
  * Host.  Writes into buf (NUL-terminated) the kernel nvfp4_linear launches for

@@ -63,6 +63,7 @@ def test_header_constants_match_binding():
                   (nv.ERR_HIP, "NVFP4_ERR_HIP"), (nv.ERR_DEVICE, "NVFP4_ERR_DEVICE"),
                   (nv.ERR_TILEFILE, "NVFP4_ERR_TILEFILE"), (nv.ERR_BUFFER, "NVFP4_ERR_BUFFER"),
                   (nv.ERR_TILE, "NVFP4_ERR_TILE"), (nv.ERR_SCRATCH, "NVFP4_ERR_SCRATCH"),
+                  (nv.ERR_LIBRARY, "NVFP4_ERR_LIBRARY"),
                   (nv.OUT_BF16, "NVFP4_OUT_BF16"), (nv.OUT_F32, "NVFP4_OUT_F32")]:
         assert enum(c) == py, c
     assert int(re.search(r"#define NVFP4_MAX_M (\d+)", text).group(1)) == nv.MAX_M
@@ -216,11 +217,11 @@ def test_tile_struct_matches_the_header():
 
 def test_strerror_covers_every_status():
     seen = set()
-    for st in range(-12, 1):
+    for st in range(-13, 1):
         msg = nv.strerror(st)
         assert msg and msg != "unknown status"
         seen.add(msg)
-    assert len(seen) == 13
+    assert len(seen) == 14
     assert nv.strerror(-99) == "unknown status"
 
 

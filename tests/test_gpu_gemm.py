@@ -1,7 +1,8 @@
 """The many-row regime (nvfp4_gemm), the expand-to-bf16 regime
-(nvfp4_dequant_bf16 + nvfp4_gemm_expanded) and the row-count dispatcher
-(nvfp4_matmul) on the GPU: parity with the fp64 oracle, bit-exact expansion,
-and every row's bits equal to nvfp4_linear's for the same row (gpu)."""
+(nvfp4_dequant_bf16 + nvfp4_gemm_expanded, or + nvfp4_gemm_library) and the
+row-count dispatcher (nvfp4_matmul) on the GPU: parity with the fp64 oracle,
+bit-exact expansion, and every row's bits equal to nvfp4_linear's for the
+same row, except on the library GEMM, which picks its own K order (gpu)."""
 import numpy as np
 import pytest
 import torch
@@ -147,6 +148,71 @@ def test_expanded_gemm_equals_gemm():
         torch.cuda.synchronize()
         assert st == nv.OK
         assert torch.equal(bits(y), ref), (n, k, m)
+
+
+def _library(xd, wbf, w, m, od=nv.OUT_BF16):
+    y = torch.empty((m, w.n), dtype=torch.float32 if od == nv.OUT_F32 else torch.bfloat16, device=DEV)
+    st = nv.gemm_library_raw(xd.data_ptr(), wbf.data_ptr(), w.t, y.data_ptr(), m, w.n, w.k, od, _stream())
+    torch.cuda.synchronize()
+    assert st == nv.OK, st
+    return y
+
+
+def test_library_gemm_parity_and_repeatability():
+    # Expand once, then the library GEMM: within the oracle's tolerance (bf16
+    # and fp32 outputs) on sampled columns of large and ragged shapes, and the
+    # same bits on a second call of the same shape.
+    for n, k, m in [(8192, 4096, 1536), (4136, 4096, 70), (333, 1024, 200), (24576, 4096, 33)]:
+        w = Weight.from_f32(workload.weights_f32(n, k, n + m + 1))
+        x = workload.activations_bf16(m, k, 93 + m)
+        xd = upload_bits(x)
+        wbf = _expanded(w, False)
+        cols = np.unique(np.concatenate([np.arange(8), np.arange(n - 8, n), workload.rng(n).integers(0, n, 64)]))
+        for od in (nv.OUT_BF16, nv.OUT_F32):
+            y = _library(xd, wbf, w, m, od)
+            check_parity(y, x, w, cols=cols, label=f"library gemm {n}x{k}")
+            assert torch.equal(bits(_library(xd, wbf, w, m, od)), bits(y)), (n, k, m, od)
+
+
+def test_library_gemm_in_a_graph_matches_eager():
+    # After a first call outside capture, a captured call replays with the
+    # eager call's bits, replay after replay, with eager work in between.
+    n, k, m = 4096, 8192, 1100
+    w = Weight.from_f32(workload.weights_f32(n, k, 17))
+    xd = upload_bits(workload.activations_bf16(m, k, 18))
+    wbf = _expanded(w, False)
+    ref = bits(_library(xd, wbf, w, m)).clone()
+    y = torch.full((m, n), -1.0, dtype=torch.bfloat16, device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            assert nv.gemm_library_raw(xd.data_ptr(), wbf.data_ptr(), w.t, y.data_ptr(), m, n, k, nv.OUT_BF16,
+                                       s.cuda_stream) == nv.OK
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bits(y), ref)
+        _library(xd, wbf, w, 64)
+
+
+def test_library_gemm_contract_and_errors():
+    w = Weight.from_f32(workload.weights_f32(64, 256, 3))
+    wbf = _expanded(w, False)
+    x = torch.zeros((3, 256), dtype=torch.bfloat16, device=DEV)
+    y = torch.empty((3, 64), dtype=torch.bfloat16, device=DEV)
+    s = _stream()
+    assert nv.gemm_library_raw(x.data_ptr(), wbf.data_ptr(), w.t, y.data_ptr(), 0, 64, 256, nv.OUT_BF16, s) == nv.OK
+    assert nv.gemm_library_raw(x.data_ptr(), wbf.data_ptr(), w.t, y.data_ptr(), 3, 64, 100, nv.OUT_BF16,
+                               s) == nv.ERR_SHAPE
+    assert nv.gemm_library_raw(x.data_ptr() + 2, wbf.data_ptr(), w.t, y.data_ptr(), 3, 64, 256, nv.OUT_BF16,
+                               s) == nv.ERR_ALIGN
+    assert nv.gemm_library_raw(x.data_ptr(), wbf.data_ptr(), w.t, y.data_ptr(), 3, 64, 256, 7, s) == nv.ERR_DTYPE
+    assert nv.gemm_library_raw(x.data_ptr(), 0, w.t, y.data_ptr(), 3, 64, 256, nv.OUT_BF16, s) == nv.ERR_NULL
 
 
 def test_gemm_contract_and_errors():

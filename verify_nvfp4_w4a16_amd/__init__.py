@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "libnvfp4_w4a16.so")
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_NONFINITE = -1, -2, -3, -4, -5
 ERR_BADSCALE, ERR_HIP, ERR_DEVICE, ERR_TILEFILE, ERR_BUFFER = -6, -7, -8, -9, -10
-ERR_TILE, ERR_SCRATCH = -11, -12
+ERR_TILE, ERR_SCRATCH, ERR_LIBRARY = -11, -12, -13
 OUT_BF16, OUT_F32 = 0, 1
 KERNEL_AUTO, KERNEL_PERSISTENT, KERNEL_TILE, KERNEL_SPLIT, KERNEL_GENERIC, KERNEL_WHOLE = 0, 1, 2, 3, 4, 5
 MAX_M = 32
@@ -29,7 +29,7 @@ EXPORTED = ("nvfp4_pack", "nvfp4_check_scales", "nvfp4_linear_shape_ok", "nvfp4_
             "nvfp4_linear", "nvfp4_linear_tiled", "nvfp4_tile_info", "nvfp4_strerror",
             "nvfp4_timeout_status", "nvfp4_linear_noalloc", "nvfp4_launch_info",
             "nvfp4_read_probe", "nvfp4_gemm_shape_ok", "nvfp4_gemm", "nvfp4_matmul",
-            "nvfp4_dequant_bf16", "nvfp4_gemm_expanded", "nvfp4_linear_dual", "nvfp4_linear_silu_input",
+            "nvfp4_dequant_bf16", "nvfp4_gemm_expanded", "nvfp4_gemm_library", "nvfp4_linear_dual", "nvfp4_linear_silu_input",
             "nvfp4_linear_deinterleave", "nvfp4_linear_grouped", "fp8_w8a16_pack", "fp8_w8a16_shape_ok",
             "fp8_w8a16_linear")
 
@@ -89,6 +89,7 @@ def _load() -> ctypes.CDLL:
     lib.fp8_w8a16_shape_ok.argtypes = [i64, i64, i64]
     lib.fp8_w8a16_linear.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
     lib.nvfp4_gemm_expanded.argtypes = [vp, vp, ctypes.c_float, vp, i64, i64, i64, ctypes.c_int, vp]
+    lib.nvfp4_gemm_library.argtypes = [vp, vp, ctypes.c_float, vp, i64, i64, i64, ctypes.c_int, vp]
     lib.nvfp4_strerror.argtypes = [ctypes.c_int]
     lib.nvfp4_strerror.restype = ctypes.c_char_p
     for name in EXPORTED:
@@ -220,6 +221,13 @@ def gemm_expanded_raw(x_ptr: int, wbf_ptr: int, tensor_scale: float, y_ptr: int,
     """nvfp4_gemm_expanded on raw device addresses; returns the status."""
     return _lib().nvfp4_gemm_expanded(x_ptr, wbf_ptr, ctypes.c_float(tensor_scale), y_ptr, m, n, k, y_dtype,
                                       stream)
+
+
+def gemm_library_raw(x_ptr: int, wbf_ptr: int, tensor_scale: float, y_ptr: int,
+                     m: int, n: int, k: int, y_dtype: int, stream: int) -> int:
+    """nvfp4_gemm_library on raw device addresses; returns the status."""
+    return _lib().nvfp4_gemm_library(x_ptr, wbf_ptr, ctypes.c_float(tensor_scale), y_ptr, m, n, k, y_dtype,
+                                     stream)
 
 
 def linear_dual_raw(x_ptr, w0_ptr, s0_ptr, t0, y0_ptr, w1_ptr, s1_ptr, t1, y1_ptr, m, n, k, y_dtype,

@@ -22,7 +22,7 @@ ARCH = "gfx950"
 
 HOST_SOURCES = ["host/pack.cpp", "host/tiles.cpp"]
 HIP_SOURCES = ["kernels/nvfp4_linear.hip", "kernels/nvfp4_gemm.hip", "kernels/nvfp4_fused.hip",
-               "kernels/w8a16.hip", "kernels/read_probe.hip"]
+               "kernels/w8a16.hip", "kernels/read_probe.hip", "kernels/library_gemm.hip"]
 
 # -ffp-contract=off keeps the packer's float64 steps unfused (bit-exact rule).
 HOST_FLAGS = ["-std=c++17", "-O3", "-fPIC", "-ffp-contract=off", "-Wall", "-Wextra",
@@ -92,7 +92,8 @@ def build(verbose: bool = False) -> str:
             raise RuntimeError(f"{src}: kernels spill to scratch: {spills}")
         objs.append(obj)
     tmp = LIB + ".tmp"
-    cmd = [hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-pthread", *objs, "-o", tmp]
+    # hipBLASLt: the library GEMM of the expand path
+    cmd = [hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-pthread", *objs, "-lhipblaslt", "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     _run(cmd)

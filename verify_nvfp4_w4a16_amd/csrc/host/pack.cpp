@@ -240,6 +240,7 @@ extern "C" const char* nvfp4_strerror(int status) {
         case NVFP4_ERR_BUFFER: return "text buffer too small";
         case NVFP4_ERR_TILE: return "launch tile does not fit the shape";
         case NVFP4_ERR_SCRATCH: return "the call needs more exchange memory than the fixed scratch of nvfp4_linear_noalloc holds";
+        case NVFP4_ERR_LIBRARY: return "the GEMM library (hipBLASLt) reported an error";
         default: return "unknown status";
     }
 }

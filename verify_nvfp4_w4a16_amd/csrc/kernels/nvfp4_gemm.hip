@@ -122,6 +122,9 @@ nvfp4_gemm_kernel(GemmArgs a) {
     const bool xfull = row0 + kRows <= a.m;
     auto xrow_of = [&](int i) { return (int64_t)(xfull ? row0 + xr0 + 16 * i : min(row0 + xr0 + 16 * i, a.m - 1)); };
 
+    // Plain (cached) loads: every row tile of the grid reads these weights
+    // again, and the later readers find them in L2 (measured on MI355X: 15-20 %
+    // faster than non-temporal loads at 256..4096 rows).
     auto load_b = [&](BRegs<BF16W>& b, int kl) {
         const int kb = kbase + kl;
 #pragma unroll
@@ -129,10 +132,10 @@ nvfp4_gemm_kernel(GemmArgs a) {
             if constexpr (BF16W) {
 #pragma unroll
                 for (int s = 0; s < 4; ++s)
-                    b.w[c][s] = load16_stream(wrow[c] + (int64_t)(kb + 32 * kq + 8 * s) * 2);
+                    b.w[c][s] = load16(wrow[c] + (int64_t)(kb + 32 * kq + 8 * s) * 2);
             } else {
-                b.w[c] = load16_stream(wrow[c] + kb / 2 + 16 * kq);
-                b.s[c] = load8_stream(srow[c] + kb / 16);
+                b.w[c] = load16(wrow[c] + kb / 2 + 16 * kq);
+                b.s[c] = *reinterpret_cast<const uint64_t*>(srow[c] + kb / 16);
             }
         }
     };

@@ -5,10 +5,10 @@
 // "Module ops" w4a16_gemm (C = A @ dequant(B), A bf16 [M, K], B NVFP4) is the
 // operation; w4a16_gemm_n128_m128 loads one weight tile for 128 rows.  Here a
 // workgroup owns 128 rows x 64 columns: x comes into LDS one 128-k block at a
-// time (registers -> LDS, double-buffered), and each of the four wavefronts
-// decodes the weights of its 32 columns in registers and multiplies them
-// with 64 rows of x (v_mfma_f32_16x16x32_bf16, 4 x 2 tiles), so one decoded
-// operand serves four MFMAs.  Column tiles are the fastest grid dimension, so
+// time (direct-to-LDS loads, double-buffered), and each of the four
+// wavefronts decodes the weights of its 32 columns in registers and
+// multiplies them with 64 rows of x (v_mfma_f32_16x16x32_bf16, 4 x 2 tiles),
+// so one decoded operand serves four MFMAs.  Column tiles are the fastest grid dimension, so
 // the eight XCDs (workgroups dealt round-robin) each keep one eighth of the
 // weight columns in their L2 across the row tiles.
 //
@@ -43,9 +43,28 @@ constexpr int kCols = 64;               // columns per workgroup
 constexpr int kMT = 4;                  // 16-row tiles per wavefront
 constexpr int kC = 2;                   // 16-column tiles per wavefront
 constexpr int kThreads = 256;
-constexpr int kPitch = kBlockK + 8;     // LDS row pitch of an x block, bf16 elements
-constexpr int kXVec = kRows * kBlockK / 8 / kThreads;   // 16-byte x pieces per thread per block
+constexpr int kPitch = kBlockK;         // LDS row of an x block: 16 pieces of 8 k, swizzled
+constexpr int kXLoads = kRows * kBlockK * 2 / 1024 / (kThreads / kWave);   // 1 KB direct loads per wavefront per block
 constexpr size_t kGemmLds = 2 * size_t(kRows) * kPitch * sizeof(uint16_t);
+
+// Waits until at most N vector memory operations of this wavefront are
+// outstanding (direct-to-LDS loads included) and keeps LDS reads below it.
+template <int N>
+__device__ __forceinline__ void gemm_wait_vm() {
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Workgroup barrier that waits for this wavefront's LDS operations only
+// (__syncthreads would also drain the weight loads in flight).
+__device__ __forceinline__ void gemm_lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
 constexpr int64_t kChunkedMaxM = 128;   // nvfp4_matmul: 32-row slices of the skinny product up to here
 
 struct GemmArgs {
@@ -84,7 +103,7 @@ nvfp4_gemm_kernel(GemmArgs a) {
     extern __shared__ __align__(16) uint16_t xs[];     // [2][kRows][kPitch]
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
-    const int wave = tid / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int wm = wave / 2, wn = wave % 2;
     const int col_lane = lane % 16;
     const int kq = lane / 16;
@@ -109,18 +128,11 @@ nvfp4_gemm_kernel(GemmArgs a) {
             srow[c] = a.sc + (int64_t)n * (a.k / 16);
         }
     }
-    // this thread's 16-byte pieces of an x block: piece v = tid + 256 i is
-    // row tid / 16 + 16 i, k 8 (tid % 16) of the block (rows past M read row
-    // M - 1, never stored)
-    const int xr0 = tid / 16, xp = tid % 16;
-    const uint16_t* xsrc0 = a.x + 8 * xp;
-    // The 32-k quarter q of row r sits at slot (q + r / 4) % 4 of the row:
-    // with the row pitch 4 banks apart, the A reads of 16 rows x 4 quarters
-    // would otherwise meet in the same banks (same rotation as the skinny
-    // kernels' x windows).
-    const int xdst0 = xr0 * kPitch + 32 * ((xp / 4 + xr0 / 4) % 4) + 8 * (xp % 4);
-    const bool xfull = row0 + kRows <= a.m;
-    auto xrow_of = [&](int i) { return (int64_t)(xfull ? row0 + xr0 + 16 * i : min(row0 + xr0 + 16 * i, a.m - 1)); };
+    // x block rows r = 32 wave + 4 i + lane / 16 come in by direct-to-LDS
+    // loads: lane l writes slot l % 16 of its row, which holds the row's
+    // 16-byte piece p = slot ^ (r % 16) (8 k), so the 16 rows of one A read
+    // fall into 16 different bank groups.  Rows past M read row M - 1.
+    const int xslot = lane % 16;
 
     // Plain (cached) loads: every row tile of the grid reads these weights
     // again, and the later readers find them in L2 (measured on MI355X: 15-20 %
@@ -139,15 +151,19 @@ nvfp4_gemm_kernel(GemmArgs a) {
             }
         }
     };
-    u32x4 xr[kXVec];
-    auto load_x = [&](int kl) {
+    const char* xwg = reinterpret_cast<const char*>(a.x + (int64_t)row0 * a.k + kbase);
+    uint32_t xoff[kXLoads];
 #pragma unroll
-        for (int i = 0; i < kXVec; ++i) xr[i] = load16(xsrc0 + xrow_of(i) * a.k + kbase + kl);
-    };
-    auto store_x = [&](int buf) {
+    for (int i = 0; i < kXLoads; ++i) {
+        const int r = 32 * wave + 4 * i + lane / 16;
+        const int rr = min(row0 + r, a.m - 1) - row0;
+        xoff[i] = static_cast<uint32_t>(rr * a.k + 8 * (xslot ^ (r % 16))) * 2u;
+    }
+    auto load_x = [&](int kl, int buf) {
+        const char* base = xwg + 2 * kl;
 #pragma unroll
-        for (int i = 0; i < kXVec; ++i)
-            *reinterpret_cast<u32x4*>(xs + buf * kRows * kPitch + xdst0 + 16 * kPitch * i) = xr[i];
+        for (int i = 0; i < kXLoads; ++i)
+            __builtin_amdgcn_global_load_lds(base + xoff[i], xs + (buf * kRows + 32 * wave + 4 * i) * kPitch, 16, 0, 0);
     };
 
     f32x4 acc[kMT][kC], grp[kMT][kC], tot[kMT][kC];
@@ -157,15 +173,19 @@ nvfp4_gemm_kernel(GemmArgs a) {
         for (int c = 0; c < kC; ++c) acc[t][c] = grp[t][c] = tot[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     BRegs<BF16W> bcur, bnext;
-    load_x(0);
+    load_x(0, 0);
     load_b(bcur, 0);
-    store_x(0);
-    __syncthreads();
+    gemm_wait_vm<0>();
+    gemm_lds_barrier();
 
-    for (int b = 0; b < nblocks; ++b) {
+    // segments, then their 128-k blocks: the fold runs once per segment
+    const int nseg = nblocks / seg_blocks;
+    for (int sg = 0; sg < nseg; ++sg) {
+      for (int bb = 0; bb < seg_blocks; ++bb) {
+        const int b = sg * seg_blocks + bb;
         const bool more = b + 1 < nblocks;
         if (more) {
-            load_x((b + 1) * kBlockK);
+            load_x((b + 1) * kBlockK, (b + 1) & 1);
             load_b(bnext, (b + 1) * kBlockK);
         }
         // multiply block b: per 32-k slice, the wavefront's kC B operands,
@@ -180,8 +200,19 @@ nvfp4_gemm_kernel(GemmArgs a) {
                 g1[c] = __builtin_amdgcn_cvt_f32_fp8(d, 1);
             }
         }
+        // A operands one 32-k slice ahead of the MFMAs that use them
+        u32x4 xa[2][kMT];
+        auto read_a = [&](u32x4 (&dst)[kMT], int s) {
+#pragma unroll
+            for (int t = 0; t < kMT; ++t) {
+                const int r = wm * 16 * kMT + 16 * t + col_lane;
+                dst[t] = *reinterpret_cast<const u32x4*>(xb + r * kPitch + 8 * ((4 * kq + s) ^ col_lane));
+            }
+        };
+        read_a(xa[0], 0);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
+            if (s < 3) read_a(xa[(s + 1) & 1], s + 1);
             bf16x8 bv[kC];
 #pragma unroll
             for (int c = 0; c < kC; ++c) {
@@ -191,38 +222,36 @@ nvfp4_gemm_kernel(GemmArgs a) {
                     bv[c] = decode8(bcur.w[c][s], s < 2 ? g0[c] : g1[c]);
             }
 #pragma unroll
-            for (int t = 0; t < kMT; ++t) {
-                const int r = wm * 16 * kMT + 16 * t + col_lane;
-                const bf16x8 xa = as_bf16x8(
-                    *reinterpret_cast<const u32x4*>(xb + r * kPitch + 32 * ((kq + col_lane / 4) % 4) + 8 * s));
-#pragma unroll
-                for (int c = 0; c < kC; ++c)
-                    acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bv[c], acc[t][c], 0, 0, 0);
-            }
-        }
-        // end of a segment: its chain joins its group's sum, and at the end
-        // of a group the group sum joins the total (first ones as they are);
-        // segments are numbered within this workgroup's K range, which is
-        // all of K or exactly one group
-        if ((b + 1) % seg_blocks == 0) {
-            const int seg = (b + 1) / seg_blocks - 1;
-            const bool gfirst_seg = seg % a.group == 0;
-            const bool gend = (seg + 1) % a.group == 0;
-            const bool first_group = seg / a.group == 0;
-#pragma unroll
             for (int t = 0; t < kMT; ++t)
 #pragma unroll
-                for (int c = 0; c < kC; ++c) {
-                    grp[t][c] = gfirst_seg ? acc[t][c] : grp[t][c] + acc[t][c];
-                    acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    if (gend) tot[t][c] = first_group ? grp[t][c] : tot[t][c] + grp[t][c];
-                }
+                for (int c = 0; c < kC; ++c)
+                    acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[s & 1][t]), bv[c], acc[t][c],
+                                                                          0, 0, 0);
         }
         if (more) {
-            store_x((b + 1) & 1);
+            gemm_wait_vm<0>();
             bcur = bnext;
-            __syncthreads();
+            gemm_lds_barrier();
         }
+      }
+      // end of segment sg: its chain joins its group's sum, and at the end
+      // of a group the group sum joins the total (first ones as they are);
+      // segments are numbered within this workgroup's K range, which is all
+      // of K or exactly one group
+      {
+        const int seg = sg;
+        const bool gfirst_seg = seg % a.group == 0;
+        const bool gend = (seg + 1) % a.group == 0;
+        const bool first_group = seg / a.group == 0;
+#pragma unroll
+        for (int t = 0; t < kMT; ++t)
+#pragma unroll
+            for (int c = 0; c < kC; ++c) {
+                grp[t][c] = gfirst_seg ? acc[t][c] : grp[t][c] + acc[t][c];
+                acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (gend) tot[t][c] = first_group ? grp[t][c] : tot[t][c] + grp[t][c];
+            }
+      }
     }
 
     if (a.parts > 1) {

@@ -391,8 +391,8 @@ int nvfp4_gemm_shape_ok(int64_t m, int64_t n, int64_t k);
  * (as nvfp4_linear), so each row's bits are those nvfp4_linear gives it, for
  * every M ("10 Kernels" 10.1).  No allocation (the first call on a device
  * runs nvfp4_init's set-up unless it has run), no host sync.  Workgroups own
- * 128 rows x 64 columns; when that gives no more workgroups than CUs and the
- * tile has split > 1, each workgroup takes one segment group and a second
+ * 128 rows x 128 columns; when that gives workgroups for at most half the
+ * CUs and the tile has split > 1, each workgroup takes one segment group and a second
  * kernel adds the group sums in order through the device buffer nvfp4_init
  * allocates (same bits): such calls on one device must not overlap in time
  * (calls on one stream, or on streams ordered by events, never do).

@@ -4,11 +4,13 @@
 //
 // "Module ops" w4a16_gemm (C = A @ dequant(B), A bf16 [M, K], B NVFP4) is the
 // operation; w4a16_gemm_n128_m128 loads one weight tile for 128 rows.  Here a
-// workgroup owns 128 rows x 64 columns: x comes into LDS one 128-k block at a
-// time (direct-to-LDS loads, double-buffered), and each of the four
-// wavefronts decodes the weights of its 32 columns in registers and
-// multiplies them with 64 rows of x (v_mfma_f32_16x16x32_bf16, 4 x 2 tiles),
-// so one decoded operand serves four MFMAs.  Column tiles are the fastest grid dimension, so
+// workgroup of eight wavefronts (one per CU, two per SIMD) owns 128 rows x 128
+// columns.  x and the packed weights come into LDS one 128-k block at a time
+// by direct-to-LDS loads, two blocks ahead of the multiply (rings of three
+// blocks, waited for by count, one barrier per block); each wavefront decodes
+// the weights of its 32 columns from LDS into registers and multiplies them
+// with 64 rows of x (v_mfma_f32_16x16x32_bf16, 4 x 2 tiles), so one decoded
+// operand serves four MFMAs.  Column tiles are the fastest grid dimension, so
 // the eight XCDs (workgroups dealt round-robin) each keep one eighth of the
 // weight columns in their L2 across the row tiles.
 //
@@ -39,13 +41,24 @@
 namespace {
 
 constexpr int kRows = 128;              // rows per workgroup
-constexpr int kCols = 64;               // columns per workgroup
+constexpr int kCols = 128;              // columns per workgroup
 constexpr int kMT = 4;                  // 16-row tiles per wavefront
 constexpr int kC = 2;                   // 16-column tiles per wavefront
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;          // eight wavefronts: 2 (rows) x 4 (columns)
 constexpr int kPitch = kBlockK;         // LDS row of an x block: 16 pieces of 8 k, swizzled
 constexpr int kXLoads = kRows * kBlockK * 2 / 1024 / (kThreads / kWave);   // 1 KB direct loads per wavefront per block
-constexpr size_t kGemmLds = 2 * size_t(kRows) * kPitch * sizeof(uint16_t);
+constexpr int kXBufs = 3;               // x blocks in the LDS ring
+constexpr size_t kXBytes = kXBufs * size_t(kRows) * kPitch * sizeof(uint16_t);
+// NVFP4 weights come into LDS too, three 128-k blocks deep: per block the
+// packed bytes of the 128 columns (eight 1 KB column tiles: lane l of tile c
+// holds column 16 c + l % 16, 32-k quarter l / 16) and their scale bytes
+// (256 B per column tile, the first 128 B used: 8 bytes per column).  With
+// BF16W the weights are register loads one block ahead.
+constexpr int kWStages = 3;
+constexpr int kWPacked = kCols * kBlockK / 2;
+constexpr int kWStage = kWPacked + (kCols / 16) * 256;
+constexpr size_t kGemmLdsNv = kXBytes + size_t(kWStages) * kWStage;
+constexpr size_t kGemmLdsBf = kXBytes;
 
 // Waits until at most N vector memory operations of this wavefront are
 // outstanding (direct-to-LDS loads included) and keeps LDS reads below it.
@@ -98,13 +111,13 @@ struct BRegs<true> {
 };
 
 template <bool BF16W, bool OUT_F32>
-__global__ void __launch_bounds__(kThreads, 2)
+__global__ void __launch_bounds__(kThreads, 1)
 nvfp4_gemm_kernel(GemmArgs a) {
     extern __shared__ __align__(16) uint16_t xs[];     // [2][kRows][kPitch]
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int wm = wave / 2, wn = wave % 2;
+    const int wm = wave / 4, wn = wave % 4;
     const int col_lane = lane % 16;
     const int kq = lane / 16;
     const int row0 = blockIdx.y * kRows;
@@ -151,11 +164,24 @@ nvfp4_gemm_kernel(GemmArgs a) {
             }
         }
     };
+    // NVFP4: wavefront w stages column tile w of each block (one 16-byte
+    // direct load of packed bytes, one 4-byte load of scale bytes per lane;
+    // lanes 32..63 repeat the scale bytes of lanes 0..31).
+    uint8_t* wls = reinterpret_cast<uint8_t*>(xs) + kXBytes;
+    const int wcol = min(static_cast<int>(blockIdx.x) * kCols + 16 * wave + lane % 16, a.n - 1);
+    const int scol = min(static_cast<int>(blockIdx.x) * kCols + 16 * wave + (lane % 32) / 2, a.n - 1);
+    const uint8_t* wsrc = a.wp + (int64_t)wcol * (a.k / 2) + kbase / 2 + 16 * (lane / 16);
+    const uint8_t* ssrc = a.sc + (int64_t)scol * (a.k / 16) + kbase / 16 + 4 * (lane % 2);
+    auto load_w = [&](int kl, int st) {
+        uint8_t* d = wls + st * kWStage;
+        __builtin_amdgcn_global_load_lds(wsrc + kl / 2, d + wave * 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(ssrc + kl / 16, d + kWPacked + wave * 256, 4, 0, 0);
+    };
     const char* xwg = reinterpret_cast<const char*>(a.x + (int64_t)row0 * a.k + kbase);
     uint32_t xoff[kXLoads];
 #pragma unroll
     for (int i = 0; i < kXLoads; ++i) {
-        const int r = 32 * wave + 4 * i + lane / 16;
+        const int r = (kRows / (kThreads / kWave)) * wave + 4 * i + lane / 16;
         const int rr = min(row0 + r, a.m - 1) - row0;
         xoff[i] = static_cast<uint32_t>(rr * a.k + 8 * (xslot ^ (r % 16))) * 2u;
     }
@@ -163,7 +189,7 @@ nvfp4_gemm_kernel(GemmArgs a) {
         const char* base = xwg + 2 * kl;
 #pragma unroll
         for (int i = 0; i < kXLoads; ++i)
-            __builtin_amdgcn_global_load_lds(base + xoff[i], xs + (buf * kRows + 32 * wave + 4 * i) * kPitch, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(base + xoff[i], xs + (buf * kRows + (kRows / (kThreads / kWave)) * wave + 4 * i) * kPitch, 16, 0, 0);
     };
 
     f32x4 acc[kMT][kC], grp[kMT][kC], tot[kMT][kC];
@@ -173,9 +199,26 @@ nvfp4_gemm_kernel(GemmArgs a) {
         for (int c = 0; c < kC; ++c) acc[t][c] = grp[t][c] = tot[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     BRegs<BF16W> bcur, bnext;
+    // blocks 0 and 1 go out first; block 0 must have landed
     load_x(0, 0);
-    load_b(bcur, 0);
-    gemm_wait_vm<0>();
+    if constexpr (BF16W) {
+        load_b(bcur, 0);
+        if (nblocks > 1) {
+            load_x(kBlockK, 1);
+            gemm_wait_vm<kXLoads>();
+        } else {
+            gemm_wait_vm<0>();
+        }
+    } else {
+        load_w(0, 0);
+        if (nblocks > 1) {
+            load_x(kBlockK, 1);
+            load_w(kBlockK, 1);
+            gemm_wait_vm<kXLoads + 2>();
+        } else {
+            gemm_wait_vm<0>();
+        }
+    }
     gemm_lds_barrier();
 
     // segments, then their 128-k blocks: the fold runs once per segment
@@ -184,18 +227,29 @@ nvfp4_gemm_kernel(GemmArgs a) {
       for (int bb = 0; bb < seg_blocks; ++bb) {
         const int b = sg * seg_blocks + bb;
         const bool more = b + 1 < nblocks;
-        if (more) {
-            load_x((b + 1) * kBlockK, (b + 1) & 1);
-            load_b(bnext, (b + 1) * kBlockK);
+        // block b + 2's x (and NVFP4 weights) go out two blocks ahead
+        if (b + 2 < nblocks) load_x((b + 2) * kBlockK, (b + 2) % kXBufs);
+        if constexpr (BF16W) {
+            if (more) load_b(bnext, (b + 1) * kBlockK);
+        } else {
+            if (b + 2 < nblocks) load_w((b + 2) * kBlockK, (b + 2) % kWStages);
+            // this block's B operands from its stage
+            const uint8_t* wst = wls + (b % kWStages) * kWStage;
+#pragma unroll
+            for (int c = 0; c < kC; ++c) {
+                const int ct = wn * kC + c;
+                bcur.w[c] = *reinterpret_cast<const u32x4*>(wst + ct * 1024 + 16 * lane);
+                bcur.s[c] = *reinterpret_cast<const uint16_t*>(wst + kWPacked + ct * 256 + 8 * col_lane + 2 * kq);
+            }
         }
         // multiply block b: per 32-k slice, the wavefront's kC B operands,
         // then each of its kMT A operands against them
-        const uint16_t* xb = xs + (b & 1) * kRows * kPitch;
+        const uint16_t* xb = xs + (b % kXBufs) * kRows * kPitch;
         float g0[kC], g1[kC];
         if constexpr (!BF16W) {
 #pragma unroll
             for (int c = 0; c < kC; ++c) {
-                const uint32_t d = static_cast<uint32_t>(bcur.s[c] >> (16 * kq));
+                const uint32_t d = static_cast<uint32_t>(bcur.s[c]);
                 g0[c] = __builtin_amdgcn_cvt_f32_fp8(d, 0);
                 g1[c] = __builtin_amdgcn_cvt_f32_fp8(d, 1);
             }
@@ -229,8 +283,16 @@ nvfp4_gemm_kernel(GemmArgs a) {
                                                                           0, 0, 0);
         }
         if (more) {
-            gemm_wait_vm<0>();
-            bcur = bnext;
+            // block b + 1 has landed; block b + 2's loads may be in flight
+            if constexpr (BF16W) {
+                gemm_wait_vm<0>();
+                bcur = bnext;
+            } else {
+                if (b + 2 < nblocks)
+                    gemm_wait_vm<kXLoads + 2>();
+                else
+                    gemm_wait_vm<0>();
+            }
             gemm_lds_barrier();
         }
       }
@@ -381,19 +443,20 @@ int gemm_launch(const void* x, const void* w, const uint8_t* scales, float t, vo
     a.part = nullptr;
     a.parts = 1;
     const int64_t col_tiles = (n + kCols - 1) / kCols, row_tiles = (m + kRows - 1) / kRows;
-    // No more tiles than CUs: one workgroup per segment group instead (the
-    // tile's split), the group sums added in order by a second kernel, so
-    // the bits do not change.  Needs the partial-sum buffer nvfp4_init
-    // allocates.  (Measured on MI355X: 1.1-2.7x faster at 128..512 rows on
-    // the decode round's products; with more tiles than CUs the extra
-    // partial-sum traffic costs more than the split gains.)
+    // Tiles for at most half the CUs (one workgroup per CU): one workgroup
+    // per segment group instead (the tile's split), the group sums added in
+    // order by a second kernel, so the bits do not change.  Needs the
+    // partial-sum buffer nvfp4_init allocates.  (Measured on MI355X: faster
+    // at 256..512 rows on the decode round's products; with tiles for every
+    // CU, e.g. 4096 columns at 1024 rows, the extra partial-sum traffic costs
+    // more than the split gains.)
     if (tile.split > 1) {
         float* part = nullptr;
         size_t bytes = 0;
         int cus = 256;
         st = nvfp4::gemm_partials(&part, &bytes, &cus);
         if (st != NVFP4_OK) return st;
-        if (part && row_tiles * col_tiles <= int64_t(cus) &&
+        if (part && 2 * row_tiles * col_tiles <= int64_t(cus) &&
             size_t(tile.split) * size_t(m) * size_t(n) * sizeof(float) <= bytes) {
             a.part = part;
             a.parts = tile.split;
@@ -401,7 +464,8 @@ int gemm_launch(const void* x, const void* w, const uint8_t* scales, float t, vo
     }
     const dim3 grid(static_cast<unsigned>(col_tiles), static_cast<unsigned>(row_tiles),
                     static_cast<unsigned>(a.parts));
-    hipLaunchKernelGGL(pick_gemm(bf16w, y_dtype), grid, dim3(kThreads), kGemmLds, static_cast<hipStream_t>(stream), a);
+    hipLaunchKernelGGL(pick_gemm(bf16w, y_dtype), grid, dim3(kThreads), bf16w ? kGemmLdsBf : kGemmLdsNv,
+                       static_cast<hipStream_t>(stream), a);
     if (hipGetLastError() != hipSuccess) return NVFP4_ERR_HIP;
     if (a.parts > 1) return nvfp4::launch_ordered_sum(a.part, a.parts, m * n, t, y, y_dtype, stream);
     return NVFP4_OK;
@@ -424,7 +488,7 @@ int gemm_setup() {
         for (int od = 0; od <= 1; ++od)
             if (hipFuncSetAttribute(reinterpret_cast<const void*>(pick_gemm(bw != 0, od)),
                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    static_cast<int>(kGemmLds)) != hipSuccess)
+                                    static_cast<int>(bw ? kGemmLdsBf : kGemmLdsNv)) != hipSuccess)
                 return NVFP4_ERR_HIP;
     return NVFP4_OK;
 }

@@ -44,9 +44,12 @@ constexpr int kRows = 128;              // rows per workgroup
 constexpr int kCols = 128;              // columns per workgroup
 constexpr int kMT = 4;                  // 16-row tiles per wavefront
 constexpr int kC = 2;                   // 16-column tiles per wavefront
-constexpr int kThreads = 512;          // eight wavefronts: 2 (rows) x 4 (columns)
+constexpr int kWavesN = kCols / (16 * kC);             // wavefronts across the columns
+constexpr int kWaves = (kRows / (16 * kMT)) * kWavesN;  // 2 (rows) x 4 (columns)
+constexpr int kThreads = kWaves * kWave;
 constexpr int kPitch = kBlockK;         // LDS row of an x block: 16 pieces of 8 k, swizzled
-constexpr int kXLoads = kRows * kBlockK * 2 / 1024 / (kThreads / kWave);   // 1 KB direct loads per wavefront per block
+constexpr int kXRowsPerWave = kRows / kWaves;           // x rows each wavefront stages
+constexpr int kXLoads = kXRowsPerWave / 4;              // 1 KB direct loads (4 rows) per wavefront per block
 constexpr int kXBufs = 3;               // x blocks in the LDS ring
 constexpr size_t kXBytes = kXBufs * size_t(kRows) * kPitch * sizeof(uint16_t);
 // NVFP4 weights come into LDS too, three 128-k blocks deep: per block the
@@ -59,6 +62,10 @@ constexpr int kWPacked = kCols * kBlockK / 2;
 constexpr int kWStage = kWPacked + (kCols / 16) * 256;
 constexpr size_t kGemmLdsNv = kXBytes + size_t(kWStages) * kWStage;
 constexpr size_t kGemmLdsBf = kXBytes;
+constexpr int kWTilesPerWave = kCols / 16 / kWaves;    // weight column tiles each wavefront stages
+constexpr int kWLoads = 2 * kWTilesPerWave;             // its direct loads per block (packed, scales)
+static_assert(kWTilesPerWave >= 1 && kWTilesPerWave * kWaves * 16 == kCols, "weight staging");
+static_assert(kXLoads >= 1 && kXLoads * 4 * kWaves == kRows, "x staging");
 
 // Waits until at most N vector memory operations of this wavefront are
 // outstanding (direct-to-LDS loads included) and keeps LDS reads below it.
@@ -117,7 +124,7 @@ nvfp4_gemm_kernel(GemmArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int wm = wave / 4, wn = wave % 4;
+    const int wm = wave / kWavesN, wn = wave % kWavesN;
     const int col_lane = lane % 16;
     const int kq = lane / 16;
     const int row0 = blockIdx.y * kRows;
@@ -164,24 +171,35 @@ nvfp4_gemm_kernel(GemmArgs a) {
             }
         }
     };
-    // NVFP4: wavefront w stages column tile w of each block (one 16-byte
-    // direct load of packed bytes, one 4-byte load of scale bytes per lane;
-    // lanes 32..63 repeat the scale bytes of lanes 0..31).
+    // NVFP4: wavefront w stages column tiles kWTilesPerWave w + j of each
+    // block (per tile one 16-byte direct load of packed bytes and one 4-byte
+    // load of scale bytes per lane; lanes 32..63 repeat the scale bytes of
+    // lanes 0..31).
     uint8_t* wls = reinterpret_cast<uint8_t*>(xs) + kXBytes;
-    const int wcol = min(static_cast<int>(blockIdx.x) * kCols + 16 * wave + lane % 16, a.n - 1);
-    const int scol = min(static_cast<int>(blockIdx.x) * kCols + 16 * wave + (lane % 32) / 2, a.n - 1);
-    const uint8_t* wsrc = a.wp + (int64_t)wcol * (a.k / 2) + kbase / 2 + 16 * (lane / 16);
-    const uint8_t* ssrc = a.sc + (int64_t)scol * (a.k / 16) + kbase / 16 + 4 * (lane % 2);
+    const uint8_t* wsrc[kWTilesPerWave];
+    const uint8_t* ssrc[kWTilesPerWave];
+#pragma unroll
+    for (int j = 0; j < kWTilesPerWave; ++j) {
+        const int ct = kWTilesPerWave * wave + j;
+        const int wcol = min(static_cast<int>(blockIdx.x) * kCols + 16 * ct + lane % 16, a.n - 1);
+        const int scol = min(static_cast<int>(blockIdx.x) * kCols + 16 * ct + (lane % 32) / 2, a.n - 1);
+        wsrc[j] = a.wp + (int64_t)wcol * (a.k / 2) + kbase / 2 + 16 * (lane / 16);
+        ssrc[j] = a.sc + (int64_t)scol * (a.k / 16) + kbase / 16 + 4 * (lane % 2);
+    }
     auto load_w = [&](int kl, int st) {
         uint8_t* d = wls + st * kWStage;
-        __builtin_amdgcn_global_load_lds(wsrc + kl / 2, d + wave * 1024, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(ssrc + kl / 16, d + kWPacked + wave * 256, 4, 0, 0);
+#pragma unroll
+        for (int j = 0; j < kWTilesPerWave; ++j) {
+            const int ct = kWTilesPerWave * wave + j;
+            __builtin_amdgcn_global_load_lds(wsrc[j] + kl / 2, d + ct * 1024, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(ssrc[j] + kl / 16, d + kWPacked + ct * 256, 4, 0, 0);
+        }
     };
     const char* xwg = reinterpret_cast<const char*>(a.x + (int64_t)row0 * a.k + kbase);
     uint32_t xoff[kXLoads];
 #pragma unroll
     for (int i = 0; i < kXLoads; ++i) {
-        const int r = (kRows / (kThreads / kWave)) * wave + 4 * i + lane / 16;
+        const int r = kXRowsPerWave * wave + 4 * i + lane / 16;
         const int rr = min(row0 + r, a.m - 1) - row0;
         xoff[i] = static_cast<uint32_t>(rr * a.k + 8 * (xslot ^ (r % 16))) * 2u;
     }
@@ -189,7 +207,8 @@ nvfp4_gemm_kernel(GemmArgs a) {
         const char* base = xwg + 2 * kl;
 #pragma unroll
         for (int i = 0; i < kXLoads; ++i)
-            __builtin_amdgcn_global_load_lds(base + xoff[i], xs + (buf * kRows + (kRows / (kThreads / kWave)) * wave + 4 * i) * kPitch, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(base + xoff[i], xs + (buf * kRows + kXRowsPerWave * wave + 4 * i) * kPitch,
+                                             16, 0, 0);
     };
 
     f32x4 acc[kMT][kC], grp[kMT][kC], tot[kMT][kC];
@@ -214,7 +233,7 @@ nvfp4_gemm_kernel(GemmArgs a) {
         if (nblocks > 1) {
             load_x(kBlockK, 1);
             load_w(kBlockK, 1);
-            gemm_wait_vm<kXLoads + 2>();
+            gemm_wait_vm<kXLoads + kWLoads>();
         } else {
             gemm_wait_vm<0>();
         }
@@ -289,7 +308,7 @@ nvfp4_gemm_kernel(GemmArgs a) {
                 bcur = bnext;
             } else {
                 if (b + 2 < nblocks)
-                    gemm_wait_vm<kXLoads + 2>();
+                    gemm_wait_vm<kXLoads + kWLoads>();
                 else
                     gemm_wait_vm<0>();
             }

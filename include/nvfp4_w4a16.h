@@ -405,12 +405,11 @@ int nvfp4_gemm(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scale
 /*
  * Device, asynchronous.  Picks the kernel by row count over one stored
  * format, as "10 Kernels" 10.2's table does: nvfp4_linear for M <= 32,
- * nvfp4_linear's kernels on 32-row slices above that (all slices in one
+ * nvfp4_linear's kernels on 32-row slices up to 64 rows (all slices in one
  * launch; the 128-row GEMM tile leaves most CUs idle there), nvfp4_gemm
- * from a row count measured to favour it.  All
- * give every row the same bits.  Like those calls, calls that use the
- * device workspace must not overlap in time on one device.  Shape contract: nvfp4_gemm's.  A slice that
- * fails stops the call with its status, earlier slices having been launched.
+ * above (row counts measured on MI355X).  All give every row the same bits.
+ * Like those calls, calls that use the device workspace must not overlap in
+ * time on one device.  Shape contract: nvfp4_gemm's.
  * Errors: those of the calls it makes.
  */
 int nvfp4_matmul(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4m3,

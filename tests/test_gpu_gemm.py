@@ -84,8 +84,8 @@ def test_gemm_rows_equal_linear_rows():
         lin = bits(_linear(upload_bits(x[r0:r0 + 32]), w, 32))
         assert torch.equal(lin, g[r0:r0 + 32]), r0
     assert torch.equal(bits(_linear(upload_bits(x[5:6]), w, 1)), g[5:6])
-    for m in (32, 33, 64, 96):
-        y = _gemm(xd, w, m, fn=nv.matmul_raw)                # 32-row slices in one launch up to 128 rows
+    for m in (32, 33, 64, 65, 96):
+        y = _gemm(xd, w, m, fn=nv.matmul_raw)                # 32-row slices in one launch up to 64 rows, then the GEMM
         assert torch.equal(bits(y), g[:m]), m
     check_parity(_gemm(xd, w, 96, torch.float32), x, w, label="gemm 4136x4096 M=96 fp32")
 

@@ -85,7 +85,7 @@ __device__ __forceinline__ void gemm_lds_barrier() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 }
-constexpr int64_t kChunkedMaxM = 128;   // nvfp4_matmul: 32-row slices of the skinny product up to here
+constexpr int64_t kChunkedMaxM = 64;    // nvfp4_matmul: 32-row slices of the skinny product up to here
 
 struct GemmArgs {
     const uint16_t* x;      // bf16 [M, K]
@@ -549,12 +549,12 @@ extern "C" int nvfp4_matmul(const void* x_bf16, const uint8_t* w_packed, const u
     if (st != NVFP4_OK) return st;
     if (m > kChunkedMaxM)
         return nvfp4_gemm(x_bf16, w_packed, scales_e4m3, tensor_scale, y, m, n, k, y_dtype, stream);
-    // 33..128 rows: the skinny product's kernels on 32-row slices, all slices
+    // 33..64 rows: the skinny product's kernels on 32-row slices, all slices
     // in one launch (blockIdx.y picks the slice; same bits), which stream the
     // weight at a few TB/s where the 128-row GEMM tile leaves most CUs idle
-    // (measured on MI355X on the decode round's shapes: 21-41 us at 64 rows
-    // against 30-73 us for the GEMM; even at 128 rows; the GEMM ahead from
-    // 192 rows on three of the four).
+    // (measured on MI355X on the decode round's shapes: 21-40 us at 33..64
+    // rows against 23-50 us for the GEMM; the GEMM ahead or level from 80
+    // rows).
     nvfp4::MultiLaunch ml;
     ml.slice_rows = NVFP4_MAX_M;
     ml.rows_total = static_cast<int>(m);

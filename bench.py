@@ -483,6 +483,18 @@ def next_rows(torch, dev, stream) -> dict:
             us = timed_graph(torch, stream, run) * 1e3 / len(ws)
             gbps = wb / (us * 1e-6) / 1e9
             fp8[f"{s.n}x{s.k}_M{m}"] = {"us": us, "weight_GBps": gbps, "frac_of_peak": gbps / PEAK_HBM_GBPS}
+        # many rows: fp8_w8a16_gemm (what fp8_w8a16_matmul runs above 32 rows)
+        for m in (64, 256, 1024):
+            x = xs(m, s.k, 23)
+            y = torch.empty((m, s.n), dtype=torch.bfloat16, device=dev)
+            def run_g(h):
+                for c, sc in ws:
+                    call(nv.fp8_gemm_raw, x.data_ptr(), c.data_ptr(), sc.data_ptr(), y.data_ptr(), m, s.n, s.k,
+                         nv.OUT_BF16, h)
+            us = timed_graph(torch, stream, run_g) * 1e3 / len(ws)
+            tf = 2.0 * m * s.n * s.k / (us * 1e-6) / 1e12
+            fp8[f"gemm_{s.n}x{s.k}_M{m}"] = {"us": us, "weight_GBps": wb / (us * 1e-6) / 1e9, "TFLOPs": tf,
+                                             "frac_of_bf16_mfma_peak": tf / PEAK_BF16_MFMA_TFLOPS}
         del ws
     out["fp8_w8a16"] = fp8
     torch.cuda.synchronize()

@@ -375,6 +375,40 @@ int fp8_w8a16_linear(const void* x_bf16, const uint8_t* w_e4m3, const float* blo
                      int64_t m, int64_t n, int64_t k, int y_dtype, void* stream);
 
 /*
+ * Host, pure.  The shape contract of fp8_w8a16_gemm and fp8_w8a16_matmul:
+ * 0 <= M <= 65535 * 128, N and K positive multiples of 128, N <= 2^28,
+ * K <= 2^20, M * N <= 2^40 ("Module ops" w8a16_tc_rows_shape_ok checks a
+ * kernel's contract likewise).  Returns NVFP4_OK or NVFP4_ERR_SHAPE.
+ */
+int fp8_w8a16_gemm_shape_ok(int64_t m, int64_t n, int64_t k);
+
+/*
+ * Device, asynchronous on `stream`.  fp8_w8a16_linear's product for any row
+ * count, the prefill forms of the FP8 family ("Module ops" w8a16_gemm,
+ * w8a16_gemm_n128_m128 and the pipelined forms; "10 Kernels" 10.3 for the
+ * format): same arguments, layouts and alignment, shape contract
+ * fp8_w8a16_gemm_shape_ok; M == 0 launches nothing.  Same MFMA inputs, block
+ * chains and two-level segment order as fp8_w8a16_linear, so each row's bits
+ * are those it gives the row at 1..32 rows ("10 Kernels" 10.1).  Workgroups
+ * own 128 rows x 128 columns; where that gives workgroups for at most half
+ * the CUs and the tile has more than one segment group, the K split goes
+ * through the device buffer nvfp4_init allocates (same bits): such calls on
+ * one device must not overlap in time.  No allocation, no host sync.
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, HIP, DEVICE.
+ */
+int fp8_w8a16_gemm(const void* x_bf16, const uint8_t* w_e4m3, const float* block_scales, void* y,
+                   int64_t m, int64_t n, int64_t k, int y_dtype, void* stream);
+
+/*
+ * Device, asynchronous.  Picks the FP8 kernel by row count ("10 Kernels"
+ * 10.2's regimes over the format of 10.3): fp8_w8a16_linear for M <= 32,
+ * fp8_w8a16_gemm above; both give every row the same bits.  Shape contract:
+ * fp8_w8a16_gemm_shape_ok.  Errors: those of the call it makes.
+ */
+int fp8_w8a16_matmul(const void* x_bf16, const uint8_t* w_e4m3, const float* block_scales, void* y,
+                     int64_t m, int64_t n, int64_t k, int y_dtype, void* stream);
+
+/*
  * Host, pure.  The shape contract of nvfp4_gemm and nvfp4_gemm_expanded:
  * 0 <= M <= 65535 * 128, 1 <= N <= 2^28, 256 <= K <= 2^20 with K % 256 == 0,
  * M * N <= 2^40 ("Module ops" w4a16_tc_rows_shape_ok likewise checks a

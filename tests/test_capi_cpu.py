@@ -351,3 +351,11 @@ def test_fp8_pack_matches_oracle():
         nv.fp8_pack(np.zeros((100, 128), np.float32))
     assert nv.fp8_shape_ok(32, 128, 128) and not nv.fp8_shape_ok(33, 128, 128)
     assert not nv.fp8_shape_ok(1, 100, 128) and not nv.fp8_shape_ok(1, 128, 64)
+
+
+def test_fp8_gemm_shape_contract():
+    assert nv.fp8_gemm_shape_ok(0, 128, 128) and nv.fp8_gemm_shape_ok(33, 128, 128)
+    assert nv.fp8_gemm_shape_ok(65535 * 128, 128, 128) and not nv.fp8_gemm_shape_ok(65535 * 128 + 1, 128, 128)
+    assert not nv.fp8_gemm_shape_ok(-1, 128, 128) and not nv.fp8_gemm_shape_ok(64, 100, 128)
+    assert not nv.fp8_gemm_shape_ok(64, 128, 64) and not nv.fp8_gemm_shape_ok(64, 128, (1 << 20) + 128)
+    assert not nv.fp8_gemm_shape_ok(1 << 22, 1 << 19, 128)          # M * N above 2^40

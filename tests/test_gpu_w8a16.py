@@ -86,3 +86,57 @@ def test_w8a16_errors():
     assert nv.fp8_linear_raw(x.data_ptr() + 8, wd.data_ptr(), sd.data_ptr(), y.data_ptr(), 2, 128, 256, 0, s) == \
         nv.ERR_ALIGN
     assert nv.fp8_linear_raw(x.data_ptr(), wd.data_ptr(), sd.data_ptr(), y.data_ptr(), 0, 128, 256, 0, s) == nv.OK
+
+
+def _gemm(xd, wd, sd, m, n, k, out_dtype=torch.bfloat16, fn=None):
+    y = torch.empty((m, n), dtype=out_dtype, device=DEV)
+    od = nv.OUT_F32 if out_dtype == torch.float32 else nv.OUT_BF16
+    st = (fn or nv.fp8_gemm_raw)(xd.data_ptr(), wd.data_ptr(), sd.data_ptr(), y.data_ptr(), m, n, k, od,
+                                 torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == nv.OK, st
+    return y
+
+
+def test_w8a16_gemm_rows_equal_linear_rows_and_parity():
+    # Many rows: every row has the bits fp8_w8a16_linear gives it (32-row
+    # slices and a single row), at every M, with and without the K split
+    # (4096 columns at 256 rows split; 1024 rows do not), ragged M; parity on
+    # sampled columns.
+    for n, k in [(4096, 4096), (8192, 4096), (4096, 12288), (384, 1152)]:
+        codes, scales = nv.fp8_pack(workload.weights_f32(n, k, 300 + n // 128))
+        wd, sd = upload_u8(codes), torch.from_numpy(scales).to(DEV)
+        x = workload.activations_bf16(1024, k, 400 + k, outliers=True)
+        xd = upload_bits(x)
+        full = bits(_gemm(xd, wd, sd, 1024, n, k)).clone()
+        for r0 in (0, 32, 992):
+            lin = bits(_run(upload_bits(x[r0:r0 + 32]), wd, sd, 32, n, k))
+            assert torch.equal(lin, full[r0:r0 + 32]), (n, k, r0)
+        assert torch.equal(bits(_run(upload_bits(x[77:78]), wd, sd, 1, n, k)), full[77:78])
+        for m in (33, 70, 256, 600):
+            y = _gemm(xd, wd, sd, m, n, k)
+            assert torch.equal(bits(y), full[:m]), (n, k, m)
+            y = _gemm(xd, wd, sd, m, n, k, fn=nv.fp8_matmul_raw)
+            assert torch.equal(bits(y), full[:m]), (n, k, m, "matmul")
+        cols = np.unique(np.concatenate([np.arange(16), np.arange(n - 16, n), workload.rng(n + 1).integers(0, n, 96)]))
+        _parity(_gemm(xd, wd, sd, 1024, n, k), x, codes, scales, cols, f"w8a16 gemm {n}x{k}")
+        _parity(_gemm(xd, wd, sd, 70, n, k, torch.float32), x[:70], codes, scales, cols, f"w8a16 gemm {n}x{k} fp32")
+
+
+def test_w8a16_gemm_contract_and_errors():
+    assert nv.fp8_gemm_shape_ok(0, 128, 128) and nv.fp8_gemm_shape_ok(4096, 8192, 4096)
+    assert not nv.fp8_gemm_shape_ok(64, 100, 128) and not nv.fp8_gemm_shape_ok(64, 128, 100)
+    assert not nv.fp8_gemm_shape_ok(-1, 128, 128)
+    codes, scales = nv.fp8_pack(workload.weights_f32(128, 256, 5))
+    wd, sd = upload_u8(codes), torch.from_numpy(scales).to(DEV)
+    x = torch.zeros((40, 256), dtype=torch.bfloat16, device=DEV)
+    y = torch.empty((40, 128), dtype=torch.bfloat16, device=DEV)
+    s = torch.cuda.current_stream().cuda_stream
+    assert nv.fp8_gemm_raw(x.data_ptr(), wd.data_ptr(), sd.data_ptr(), y.data_ptr(), 0, 128, 256, 0, s) == nv.OK
+    assert nv.fp8_gemm_raw(x.data_ptr() + 2, wd.data_ptr(), sd.data_ptr(), y.data_ptr(), 40, 128, 256, 0, s) == \
+        nv.ERR_ALIGN
+    assert nv.fp8_gemm_raw(x.data_ptr(), wd.data_ptr(), sd.data_ptr(), y.data_ptr(), 40, 128, 256, 5, s) == \
+        nv.ERR_DTYPE
+    assert nv.fp8_gemm_raw(x.data_ptr(), 0, sd.data_ptr(), y.data_ptr(), 40, 128, 256, 0, s) == nv.ERR_NULL
+    assert nv.fp8_matmul_raw(x.data_ptr(), wd.data_ptr(), sd.data_ptr(), y.data_ptr(), 40, 128, 200, 0, s) == \
+        nv.ERR_SHAPE

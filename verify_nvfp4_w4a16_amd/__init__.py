@@ -31,7 +31,7 @@ EXPORTED = ("nvfp4_pack", "nvfp4_check_scales", "nvfp4_linear_shape_ok", "nvfp4_
             "nvfp4_read_probe", "nvfp4_gemm_shape_ok", "nvfp4_gemm", "nvfp4_matmul",
             "nvfp4_dequant_bf16", "nvfp4_gemm_expanded", "nvfp4_gemm_library", "nvfp4_linear_dual", "nvfp4_linear_silu_input",
             "nvfp4_linear_deinterleave", "nvfp4_linear_grouped", "fp8_w8a16_pack", "fp8_w8a16_shape_ok",
-            "fp8_w8a16_linear")
+            "fp8_w8a16_linear", "fp8_w8a16_gemm_shape_ok", "fp8_w8a16_gemm", "fp8_w8a16_matmul")
 
 
 class Tile(ctypes.Structure):
@@ -88,6 +88,9 @@ def _load() -> ctypes.CDLL:
     lib.fp8_w8a16_pack.argtypes = [vp, i64, i64, vp, vp]
     lib.fp8_w8a16_shape_ok.argtypes = [i64, i64, i64]
     lib.fp8_w8a16_linear.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
+    lib.fp8_w8a16_gemm_shape_ok.argtypes = [i64, i64, i64]
+    lib.fp8_w8a16_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
+    lib.fp8_w8a16_matmul.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
     lib.nvfp4_gemm_expanded.argtypes = [vp, vp, ctypes.c_float, vp, i64, i64, i64, ctypes.c_int, vp]
     lib.nvfp4_gemm_library.argtypes = [vp, vp, ctypes.c_float, vp, i64, i64, i64, ctypes.c_int, vp]
     lib.nvfp4_strerror.argtypes = [ctypes.c_int]
@@ -281,6 +284,20 @@ def fp8_shape_ok(m: int, n: int, k: int) -> bool:
 def fp8_linear_raw(x_ptr, w_ptr, s_ptr, y_ptr, m, n, k, y_dtype, stream) -> int:
     """fp8_w8a16_linear on raw device addresses; returns the status."""
     return _lib().fp8_w8a16_linear(x_ptr, w_ptr, s_ptr, y_ptr, m, n, k, y_dtype, stream)
+
+
+def fp8_gemm_shape_ok(m: int, n: int, k: int) -> bool:
+    return _lib().fp8_w8a16_gemm_shape_ok(m, n, k) == OK
+
+
+def fp8_gemm_raw(x_ptr, w_ptr, s_ptr, y_ptr, m, n, k, y_dtype, stream) -> int:
+    """fp8_w8a16_gemm on raw device addresses; returns the status."""
+    return _lib().fp8_w8a16_gemm(x_ptr, w_ptr, s_ptr, y_ptr, m, n, k, y_dtype, stream)
+
+
+def fp8_matmul_raw(x_ptr, w_ptr, s_ptr, y_ptr, m, n, k, y_dtype, stream) -> int:
+    """fp8_w8a16_matmul on raw device addresses; returns the status."""
+    return _lib().fp8_w8a16_matmul(x_ptr, w_ptr, s_ptr, y_ptr, m, n, k, y_dtype, stream)
 
 
 def gemm_shape_ok(m: int, n: int, k: int) -> bool:

@@ -225,6 +225,16 @@ extern "C" int fp8_w8a16_shape_ok(int64_t m, int64_t n, int64_t k) {
     return NVFP4_OK;
 }
 
+extern "C" int fp8_w8a16_gemm_shape_ok(int64_t m, int64_t n, int64_t k) {
+    constexpr int64_t kB = 128;
+    // rows: at most 65535 workgroup rows (the grid's y limit) of 128
+    if (m < 0 || m > int64_t(65535) * 128) return NVFP4_ERR_SHAPE;
+    if (n < kB || n > (int64_t(1) << 28) || n % kB) return NVFP4_ERR_SHAPE;
+    if (k < kB || k > (int64_t(1) << 20) || k % kB) return NVFP4_ERR_SHAPE;
+    if (m * n > (int64_t(1) << 40)) return NVFP4_ERR_SHAPE;
+    return NVFP4_OK;
+}
+
 extern "C" const char* nvfp4_strerror(int status) {
     switch (status) {
         case NVFP4_OK: return "ok";

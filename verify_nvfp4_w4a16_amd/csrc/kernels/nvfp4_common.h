@@ -76,4 +76,24 @@ __device__ __forceinline__ uint64_t load8_stream(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const uint64_t*>(p));
 }
 
+// For the many-row GEMMs, whose x and weights come in by direct-to-LDS loads.
+// Waits until at most N vector memory operations of this wavefront are
+// outstanding (direct-to-LDS loads included) and keeps LDS reads below it.
+template <int N>
+__device__ __forceinline__ void gemm_wait_vm() {
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Workgroup barrier that waits for this wavefront's LDS operations only
+// (__syncthreads would also drain the weight loads in flight).
+__device__ __forceinline__ void gemm_lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 }  // namespace

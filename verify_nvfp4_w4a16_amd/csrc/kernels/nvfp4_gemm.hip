@@ -67,24 +67,6 @@ constexpr int kWLoads = 2 * kWTilesPerWave;             // its direct loads per 
 static_assert(kWTilesPerWave >= 1 && kWTilesPerWave * kWaves * 16 == kCols, "weight staging");
 static_assert(kXLoads >= 1 && kXLoads * 4 * kWaves == kRows, "x staging");
 
-// Waits until at most N vector memory operations of this wavefront are
-// outstanding (direct-to-LDS loads included) and keeps LDS reads below it.
-template <int N>
-__device__ __forceinline__ void gemm_wait_vm() {
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-}
-
-// Workgroup barrier that waits for this wavefront's LDS operations only
-// (__syncthreads would also drain the weight loads in flight).
-__device__ __forceinline__ void gemm_lds_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-}
 constexpr int64_t kChunkedMaxM = 64;    // nvfp4_matmul: 32-row slices of the skinny product up to here
 
 struct GemmArgs {

@@ -15,6 +15,15 @@
 // sum joins the segment's chain as fma(S, block, chain), blocks in increasing
 // k; the segment chains are added in the two-level order of the (N, K) tile,
 // so a row's bits do not depend on M or on the other rows ("10 Kernels" 10.1).
+//
+// fp8_w8a16_gemm_kernel is the same product for any row count (the pages'
+// w8a16_gemm_n128_m128 and pipelined forms for prefill chunks), laid out like
+// nvfp4_gemm_kernel: one workgroup of eight wavefronts per CU owns 128 rows x
+// 128 columns (wavefronts 2 x 4, each 64 rows x 32 columns), x and the e4m3
+// codes come into LDS by direct-to-LDS loads two 128-k blocks ahead, and each
+// wavefront walks every segment of K in order, so the MFMA inputs, the block
+// chains and the two-level fold are those of fp8_w8a16_kernel: every row has
+// the bits fp8_w8a16_linear gives it.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -227,6 +236,208 @@ fp8_w8a16_kernel(W8Args a) {
     }
 }
 
+// ---- many rows ----------------------------------------------------------
+
+constexpr int kGRows = 128;                 // rows per workgroup
+constexpr int kGCols = 128;                 // columns per workgroup: one scale block
+constexpr int kGMT = 4;                     // 16-row tiles per wavefront
+constexpr int kGC = 2;                      // 16-column tiles per wavefront
+constexpr int kGWavesN = kGCols / (16 * kGC);
+constexpr int kGWaves = (kGRows / (16 * kGMT)) * kGWavesN;
+constexpr int kGThreads = kGWaves * kWave;
+constexpr int kGXRowsPerWave = kGRows / kGWaves;
+constexpr int kGXLoads = kGXRowsPerWave / 4;                 // 1 KB direct loads of x per wavefront per block
+constexpr int kGRing = 3;                                    // blocks in the LDS rings
+constexpr size_t kGXBytes = size_t(kGRing) * kGRows * kFp8Block * sizeof(uint16_t);
+// per block: the codes of the 128 columns (per column tile two 1 KB halves:
+// lane l of half h holds column 16 c + l % 16, bytes 64 h + 16 (l / 16) .. +15
+// of the block), then each wavefront's copy of the block's scale (256 B: one
+// float per lane, all equal)
+constexpr int kGWCodes = kGCols * kFp8Block;
+constexpr int kGWStage = kGWCodes + kGWaves * 256;
+constexpr size_t kGLds = kGXBytes + size_t(kGRing) * kGWStage;
+constexpr int kGWTilesPerWave = kGCols / 16 / kGWaves;
+constexpr int kGWLoads = 3 * kGWTilesPerWave;                // per block: two code halves and the scale
+static_assert(kGWTilesPerWave == 1, "one column tile staged per wavefront");
+static_assert(kGXLoads * 4 * kGWaves == kGRows, "x staging");
+static_assert(kGLds <= size_t(kMaxLdsBytes), "LDS");
+
+struct W8GemmArgs {
+    const uint16_t* x;     // bf16 [M, K]
+    const uint8_t* w;      // e4m3 [N, K]
+    const float* s;        // fp32 [N/128, K/128]
+    void* y;               // [M, N]
+    int m, n, k;
+    int k_per_wave;        // segment length (fp8_tile)
+    int group;             // segments per segment group
+    float* part;           // parts > 1: group sums [parts][M][N] (blockIdx.z is the group)
+    int parts;
+};
+
+template <bool OUT_F32>
+__global__ void __launch_bounds__(kGThreads, 1)
+fp8_w8a16_gemm_kernel(W8GemmArgs a) {
+    extern __shared__ __align__(16) uint16_t xs[];     // [kGRing][kGRows][128], then the weight ring
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm = wave / kGWavesN, wn = wave % kGWavesN;
+    const int col_lane = lane % 16;
+    const int kq = lane / 16;
+    const int row0 = blockIdx.y * kGRows;
+    const int colwg = blockIdx.x * kGCols;
+    const int col0 = colwg + wn * kGC * 16;
+    const int nblocks = a.k / kFp8Block / a.parts;
+    const int kbase = static_cast<int>(blockIdx.z) * nblocks * kFp8Block;
+    const int seg_blocks = a.k_per_wave / kFp8Block;
+
+    // x rows as in nvfp4_gemm_kernel: row r's 16-byte piece p sits at slot
+    // p ^ (r % 16), so the 16 rows of one A read meet 16 bank groups
+    const int xslot = lane % 16;
+    const char* xwg = reinterpret_cast<const char*>(a.x + (int64_t)row0 * a.k + kbase);
+    uint32_t xoff[kGXLoads];
+#pragma unroll
+    for (int i = 0; i < kGXLoads; ++i) {
+        const int r = kGXRowsPerWave * wave + 4 * i + lane / 16;
+        const int rr = min(row0 + r, a.m - 1) - row0;          // rows past M read row M - 1 (never stored)
+        xoff[i] = static_cast<uint32_t>(rr * a.k + 8 * (xslot ^ (r % 16))) * 2u;
+    }
+    auto load_x = [&](int kl, int buf) {
+        const char* base = xwg + 2 * kl;
+#pragma unroll
+        for (int i = 0; i < kGXLoads; ++i)
+            __builtin_amdgcn_global_load_lds(base + xoff[i],
+                                             xs + (buf * kGRows + kGXRowsPerWave * wave + 4 * i) * kFp8Block, 16, 0, 0);
+    };
+    // wavefront w stages column tile w of each block and a copy of its scale
+    uint8_t* wls = reinterpret_cast<uint8_t*>(xs) + kGXBytes;
+    const uint8_t* wsrc = a.w + (int64_t)(colwg + 16 * wave + lane % 16) * a.k + kbase + 16 * (lane / 16);
+    const float* ssrc = a.s + (int64_t)(colwg / kFp8Block) * (a.k / kFp8Block) + kbase / kFp8Block;
+    auto load_w = [&](int kl, int st) {
+        uint8_t* d = wls + st * kGWStage;
+        __builtin_amdgcn_global_load_lds(wsrc + kl, d + wave * 2048, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(wsrc + kl + 64, d + wave * 2048 + 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(ssrc + kl / kFp8Block, d + kGWCodes + wave * 256, 4, 0, 0);
+    };
+
+    f32x4 blk[kGMT][kGC], acc[kGMT][kGC], grp[kGMT][kGC], tot[kGMT][kGC];
+#pragma unroll
+    for (int t = 0; t < kGMT; ++t)
+#pragma unroll
+        for (int c = 0; c < kGC; ++c) acc[t][c] = grp[t][c] = tot[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    load_x(0, 0);
+    load_w(0, 0);
+    if (nblocks > 1) {
+        load_x(kFp8Block, 1);
+        load_w(kFp8Block, 1);
+        gemm_wait_vm<kGXLoads + kGWLoads>();              // block 0 has landed
+    } else {
+        gemm_wait_vm<0>();
+    }
+    gemm_lds_barrier();
+
+    const int nseg = nblocks / seg_blocks;
+    for (int sg = 0; sg < nseg; ++sg) {
+      for (int bb = 0; bb < seg_blocks; ++bb) {
+        const int b = sg * seg_blocks + bb;
+        if (b + 2 < nblocks) {
+            load_x((b + 2) * kFp8Block, (b + 2) % kGRing);
+            load_w((b + 2) * kFp8Block, (b + 2) % kGRing);
+        }
+        const uint16_t* xb = xs + (b % kGRing) * kGRows * kFp8Block;
+        const uint8_t* wst = wls + (b % kGRing) * kGWStage;
+        u32x4 wv[kGC][2];
+#pragma unroll
+        for (int c = 0; c < kGC; ++c) {
+            const int ct = wn * kGC + c;
+            wv[c][0] = *reinterpret_cast<const u32x4*>(wst + ct * 2048 + 16 * lane);
+            wv[c][1] = *reinterpret_cast<const u32x4*>(wst + ct * 2048 + 1024 + 16 * lane);
+        }
+        const float scale = *reinterpret_cast<const float*>(wst + kGWCodes + wave * 256 + 4 * lane);
+        // A operands one MFMA step ahead; step s takes k = slot_k(s, kq) .. + 7
+        u32x4 xa[2][kGMT];
+        auto read_a = [&](u32x4 (&dst)[kGMT], int s) {
+            const int piece = slot_k(s, kq) / 8;
+#pragma unroll
+            for (int t = 0; t < kGMT; ++t) {
+                const int r = wm * 16 * kGMT + 16 * t + col_lane;
+                dst[t] = *reinterpret_cast<const u32x4*>(xb + r * kFp8Block + 8 * (piece ^ col_lane));
+            }
+        };
+#pragma unroll
+        for (int t = 0; t < kGMT; ++t)
+#pragma unroll
+            for (int c = 0; c < kGC; ++c) blk[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        read_a(xa[0], 0);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            if (s < 3) read_a(xa[(s + 1) & 1], s + 1);
+            bf16x8 bv[kGC];
+#pragma unroll
+            for (int c = 0; c < kGC; ++c) {
+                const u32x4 q = wv[c][s / 2];
+                bv[c] = fp8x8_to_bf16(q[2 * (s % 2)], q[2 * (s % 2) + 1]);
+            }
+#pragma unroll
+            for (int t = 0; t < kGMT; ++t)
+#pragma unroll
+                for (int c = 0; c < kGC; ++c)
+                    blk[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[s & 1][t]), bv[c], blk[t][c],
+                                                                        0, 0, 0);
+        }
+        // the block sum joins the segment's chain with its scale
+#pragma unroll
+        for (int t = 0; t < kGMT; ++t)
+#pragma unroll
+            for (int c = 0; c < kGC; ++c)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[t][c][j] = __builtin_fmaf(scale, blk[t][c][j], acc[t][c][j]);
+        if (b + 1 < nblocks) {
+            if (b + 2 < nblocks)
+                gemm_wait_vm<kGXLoads + kGWLoads>();      // block b + 1 has landed
+            else
+                gemm_wait_vm<0>();
+            gemm_lds_barrier();
+        }
+      }
+      // end of segment sg: the two-level order of the tile
+      {
+        const bool gfirst_seg = sg % a.group == 0;
+        const bool gend = (sg + 1) % a.group == 0;
+        const bool first_group = sg / a.group == 0;
+#pragma unroll
+        for (int t = 0; t < kGMT; ++t)
+#pragma unroll
+            for (int c = 0; c < kGC; ++c) {
+                grp[t][c] = gfirst_seg ? acc[t][c] : grp[t][c] + acc[t][c];
+                acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (gend) tot[t][c] = first_group ? grp[t][c] : tot[t][c] + grp[t][c];
+            }
+      }
+    }
+
+    const bool part_out = a.parts > 1;
+    float* dst = part_out ? a.part + (int64_t)blockIdx.z * a.m * a.n : nullptr;
+#pragma unroll
+    for (int t = 0; t < kGMT; ++t)
+#pragma unroll
+        for (int c = 0; c < kGC; ++c) {
+            const int n = col0 + 16 * c + col_lane;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int m = row0 + wm * 16 * kGMT + 16 * t + 4 * kq + j;
+                if (m >= a.m) continue;
+                if (part_out)
+                    dst[(int64_t)m * a.n + n] = grp[t][c][j];
+                else if (OUT_F32)
+                    static_cast<float*>(a.y)[(int64_t)m * a.n + n] = tot[t][c][j];
+                else
+                    static_cast<uint16_t*>(a.y)[(int64_t)m * a.n + n] = f32_to_bf16_rne(tot[t][c][j]);
+            }
+        }
+}
+
 using W8Fn = void (*)(W8Args);
 
 template <int MT>
@@ -260,6 +471,11 @@ void fp8_tile(int64_t n, int64_t k, int* waves, int* group) {
 namespace nvfp4 {
 
 int w8a16_setup() {
+    for (int od = 0; od <= 1; ++od)
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(od ? fp8_w8a16_gemm_kernel<true>
+                                                                  : fp8_w8a16_gemm_kernel<false>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kGLds)) != hipSuccess)
+            return NVFP4_ERR_HIP;
     for (int mt = 1; mt <= 2; ++mt)
         for (int c = 1; c <= 2; ++c)
             for (int xl = 0; xl <= 1; ++xl)
@@ -343,4 +559,63 @@ extern "C" int fp8_w8a16_linear(const void* x_bf16, const uint8_t* w_e4m3, const
     if (hipGetLastError() != hipSuccess) return NVFP4_ERR_HIP;
     if (parts > 1) return nvfp4::launch_ordered_sum(buf, parts, m * n, 1.0f, y, y_dtype, stream);
     return NVFP4_OK;
+}
+
+extern "C" int fp8_w8a16_gemm(const void* x_bf16, const uint8_t* w_e4m3, const float* block_scales, void* y,
+                              int64_t m, int64_t n, int64_t k, int y_dtype, void* stream) {
+    int st = fp8_w8a16_gemm_shape_ok(m, n, k);
+    if (st != NVFP4_OK) return st;
+    if (y_dtype != NVFP4_OUT_BF16 && y_dtype != NVFP4_OUT_F32) return NVFP4_ERR_DTYPE;
+    if (m == 0) return NVFP4_OK;
+    if (!x_bf16 || !w_e4m3 || !block_scales || !y) return NVFP4_ERR_NULL;
+    auto misaligned = [](const void* p, uintptr_t al) { return (reinterpret_cast<uintptr_t>(p) & (al - 1)) != 0; };
+    if (misaligned(x_bf16, 16) || misaligned(w_e4m3, 16) || misaligned(block_scales, 4) ||
+        misaligned(y, y_dtype == NVFP4_OUT_F32 ? 4 : 2))
+        return NVFP4_ERR_ALIGN;
+    st = nvfp4::device_setup();
+    if (st != NVFP4_OK) return st;
+    W8GemmArgs a;
+    a.x = static_cast<const uint16_t*>(x_bf16);
+    a.w = w_e4m3;
+    a.s = block_scales;
+    a.y = y;
+    a.m = static_cast<int>(m);
+    a.n = static_cast<int>(n);
+    a.k = static_cast<int>(k);
+    int waves = 1, group = 1;
+    fp8_tile(n, k, &waves, &group);
+    a.k_per_wave = static_cast<int>(k / waves);
+    a.group = group;
+    a.part = nullptr;
+    a.parts = 1;
+    const int64_t col_tiles = n / kGCols, row_tiles = (m + kGRows - 1) / kGRows;
+    // Tiles for at most half the CUs: one workgroup per segment group, the
+    // group sums added in order by a second kernel through the buffer
+    // nvfp4_init allocates (same bits), as nvfp4_gemm does.
+    const int split = waves / group;
+    float* buf = nullptr;
+    if (split > 1) {
+        size_t bytes = 0;
+        int cus = 256;
+        st = nvfp4::gemm_partials(&buf, &bytes, &cus);
+        if (st != NVFP4_OK) return st;
+        if (buf && 2 * row_tiles * col_tiles <= int64_t(cus) && size_t(split) * size_t(m) * size_t(n) * 4 <= bytes) {
+            a.part = buf;
+            a.parts = split;
+        }
+    }
+    auto fn = y_dtype == NVFP4_OUT_F32 ? fp8_w8a16_gemm_kernel<true> : fp8_w8a16_gemm_kernel<false>;
+    hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(col_tiles), static_cast<unsigned>(row_tiles),
+                                static_cast<unsigned>(a.parts)),
+                       dim3(kGThreads), kGLds, static_cast<hipStream_t>(stream), a);
+    if (hipGetLastError() != hipSuccess) return NVFP4_ERR_HIP;
+    if (a.parts > 1) return nvfp4::launch_ordered_sum(a.part, a.parts, m * n, 1.0f, y, y_dtype, stream);
+    return NVFP4_OK;
+}
+
+extern "C" int fp8_w8a16_matmul(const void* x_bf16, const uint8_t* w_e4m3, const float* block_scales, void* y,
+                                int64_t m, int64_t n, int64_t k, int y_dtype, void* stream) {
+    if (m >= 0 && m <= NVFP4_MAX_M)
+        return fp8_w8a16_linear(x_bf16, w_e4m3, block_scales, y, m, n, k, y_dtype, stream);
+    return fp8_w8a16_gemm(x_bf16, w_e4m3, block_scales, y, m, n, k, y_dtype, stream);
 }

@@ -2,7 +2,8 @@
 (gpu): two 12288x4096 projections over one x, the silu input on 4096x12288,
 the de-interleaved Q|K|V|Z store on 12288x4096, a grouped launch over 128
 experts of 1536x4096, the FP8 product on every decode-round shape at 1, 16
-and 32 rows, and the expanded weight of 8192x4096.  The oracle computes
+and 32 rows and its GEMM at 64 and 1024 rows, and the expanded weight of
+8192x4096.  The oracle computes
 sampled columns (or rows) one by one; the launches are the ones the benchmark
 makes."""
 import numpy as np
@@ -125,3 +126,25 @@ def test_expanded_weight_at_bench_size():
         got = dst[torch.from_numpy(rows).to(DEV)].cpu().numpy().view(np.uint16)
         want = oracle.dequant_bf16(packed[rows], scales[rows], t, bool(apply_t))
         assert np.array_equal(got, want), apply_t
+
+
+@pytest.mark.parametrize("shape", workload.ROUND_SHAPES, ids=lambda s: f"{s.n}x{s.k}")
+def test_fp8_gemm_at_bench_size(shape):
+    codes, scales = nv.fp8_pack(workload.weights_f32(shape.n, shape.k, 21))
+    wd, sd = upload_u8(codes), torch.from_numpy(scales).to(DEV)
+    cols = _cols(shape.n, 7)
+    blocks = np.unique(cols // 128)
+    sub_codes = np.concatenate([codes[128 * b:128 * (b + 1)] for b in blocks])
+    sub_scales = scales[blocks]
+    sub_cols = np.searchsorted(blocks, cols // 128) * 128 + cols % 128
+    for m in (64, 1024):
+        x = workload.activations_bf16(m, shape.k, 23)
+        y = torch.empty((m, shape.n), dtype=torch.bfloat16, device=DEV)
+        assert nv.fp8_gemm_raw(upload_bits(x).data_ptr(), wd.data_ptr(), sd.data_ptr(), y.data_ptr(), m,
+                               shape.n, shape.k, nv.OUT_BF16, _s()) == nv.OK
+        torch.cuda.synchronize()
+        ref = oracle.linear_fp8_ref(x, sub_codes, sub_scales, sub_cols)
+        bnd = oracle.bound_fp8(x, sub_codes, sub_scales, sub_cols)
+        viol = oracle.max_violation(to_f64(y)[:, cols], ref, bnd, "bf16")
+        print(f"[parity] fp8 gemm {shape.n}x{shape.k} M={m} max err/tol = {viol:.3g}", flush=True)
+        assert viol <= 1.0, (m, viol)

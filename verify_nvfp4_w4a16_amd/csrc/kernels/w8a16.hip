@@ -19,7 +19,7 @@
 // fp8_w8a16_gemm_kernel is the same product for any row count (the pages'
 // w8a16_gemm_n128_m128 and pipelined forms for prefill chunks), laid out like
 // nvfp4_gemm_kernel: one workgroup of eight wavefronts per CU owns 128 rows x
-// 128 columns (wavefronts 2 x 4, each 64 rows x 32 columns), x and the e4m3
+// 128 columns (wavefronts 4 x 2, each 32 rows x 64 columns), x and the e4m3
 // codes come into LDS by direct-to-LDS loads two 128-k blocks ahead, and each
 // wavefront walks every segment of K in order, so the MFMA inputs, the block
 // chains and the two-level fold are those of fp8_w8a16_kernel: every row has
@@ -240,8 +240,10 @@ fp8_w8a16_kernel(W8Args a) {
 
 constexpr int kGRows = 128;                 // rows per workgroup
 constexpr int kGCols = 128;                 // columns per workgroup: one scale block
-constexpr int kGMT = 4;                     // 16-row tiles per wavefront
-constexpr int kGC = 2;                      // 16-column tiles per wavefront
+constexpr int kGMT = 2;                     // 16-row tiles per wavefront
+constexpr int kGC = 4;                      // 16-column tiles per wavefront (one decode serves 2 MFMAs:
+                                            // the FP8 decode is cheap, the A reads are not; 2 x 4 tiles
+                                            // measured about 5 % slower)
 constexpr int kGWavesN = kGCols / (16 * kGC);
 constexpr int kGWaves = (kGRows / (16 * kGMT)) * kGWavesN;
 constexpr int kGThreads = kGWaves * kWave;

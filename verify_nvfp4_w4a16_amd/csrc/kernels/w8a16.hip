@@ -286,8 +286,16 @@ fp8_w8a16_gemm_kernel(W8GemmArgs a) {
     const int wm = wave / kGWavesN, wn = wave % kGWavesN;
     const int col_lane = lane % 16;
     const int kq = lane / 16;
-    const int row0 = blockIdx.y * kGRows;
-    const int colwg = blockIdx.x * kGCols;
+    // workgroups are dealt to the eight XCDs round-robin; give each XCD a
+    // contiguous run of tiles in row-major order, so an XCD works on few row
+    // tiles (its x stays in its L2) while the weights stream
+    const int tiles_xy = gridDim.x * gridDim.y;
+    const int lid = blockIdx.x + gridDim.x * blockIdx.y;
+    const int q8 = tiles_xy / 8, r8 = tiles_xy % 8, xcd = lid % 8;
+    const int vid = xcd * q8 + min(xcd, r8) + lid / 8;
+    const int tile_x = vid % gridDim.x, tile_y = vid / gridDim.x;
+    const int row0 = tile_y * kGRows;
+    const int colwg = tile_x * kGCols;
     const int col0 = colwg + wn * kGC * 16;
     const int nblocks = a.k / kFp8Block / a.parts;
     const int kbase = static_cast<int>(blockIdx.z) * nblocks * kFp8Block;

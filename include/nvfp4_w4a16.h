@@ -393,7 +393,8 @@ int fp8_w8a16_gemm_shape_ok(int64_t m, int64_t n, int64_t k);
  * own 128 rows x 128 columns; where that gives workgroups for at most half
  * the CUs and the tile has more than one segment group, the K split goes
  * through the device buffer nvfp4_init allocates (same bits): such calls on
- * one device must not overlap in time.  No allocation, no host sync.
+ * one device must not overlap in time.  No allocation (the first call on a
+ * device runs nvfp4_init's set-up unless it has run), no host sync.
  * Errors: NULL, SHAPE, ALIGN, DTYPE, HIP, DEVICE.
  */
 int fp8_w8a16_gemm(const void* x_bf16, const uint8_t* w_e4m3, const float* block_scales, void* y,

@@ -384,12 +384,18 @@ def next_rows(torch, dev, stream) -> dict:
     torch.cuda.synchronize()
     us_lib = per_call(lambda h: call(nv.gemm_library_raw, x.data_ptr(), wbf.data_ptr(), t,
                                      y.data_ptr(), m, n, k, nv.OUT_BF16, h))
+    # the pages' third regime done per call: expand, then the library GEMM
+    def expand_then_library(h):
+        call(nv.dequant_bf16_raw, wp0.data_ptr(), sc0.data_ptr(), t, 0, wbf.data_ptr(), n, k, h)
+        call(nv.gemm_library_raw, x.data_ptr(), wbf.data_ptr(), t, y.data_ptr(), m, n, k, nv.OUT_BF16, h)
+    us_exp_lib = per_call(expand_then_library)
     out["expand_8192x4096_M4096"] = {"expand_us": us_expand, "expand_GBps_read_plus_write":
                                      (wb + 2 * n * k) / (us_expand * 1e-6) / 1e9,
                                      "gemm_expanded_us": us_exp_gemm, "gemm_nvfp4_us": us_gemm,
                                      "gemm_expanded_TFLOPs": 2.0 * m * n * k / (us_exp_gemm * 1e-6) / 1e12,
                                      "gemm_library_us": us_lib,
-                                     "gemm_library_TFLOPs": 2.0 * m * n * k / (us_lib * 1e-6) / 1e12}
+                                     "gemm_library_TFLOPs": 2.0 * m * n * k / (us_lib * 1e-6) / 1e12,
+                                     "expand_then_library_us": us_exp_lib}
     # the library GEMM on the decode round's shapes at 1024 and 4096 rows
     # against nvfp4_gemm (one weight, warm: both reread it per row tile)
     lib_rows = {}
@@ -408,8 +414,13 @@ def next_rows(torch, dev, stream) -> dict:
                                          y1.data_ptr(), mm, s.n, s.k, nv.OUT_BF16, h))
             ug = per_call(lambda h: call(nv.gemm_raw, x1.data_ptr(), wp1.data_ptr(), sc1.data_ptr(), t1,
                                          y1.data_ptr(), mm, s.n, s.k, nv.OUT_BF16, h))
+            def etl(h):
+                call(nv.dequant_bf16_raw, wp1.data_ptr(), sc1.data_ptr(), t1, 0, wbf1.data_ptr(), s.n, s.k, h)
+                call(nv.gemm_library_raw, x1.data_ptr(), wbf1.data_ptr(), t1, y1.data_ptr(), mm, s.n, s.k,
+                     nv.OUT_BF16, h)
+            ue = per_call(etl)
             fl = 2.0 * mm * s.n * s.k
-            lib_rows[f"{s.n}x{s.k}_M{mm}"] = {"library_us": ul, "nvfp4_gemm_us": ug,
+            lib_rows[f"{s.n}x{s.k}_M{mm}"] = {"library_us": ul, "nvfp4_gemm_us": ug, "expand_then_library_us": ue,
                                                "library_TFLOPs": fl / (ul * 1e-6) / 1e12,
                                                "nvfp4_gemm_TFLOPs": fl / (ug * 1e-6) / 1e12}
         del wbf1

@@ -496,6 +496,25 @@ int nvfp4_gemm_library(const void* x_bf16, const void* w_bf16, float tensor_scal
                        int64_t m, int64_t n, int64_t k, int y_dtype, void* stream);
 
 /*
+ * Device, asynchronous.  All three regimes of "10 Kernels" 10.2's table over
+ * one stored format: nvfp4_matmul below expand_min_m rows (1..32 rows
+ * skinny, then the many-row kernels; every row nvfp4_linear's bits), and from
+ * expand_min_m rows on the third regime: the weight expanded to bf16 into
+ * w_bf16_scratch (device, caller-owned, N * K * 2 bytes, 16-byte aligned; its
+ * contents are overwritten) by nvfp4_dequant_bf16 without the tensor scale,
+ * then nvfp4_gemm_library (those rows carry the library's bits, within the
+ * same error bound).  expand_min_m = 0 takes 1,024, the pages' boundary and
+ * on MI355X about where expanding per call starts to pay; the scratch may be
+ * NULL when M stays below the threshold.  A caller that keeps the expanded
+ * weight calls nvfp4_gemm_library directly.  Shape contract: nvfp4_gemm's.
+ * Errors: SHAPE (also a negative expand_min_m), NULL, and those of the calls
+ * it makes.
+ */
+int nvfp4_matmul_expand(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4m3,
+                        float tensor_scale, void* y, int64_t m, int64_t n, int64_t k, int y_dtype,
+                        void* w_bf16_scratch, int64_t expand_min_m, void* stream);
+
+/*
  * Host.  Writes into buf (NUL-terminated) the kernel nvfp4_linear launches for
  * an M x N x K product with this output type on the current device, as its
  * template name reads in a kernel trace, then its grid, block and LDS bytes

@@ -215,6 +215,41 @@ def test_library_gemm_contract_and_errors():
     assert nv.gemm_library_raw(x.data_ptr(), 0, w.t, y.data_ptr(), 3, 64, 256, nv.OUT_BF16, s) == nv.ERR_NULL
 
 
+def test_matmul_expand_three_regimes():
+    # Below the threshold nvfp4_matmul's bits (the scratch may be NULL); from
+    # it on, the expanded weight through the library: the bits of
+    # nvfp4_dequant_bf16 + nvfp4_gemm_library, within the oracle's tolerance.
+    n, k = 4096, 4096
+    w = Weight.from_f32(workload.weights_f32(n, k, 51))
+    x = workload.activations_bf16(1100, k, 52)
+    xd = upload_bits(x)
+    scratch = torch.empty((n, k), dtype=torch.bfloat16, device=DEV)
+    s = _stream()
+
+    def run(m, scratch_ptr, threshold):
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+        st = nv.matmul_expand_raw(xd.data_ptr(), w.wp.data_ptr(), w.sc.data_ptr(), w.t, y.data_ptr(), m, n, k,
+                                  nv.OUT_BF16, scratch_ptr, threshold, s)
+        torch.cuda.synchronize()
+        assert st == nv.OK, st
+        return y
+
+    for m in (5, 64, 300):
+        assert torch.equal(bits(run(m, 0, 0)), bits(_gemm(xd, w, m, fn=nv.matmul_raw))), m
+    wbf = _expanded(w, False)
+    for m, threshold in ((1100, 0), (300, 256)):
+        y = run(m, scratch.data_ptr(), threshold)
+        assert torch.equal(bits(y), bits(_library(xd, wbf, w, m))), (m, threshold)
+        assert torch.equal(scratch.view(torch.int16), wbf), "scratch holds the expanded weight"
+        cols = np.unique(np.concatenate([np.arange(8), workload.rng(53).integers(0, n, 64)]))
+        check_parity(y, x[:m], w, cols=cols, label=f"matmul_expand M={m}")
+    y = torch.empty((1100, n), dtype=torch.bfloat16, device=DEV)
+    assert nv.matmul_expand_raw(xd.data_ptr(), w.wp.data_ptr(), w.sc.data_ptr(), w.t, y.data_ptr(), 1100, n, k,
+                                nv.OUT_BF16, 0, 0, s) == nv.ERR_NULL
+    assert nv.matmul_expand_raw(xd.data_ptr(), w.wp.data_ptr(), w.sc.data_ptr(), w.t, y.data_ptr(), 1100, n, k,
+                                nv.OUT_BF16, scratch.data_ptr(), -1, s) == nv.ERR_SHAPE
+
+
 def test_gemm_contract_and_errors():
     assert nv.gemm_shape_ok(0, 1, 256) and nv.gemm_shape_ok(4096, 8192, 4096)
     assert not nv.gemm_shape_ok(1, 1, 100) and not nv.gemm_shape_ok(-1, 1, 256)

@@ -29,7 +29,7 @@ EXPORTED = ("nvfp4_pack", "nvfp4_check_scales", "nvfp4_linear_shape_ok", "nvfp4_
             "nvfp4_linear", "nvfp4_linear_tiled", "nvfp4_tile_info", "nvfp4_strerror",
             "nvfp4_timeout_status", "nvfp4_linear_noalloc", "nvfp4_launch_info",
             "nvfp4_read_probe", "nvfp4_gemm_shape_ok", "nvfp4_gemm", "nvfp4_matmul",
-            "nvfp4_dequant_bf16", "nvfp4_gemm_expanded", "nvfp4_gemm_library", "nvfp4_linear_dual", "nvfp4_linear_silu_input",
+            "nvfp4_dequant_bf16", "nvfp4_gemm_expanded", "nvfp4_gemm_library", "nvfp4_matmul_expand", "nvfp4_linear_dual", "nvfp4_linear_silu_input",
             "nvfp4_linear_deinterleave", "nvfp4_linear_grouped", "fp8_w8a16_pack", "fp8_w8a16_shape_ok",
             "fp8_w8a16_linear", "fp8_w8a16_gemm_shape_ok", "fp8_w8a16_gemm", "fp8_w8a16_matmul")
 
@@ -93,6 +93,7 @@ def _load() -> ctypes.CDLL:
     lib.fp8_w8a16_matmul.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
     lib.nvfp4_gemm_expanded.argtypes = [vp, vp, ctypes.c_float, vp, i64, i64, i64, ctypes.c_int, vp]
     lib.nvfp4_gemm_library.argtypes = [vp, vp, ctypes.c_float, vp, i64, i64, i64, ctypes.c_int, vp]
+    lib.nvfp4_matmul_expand.argtypes = [vp, vp, vp, ctypes.c_float, vp, i64, i64, i64, ctypes.c_int, vp, i64, vp]
     lib.nvfp4_strerror.argtypes = [ctypes.c_int]
     lib.nvfp4_strerror.restype = ctypes.c_char_p
     for name in EXPORTED:
@@ -231,6 +232,13 @@ def gemm_library_raw(x_ptr: int, wbf_ptr: int, tensor_scale: float, y_ptr: int,
     """nvfp4_gemm_library on raw device addresses; returns the status."""
     return _lib().nvfp4_gemm_library(x_ptr, wbf_ptr, ctypes.c_float(tensor_scale), y_ptr, m, n, k, y_dtype,
                                      stream)
+
+
+def matmul_expand_raw(x_ptr: int, w_ptr: int, s_ptr: int, tensor_scale: float, y_ptr: int, m: int, n: int, k: int,
+                      y_dtype: int, scratch_ptr: int, expand_min_m: int, stream: int) -> int:
+    """nvfp4_matmul_expand on raw device addresses; returns the status."""
+    return _lib().nvfp4_matmul_expand(x_ptr, w_ptr, s_ptr, ctypes.c_float(tensor_scale), y_ptr, m, n, k, y_dtype,
+                                      scratch_ptr, expand_min_m, stream)
 
 
 def linear_dual_raw(x_ptr, w0_ptr, s0_ptr, t0, y0_ptr, w1_ptr, s1_ptr, t1, y1_ptr, m, n, k, y_dtype,

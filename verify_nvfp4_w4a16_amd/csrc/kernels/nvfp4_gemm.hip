@@ -10,10 +10,9 @@
 // blocks, waited for by count, one barrier per block); each wavefront decodes
 // the weights of its 32 columns from LDS into registers and multiplies them
 // with 64 rows of x (v_mfma_f32_16x16x32_bf16, 4 x 2 tiles), so one decoded
-// operand serves four MFMAs.  Workgroups are dealt to the eight XCDs
-// round-robin; the tile order gives each XCD a contiguous run of tiles in
-// row-major order, so its L2 holds the x rows of few row tiles while the
-// weights stream (2-10 % faster than the plain grid order on MI355X).
+// operand serves four MFMAs.  Column tiles are the fastest grid dimension, so
+// the eight XCDs (workgroups dealt round-robin) each keep one eighth of the
+// weight columns in their L2 across the row tiles.
 //
 // The K order is the one of every other kernel of this library, fixed by the
 // (N, K) tile: K cut into `waves` segments, each one MFMA chain in increasing
@@ -110,16 +109,8 @@ nvfp4_gemm_kernel(GemmArgs a) {
     const int wm = wave / kWavesN, wn = wave % kWavesN;
     const int col_lane = lane % 16;
     const int kq = lane / 16;
-    // workgroups are dealt to the eight XCDs round-robin; give each XCD a
-    // contiguous run of tiles in row-major order, so an XCD works on few row
-    // tiles (its x stays in its L2) while the weights stream
-    const int tiles_xy = gridDim.x * gridDim.y;
-    const int lid = blockIdx.x + gridDim.x * blockIdx.y;
-    const int q8 = tiles_xy / 8, r8 = tiles_xy % 8, xcd = lid % 8;
-    const int vid = xcd * q8 + min(xcd, r8) + lid / 8;
-    const int tile_x = vid % gridDim.x, tile_y = vid / gridDim.x;
-    const int row0 = tile_y * kRows;
-    const int col0 = tile_x * kCols + wn * kC * 16;
+    const int row0 = blockIdx.y * kRows;
+    const int col0 = blockIdx.x * kCols + wn * kC * 16;
     // K blocks of this workgroup: all of K, or one segment group's
     const int nblocks = a.k / kBlockK / a.parts;
     const int kbase = static_cast<int>(blockIdx.z) * nblocks * kBlockK;
@@ -172,8 +163,8 @@ nvfp4_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < kWTilesPerWave; ++j) {
         const int ct = kWTilesPerWave * wave + j;
-        const int wcol = min(tile_x * kCols + 16 * ct + lane % 16, a.n - 1);
-        const int scol = min(tile_x * kCols + 16 * ct + (lane % 32) / 2, a.n - 1);
+        const int wcol = min(static_cast<int>(blockIdx.x) * kCols + 16 * ct + lane % 16, a.n - 1);
+        const int scol = min(static_cast<int>(blockIdx.x) * kCols + 16 * ct + (lane % 32) / 2, a.n - 1);
         wsrc[j] = a.wp + (int64_t)wcol * (a.k / 2) + kbase / 2 + 16 * (lane / 16);
         ssrc[j] = a.sc + (int64_t)scol * (a.k / 16) + kbase / 16 + 4 * (lane % 2);
     }

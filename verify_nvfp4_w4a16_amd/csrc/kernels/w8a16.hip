@@ -19,7 +19,7 @@
 // fp8_w8a16_gemm_kernel is the same product for any row count (the pages'
 // w8a16_gemm_n128_m128 and pipelined forms for prefill chunks), laid out like
 // nvfp4_gemm_kernel: one workgroup of eight wavefronts per CU owns 128 rows x
-// 128 columns (wavefronts 4 x 2, each 32 rows x 64 columns), x and the e4m3
+// 128 columns (wavefronts 2 x 4, each 64 rows x 32 columns), x and the e4m3
 // codes come into LDS by direct-to-LDS loads two 128-k blocks ahead, and each
 // wavefront walks every segment of K in order, so the MFMA inputs, the block
 // chains and the two-level fold are those of fp8_w8a16_kernel: every row has
@@ -240,10 +240,8 @@ fp8_w8a16_kernel(W8Args a) {
 
 constexpr int kGRows = 128;                 // rows per workgroup
 constexpr int kGCols = 128;                 // columns per workgroup: one scale block
-constexpr int kGMT = 2;                     // 16-row tiles per wavefront
-constexpr int kGC = 4;                      // 16-column tiles per wavefront (one decode serves 2 MFMAs:
-                                            // the FP8 decode is cheap, the A reads are not; 2 x 4 tiles
-                                            // measured about 5 % slower)
+constexpr int kGMT = 4;                     // 16-row tiles per wavefront
+constexpr int kGC = 2;                      // 16-column tiles per wavefront
 constexpr int kGWavesN = kGCols / (16 * kGC);
 constexpr int kGWaves = (kGRows / (16 * kGMT)) * kGWavesN;
 constexpr int kGThreads = kGWaves * kWave;
@@ -286,16 +284,8 @@ fp8_w8a16_gemm_kernel(W8GemmArgs a) {
     const int wm = wave / kGWavesN, wn = wave % kGWavesN;
     const int col_lane = lane % 16;
     const int kq = lane / 16;
-    // workgroups are dealt to the eight XCDs round-robin; give each XCD a
-    // contiguous run of tiles in row-major order, so an XCD works on few row
-    // tiles (its x stays in its L2) while the weights stream
-    const int tiles_xy = gridDim.x * gridDim.y;
-    const int lid = blockIdx.x + gridDim.x * blockIdx.y;
-    const int q8 = tiles_xy / 8, r8 = tiles_xy % 8, xcd = lid % 8;
-    const int vid = xcd * q8 + min(xcd, r8) + lid / 8;
-    const int tile_x = vid % gridDim.x, tile_y = vid / gridDim.x;
-    const int row0 = tile_y * kGRows;
-    const int colwg = tile_x * kGCols;
+    const int row0 = blockIdx.y * kGRows;
+    const int colwg = blockIdx.x * kGCols;
     const int col0 = colwg + wn * kGC * 16;
     const int nblocks = a.k / kFp8Block / a.parts;
     const int kbase = static_cast<int>(blockIdx.z) * nblocks * kFp8Block;

@@ -84,8 +84,12 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+WARM_MS = 20.0      # replay at least this long before timing: a graph timed right after a pause ran up to 10 % slow
+
+
 def timed_graph(torch, stream, fn, reps: int = 5, warm: int = 2) -> float:
-    """Median milliseconds of one replay of a graph capturing fn(stream_handle)."""
+    """Median milliseconds of one replay of a graph capturing fn(stream_handle),
+    after at least `warm` replays and WARM_MS of them."""
     g = torch.cuda.CUDAGraph()
     stream.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(stream):
@@ -95,6 +99,12 @@ def timed_graph(torch, stream, fn, reps: int = 5, warm: int = 2) -> float:
     torch.cuda.synchronize()
     ts = []
     with torch.cuda.stream(stream):
+        s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        g.replay()
+        e0.record(stream)
+        e0.synchronize()
+        warm = max(warm, min(200, int(WARM_MS / max(s0.elapsed_time(e0), 1e-3))))
         for i in range(warm + reps):
             s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             s.record(stream)
@@ -603,7 +613,11 @@ def main() -> int:
                     help="only run a 1 GiB device copy 5 times (counter calibration) and exit")
     ap.add_argument("--next-only", action="store_true",
                     help="only time the other regimes and forms (GEMM, expand, fused, grouped, FP8) and exit")
+    ap.add_argument("--warm-ms", type=float, default=WARM_MS,
+                    help="replay each timed graph at least this long before timing it (0: two replays; "
+                         "for counter collection, which does not need warm clocks)")
     args = ap.parse_args()
+    globals()["WARM_MS"] = args.warm_ms
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the NVFP4 skinny product has no collective; "

@@ -270,10 +270,12 @@ int nvfp4_linear_dual(const void* x_bf16, const uint8_t* w_packed0, const uint8_
  * activation is silu(gate) * up, formed per element from the bf16 gate
  * [M, K] and up [M, K] (16-byte aligned): silu(g) = g / (1 + exp(-g)) and
  * the product with u in fp32, rounded once to bf16, then the product of
- * nvfp4_linear with that x (same bits as nvfp4_linear on it).  One call, two
- * launches: a small kernel writes the activation (M * K * 2 bytes) to the
- * device buffer nvfp4_init allocates, then nvfp4_linear runs on it; calls
- * that use the device workspace must not overlap in time on one device.
+ * nvfp4_linear with that x (same bits as nvfp4_linear on it).  At M = 1,
+ * where the product runs on the per-tile kernel, one launch: each wavefront
+ * forms the activation of its K slice in LDS.  Otherwise two launches: a
+ * small kernel writes the activation (M * K * 2 bytes) to the device buffer
+ * nvfp4_init allocates, then nvfp4_linear runs on it; calls that use the
+ * device workspace must not overlap in time on one device.
  * Errors: NULL, SHAPE, ALIGN, DTYPE, HIP (also: the device buffer could not
  * be allocated), DEVICE, TILEFILE.
  */

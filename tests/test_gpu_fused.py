@@ -82,6 +82,16 @@ def test_silu_input_forms_the_activation_once_and_multiplies_it():
     # apart at most, and only where the value sits next to a rounding midpoint
     assert off.mean() < 2e-3, off.mean()
     assert np.all(np.abs(h_bits.astype(np.int32)[off] - h_ref.astype(np.int32)[off]) == 1)
+    # at one row the activation is formed inside the product's kernel: the
+    # same bits as the activation formed first (here read back through the
+    # identity weight), also for gate values where silu saturates or vanishes
+    edge = g[:1].copy()
+    edge[0, :8] = workload.f32_to_bf16_bits(np.array([0.0, -0.0, 1e-30, -1e-30, 88.0, -88.0, 1e4, -1e4],
+                                                    dtype=np.float32))
+    ed = upload_bits(edge)
+    h_one = _silu(ed, ud[:1], _identity_weight(k), 1, torch.float32)
+    h_two = _silu(torch.cat([ed, ed]), torch.cat([ud[:1], ud[:1]]), _identity_weight(k), 2, torch.float32)
+    assert torch.equal(bits(h_one), bits(h_two[:1]))
     # the fused product equals nvfp4_linear on that activation, bit for bit
     w = Weight.from_f32(workload.weights_f32(n, k, 23))
     for mm in (1, 3, 7, 8, 17, 32):

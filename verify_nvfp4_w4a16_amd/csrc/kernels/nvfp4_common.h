@@ -66,6 +66,17 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return out;
 }
 
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return bits_f32(uint32_t(b) << 16); }
+
+// silu(g) * u in fp32 (one division and the library exponential), rounded
+// once to bf16: the activation of "Module ops" w4a16_gemv_silu_input.  One
+// definition for every kernel that forms it, so they agree bit for bit.
+__device__ __forceinline__ uint16_t silu_mul(uint16_t g, uint16_t u) {
+    const float gf = bf16_to_f32(g);
+    const float s = gf / (1.0f + expf(-gf));
+    return f32_to_bf16_rne(s * bf16_to_f32(u));
+}
+
 __device__ __forceinline__ u32x4 load16_stream(const void* p) {
     // Weights are read exactly once: a non-temporal load keeps them from
     // displacing the activations in the caches.

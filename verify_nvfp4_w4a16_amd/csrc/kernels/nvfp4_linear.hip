@@ -83,6 +83,9 @@ struct Args {
     int slice_rows;
     int rows_total;
     int y_bytes;           // bytes per output element (2 or 4)
+    // The silu input (per-tile kernel only): x is the gate, xu the up
+    // activation, and the kernel multiplies silu(x) * xu (rounded to bf16).
+    const uint16_t* xu;
 };
 
 // The product of this workgroup (blockIdx.y) in a several-product launch;
@@ -799,9 +802,12 @@ nvfp4_skinny_tile(Args a_in) {
     const int xpitch = ks + 8;
     const uint32_t row_bytes = static_cast<uint32_t>(a.k) / 2;
     const uint32_t scale_bytes = static_cast<uint32_t>(a.k) / 16;
-    const int wave_bytes = a.m * xpitch * 2 + NB * C * kTileBytes;
+    // the silu input: the up slice follows the gate slice
+    const bool silu = MULTI && a.xu != nullptr;
+    const int xbytes = a.m * xpitch * 2 * (silu ? 2 : 1);
+    const int wave_bytes = xbytes + NB * C * kTileBytes;
     uint16_t* xs = reinterpret_cast<uint16_t*>(ldsb + wave * wave_bytes);
-    uint8_t* wbuf = ldsb + wave * wave_bytes + a.m * xpitch * 2;
+    uint8_t* wbuf = ldsb + wave * wave_bytes + xbytes;
     const int col0 = (int)blockIdx.x * 16 * C;
     const int k0 = wave * ks;
 
@@ -815,6 +821,12 @@ nvfp4_skinny_tile(Args a_in) {
         __builtin_amdgcn_global_load_lds(a.x + (int64_t)r * a.k + k0 + p * kChunkK + 8 * xpiece(lane, r),
                                          xs + r * xpitch + p * kChunkK, 16, 0, 0);
     }
+    if (silu)
+        for (int i = 0; i < a.m * nch; ++i) {
+            const int r = i / nch, p = i % nch;
+            __builtin_amdgcn_global_load_lds(a.xu + (int64_t)r * a.k + k0 + p * kChunkK + 8 * xpiece(lane, r),
+                                             xs + a.m * xpitch + r * xpitch + p * kChunkK, 16, 0, 0);
+        }
     auto issue = [&](int j) {
         const uint32_t kb = static_cast<uint32_t>(k0 + j * kChunkK) / 2;
         uint8_t* dst = wbuf + (j % NB) * C * kTileBytes;
@@ -838,6 +850,31 @@ nvfp4_skinny_tile(Args a_in) {
     // NB - 1 chunks ahead; the last ones peeled so no load is repeated.
     constexpr int kAhead = NB - 1;
     for (int q = 0; q < kAhead && q < nch; ++q) issue(q);
+    if (silu) {
+        // The gate and up slices have landed (the chunk loads issued after
+        // them may still be in flight); each lane turns the 16 bytes its own
+        // loads brought in into the activation, in place over the gate.  The
+        // store is one the compiler does not track, so it does not wait for
+        // the chunk loads; LDS operations of one wavefront run in order.
+        if (nch >= kAhead)
+            wait_vm<kAhead * kDmaPerTile * C>();
+        else
+            wait_vm<0>();
+        for (int i = 0; i < a.m * nch; ++i) {
+            const int r = i / nch, p = i % nch;
+            uint16_t* g = xs + r * xpitch + p * kChunkK + 8 * lane;
+            uint16_t gv[8], uv[8], hv[8];
+            const u32x4 gw = *reinterpret_cast<const u32x4*>(g);
+            const u32x4 uw = *reinterpret_cast<const u32x4*>(g + a.m * xpitch);
+            __builtin_memcpy(gv, &gw, 16);
+            __builtin_memcpy(uv, &uw, 16);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) hv[e] = silu_mul(gv[e], uv[e]);
+            f32x4 hw;
+            __builtin_memcpy(&hw, hv, 16);
+            lds_store_f32x4(reinterpret_cast<float*>(g), hw);
+        }
+    }
     int j = 0;
     for (; j + kAhead < nch; ++j) {
         issue(j + kAhead);
@@ -861,7 +898,7 @@ nvfp4_skinny_tile(Args a_in) {
     lds_barrier();
     if (wave != 0) return;
     fold_waves<C, MT>(
-        acc, [&](int w2) { return reinterpret_cast<const float*>(ldsb + w2 * wave_bytes + a.m * xpitch * 2); },
+        acc, [&](int w2) { return reinterpret_cast<const float*>(ldsb + w2 * wave_bytes + xbytes); },
         waves, a.group, lane);
 #pragma unroll
     for (int c = 0; c < C; ++c) {
@@ -1666,6 +1703,7 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
         a.slice_rows = ml->slice_rows;
         a.rows_total = ml->rows_total;
         a.y_bytes = y_dtype == NVFP4_OUT_F32 ? 4 : 2;
+        a.xu = static_cast<const uint16_t*>(ml->up);
     }
     const int c = tile.cols / 16;
     const hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -1703,7 +1741,7 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
         const int64_t want = std::min<int64_t>(3, tile_per_cu);
         while (tnb > 1 && tile_resident(tnb) < want && tile_resident(tnb - 1) > tile_resident(tnb)) --tnb;
     }
-    const size_t tile_bytes = tile_lds_bytes(m, ks, tile.waves, pc, tnb);
+    size_t tile_bytes = tile_lds_bytes(m, ks, tile.waves, pc, tnb);
     const bool tile_ok = tile.cols <= 32 && ks % kChunkK == 0 && tile_bytes + 256 <= size_t(kMaxLdsBytes);
     // Measured on MI355X (decode-round and output-head shapes, M = 1..8): the
     // per-tile kernel leads at one row; up to four rows too (its workgroups
@@ -1718,6 +1756,19 @@ int launch(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4
     const bool tile_first =
         tile_ok && (m == 1 || (m <= 4 && !(many_rounds && split_ok && tile.split == 1)) ||
                     (m <= 8 && tile_resident(tnb) >= tile_per_cu));
+    if (ml && ml->up) {
+        // The silu input runs in one kernel only where the product's own
+        // choice is the per-tile kernel and its LDS also holds the up slices
+        // (as many chunk buffers as fit); otherwise the caller forms the
+        // activation first.
+        if (kernel != NVFP4_KERNEL_AUTO || !tile_first) return nvfp4::kNotFused;
+        int snb = tnb;
+        while (snb > 1 && tile_lds_bytes(2 * m, ks, tile.waves, pc, snb) + 256 > size_t(kMaxLdsBytes)) --snb;
+        if (tile_lds_bytes(2 * m, ks, tile.waves, pc, snb) + 256 > size_t(kMaxLdsBytes)) return nvfp4::kNotFused;
+        tnb = snb;
+        tile_bytes = tile_lds_bytes(2 * m, ks, tile.waves, pc, snb);
+        kernel = NVFP4_KERNEL_TILE;
+    }
     if (kernel == NVFP4_KERNEL_AUTO) {
         // The fixed scratch has a stated size: a call whose exchange would
         // need more of it is refused, not run another way.

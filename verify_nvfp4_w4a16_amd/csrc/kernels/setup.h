@@ -46,7 +46,13 @@ struct MultiLaunch {
     int omap_ngroups = 0;
     int slice_rows = 0;                     // row slices of one product: count slices of x and y
     int rows_total = 0;                     // rows of that product (m is then the slice's rows)
+    const void* up = nullptr;               // the silu input: x is the gate, this the up activation
 };
+
+// launch_multi's answer when a silu-input launch cannot run in one kernel
+// (its form would not be the per-tile kernel, or that kernel's LDS would not
+// hold the up slice too); nothing was launched.
+constexpr int kNotFused = 1;
 
 // nvfp4_linear's dispatch and kernels for such a launch; m bounds every
 // product's rows.  Arguments are validated as nvfp4_linear does, except the

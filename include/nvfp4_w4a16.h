@@ -365,12 +365,18 @@ int fp8_w8a16_shape_ok(int64_t m, int64_t n, int64_t k);
  * starts from zero and joins the row's chain as one fused multiply-add by its
  * scale, blocks in increasing k; K is cut into segments (a function of N and
  * K) added in a fixed order, so a row's bits do not depend on M ("10 Kernels"
- * 10.1).  M == 0 launches nothing; no host sync.  At 17..32 rows on weights
- * with fewer than 32 columns per CU the segment groups run in separate
- * workgroups and a second kernel adds their sums in order, through the device
- * buffer nvfp4_init allocates (the first such call on a device runs that
- * set-up): calls that use the device workspace must not overlap in time on
- * one device.
+ * 10.1).  M == 0 launches nothing; no host sync.  Where x [M, K] does not
+ * fit 64 KB of LDS and K's segments are whole 512-k windows, the many-row
+ * kernel runs it (the same bits): x in windows shared by a workgroup's
+ * columns; where fewer than one workgroup per CU would hold every segment
+ * group, the groups run in separate workgroups and meet through nvfp4_init's
+ * workspace (tagged sums, as nvfp4_linear's many-row kernel; a consumer that
+ * gives up writes NaN and sets the word nvfp4_timeout_status reads).
+ * Otherwise, at 17..32 rows on weights with fewer than 32 columns per CU, the
+ * segment groups run in separate workgroups and a second kernel adds their
+ * sums in order, through the device buffer nvfp4_init allocates.  The first
+ * call on a device that needs the workspace runs nvfp4_init's set-up: calls
+ * that use it must not overlap in time on one device.
  * Errors: NULL, SHAPE, ALIGN, DTYPE, HIP, DEVICE, TILEFILE.
  */
 int fp8_w8a16_linear(const void* x_bf16, const uint8_t* w_e4m3, const float* block_scales, void* y,

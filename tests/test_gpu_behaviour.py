@@ -175,6 +175,21 @@ for m, expect_nan in ((17, True), (32, True), (1, False)):
     # the host sees the time-out through the status word, which reading clears
     assert nv.timeout_status() == expect_nan, m
     assert not nv.timeout_status()
+# the FP8 product's many-row form meets through the same exchange (4096
+# columns: groups in separate workgroups); one row takes the register path
+codes, fscales = nv.fp8_pack(workload.weights_f32(n, k, 7))
+wd, sd = torch.from_numpy(codes).to(dev), torch.from_numpy(fscales).to(dev)
+for m, expect_nan in ((16, True), (1, False)):
+    xb = workload.activations_bf16(m, k, 60 + m)
+    x = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
+    y = torch.empty((m, n), dtype=torch.float32, device=dev)
+    st = nv.fp8_linear_raw(x.data_ptr(), wd.data_ptr(), sd.data_ptr(), y.data_ptr(), m, n, k, nv.OUT_F32,
+                           torch.cuda.current_stream().cuda_stream)
+    assert st == nv.OK, st
+    torch.cuda.synchronize()
+    nan = torch.isnan(y)
+    assert bool(nan.all()) if expect_nan else not bool(nan.any()), ("fp8", m, int(nan.sum()))
+    assert nv.timeout_status() == expect_nan, ("fp8", m)
 print("timeout path ok", flush=True)
 """
 

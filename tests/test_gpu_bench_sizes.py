@@ -112,6 +112,12 @@ def test_fp8_at_bench_size(shape):
         viol = oracle.max_violation(to_f64(y)[:, cols], ref, bnd, "bf16")
         print(f"[parity] fp8 {shape.n}x{shape.k} M={m} max err/tol = {viol:.3g}", flush=True)
         assert viol <= 1.0, (m, viol)
+        # the many-row GEMM gives every row the same bits
+        yg = torch.empty_like(y)
+        assert nv.fp8_gemm_raw(upload_bits(x).data_ptr(), wd.data_ptr(), sd.data_ptr(), yg.data_ptr(), m,
+                               shape.n, shape.k, nv.OUT_BF16, _s()) == nv.OK
+        torch.cuda.synchronize()
+        assert torch.equal(bits(yg), bits(y)), m
 
 
 def test_expanded_weight_at_bench_size():

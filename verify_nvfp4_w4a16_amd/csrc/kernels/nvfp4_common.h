@@ -39,6 +39,16 @@ __device__ __forceinline__ bf16x8 decode8(uint32_t w, float scale) {
     return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// Eight e4m3 codes (two dwords) as a bf16 B operand, exactly (e4m3 has 4
+// significant bits).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+    return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 // fp32 <-> its bits through memcpy: with this compiler, bit-casting a vector
 // element (v[j]) yields element 0 for every j.
 __device__ __forceinline__ uint32_t f32_bits(float f) {

@@ -976,9 +976,113 @@ constexpr int kXPitch = kChunkK + 8;        // LDS row pitch of an x window (bf1
 constexpr int kGenBlock = 1024;             // workspace words per generation word
 constexpr int kMaxParts = 8;                // largest split
 
-template <int C, int MT, int W, bool OUT_F32, bool MULTI>
-__global__ void __launch_bounds__(64 * W)
-nvfp4_skinny_split(SplitArgs sa) {
+// Weight formats of the many-row kernel.  For one 512-k window of one
+// 16-column tile: the LDS bytes it takes (kBytes), the direct-to-LDS loads
+// that bring it in (kDma, issued by `issue`; the last kDmaSecond of them hold
+// the window's second half, blocks 2 and 3), and `mma`, which multiplies half
+// H of a staged window into the chains acc[C][MT] with the A operands of x
+// rows xr from an x window laid out as `issue_x` stages it.
+
+// NVFP4: the chunk layout and MFMA sequence of every NVFP4 kernel.
+struct Nvfp4Window {
+    static constexpr int kBytes = kTileBytes;
+    static constexpr int kDma = kDmaPerTile;
+    static constexpr int kDmaSecond = kDmaHalf1;
+    __device__ static __forceinline__ void issue(uint8_t* dst, const Args& a, int row0, int kwin, int lane) {
+        issue_tile_chunk(dst, a.wp, a.sc, row0, a.n - 1, static_cast<uint32_t>(a.k) / 2,
+                         static_cast<uint32_t>(a.k) / 16, static_cast<uint32_t>(kwin) / 2, lane);
+    }
+    template <int C, int MT, int H>
+    __device__ static __forceinline__ void mma(f32x4 (&acc)[C][MT], const uint8_t* wsrc, const uint16_t* xsrc,
+                                               int pitch, const int (&xr)[MT], int col_lane, int kq) {
+        mma_half<C, MT, H>(acc, wsrc, xsrc, pitch, xr, col_lane, kq);
+    }
+};
+
+// FP8 block-scaled weights ("10 Kernels" 10.3): e4m3 codes [N, K] (Args::wp)
+// and fp32 scales [N/128, K/128] (Args::sc).  A window of a tile holds 256
+// bytes of scales (lane i's word: the tile's scale of the window's block
+// i % 4; a 16-column tile lies in one 128-row scale block), then blocks 0-1
+// and blocks 2-3 as 16 rows x 256 bytes each, the 16-byte piece p of row n at
+// slot p ^ n so that the 16 rows of one B read meet 16 bank groups.  Each
+// 128-k block is four MFMAs from zero, then fma(scale, block, chain): the
+// arithmetic of fp8_w8a16_kernel, with the same k in each MFMA slot.
+struct Fp8Window {
+    static constexpr int kBytes = 256 + 2 * 16 * 256;
+    static constexpr int kDma = 9;
+    static constexpr int kDmaSecond = 4;
+    __device__ static __forceinline__ void issue(uint8_t* dst, const Args& a, int row0, int kwin, int lane) {
+        const int nmax = a.n - 1;
+        const float* sc = reinterpret_cast<const float*>(a.sc) + (int64_t)(min(row0, nmax) / 128) * (a.k / 128) +
+                          kwin / 128;
+        __builtin_amdgcn_global_load_lds(sc + lane % 4, dst, 4, 0, 0);
+        const int r = lane / 16, j = lane % 16;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int n = 4 * (u % 4) + r;
+            const int row = min(row0 + n, nmax);
+            __builtin_amdgcn_global_load_lds(a.wp + (int64_t)row * a.k + kwin + 256 * (u / 4) + 16 * (j ^ n),
+                                             dst + 256 + 4096 * (u / 4) + 1024 * (u % 4), 16, 0, 0);
+        }
+    }
+    template <int MT>
+    struct Ops {
+        u32x4 xa[MT][4];
+        u32x4 w[2];
+        float s;
+    };
+    template <int C, int MT, int H>
+    __device__ static __forceinline__ void mma(f32x4 (&acc)[C][MT], const uint8_t* wsrc, const uint16_t* xsrc,
+                                               int pitch, const int (&xr)[MT], int col_lane, int kq) {
+        static_assert(C == 1, "one column tile per wavefront");
+        Ops<MT> ops[2];
+        // MFMA slot s of lane quarter kq takes k = 64 (s / 2) + 16 kq + 8 (s % 2) .. + 7 of the block:
+        // 32-k quarter 2 (s / 2) + kq / 2 of the staged x row, eighth 2 (kq % 2) + s % 2
+        auto fetch = [&](Ops<MT>& o, int b) {
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    o.xa[t][s] = *reinterpret_cast<const u32x4*>(
+                        xsrc + xr[t] * pitch + kBlockK * b + 32 * xslot(2 * (s / 2) + kq / 2, xr[t]) +
+                        16 * (kq % 2) + 8 * (s % 2));
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                o.w[h] = *reinterpret_cast<const u32x4*>(wsrc + 256 + 4096 * (b / 2) + 256 * col_lane +
+                                                         16 * ((8 * (b % 2) + 4 * h + kq) ^ col_lane));
+            o.s = *reinterpret_cast<const float*>(wsrc + 4 * b);
+        };
+        fetch(ops[0], 2 * H);
+#pragma unroll
+        for (int b = 2 * H; b < 2 * H + 2; ++b) {
+            const Ops<MT>& o = ops[b & 1];
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0); vmcnt and expcnt not waited for
+            __builtin_amdgcn_sched_barrier(0);
+            if (b + 1 < 2 * H + 2) fetch(ops[(b + 1) & 1], b + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4 blk[MT];
+#pragma unroll
+            for (int t = 0; t < MT; ++t) blk[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const u32x4 q = o.w[s / 2];
+                const bf16x8 bv = fp8x8_to_bf16(q[2 * (s % 2)], q[2 * (s % 2) + 1]);
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+                    blk[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(o.xa[t][s]), bv, blk[t], 0, 0, 0);
+            }
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[0][t][j] = __builtin_fmaf(o.s, blk[t][j], acc[0][t][j]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+};
+
+template <class F, int C, int MT, int W, bool OUT_F32, bool MULTI>
+__device__ __forceinline__ void split_body(const SplitArgs& sa) {
     constexpr int kXLoads = (16 * MT + W - 1) / W;      // x rows one wavefront loads per window
     extern __shared__ __align__(16) uint16_t lds[];    // x windows [2][M][kXPitch] | chunk buffers
     Args a_entry;
@@ -1029,9 +1133,7 @@ nvfp4_skinny_split(SplitArgs sa) {
     auto tag_of = [&](int q, int i) { return (blk(q, i) == blk(q, 0) ? glo[q] : ghi[q]) + 1; };
     const int slice = a.m * kXPitch;
     const int col_base = (cgroup * W + wave) * 16 * C;
-    const uint32_t row_bytes = static_cast<uint32_t>(a.k) / 2;
-    const uint32_t scale_bytes = static_cast<uint32_t>(a.k) / 16;
-    uint8_t* wbuf = reinterpret_cast<uint8_t*>(lds + 2 * slice) + wave * 2 * C * kTileBytes;
+    uint8_t* wbuf = reinterpret_cast<uint8_t*>(lds + 2 * slice) + wave * 2 * C * F::kBytes;
 
     int xr[MT];
 #pragma unroll
@@ -1049,12 +1151,10 @@ nvfp4_skinny_split(SplitArgs sa) {
         }
     };
     auto issue_w = [&](int win) {
-        const uint32_t kb = static_cast<uint32_t>(kbase + win * kChunkK) / 2;
-        uint8_t* dst = wbuf + (win & 1) * C * kTileBytes;
+        const int kwin = kbase + win * kChunkK;
+        uint8_t* dst = wbuf + (win & 1) * C * F::kBytes;
 #pragma unroll
-        for (int c = 0; c < C; ++c)
-            issue_tile_chunk(dst + c * kTileBytes, a.wp, a.sc, col_base + 16 * c, a.n - 1, row_bytes, scale_bytes,
-                             kb, lane);
+        for (int c = 0; c < C; ++c) F::issue(dst + c * F::kBytes, a, col_base + 16 * c, kwin, lane);
     };
 
     f32x4 acc[C][MT], grp[C][MT], tot[C][MT];
@@ -1064,8 +1164,8 @@ nvfp4_skinny_split(SplitArgs sa) {
         for (int t = 0; t < MT; ++t) acc[c][t] = grp[c][t] = tot[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     auto compute_half = [&](int win, auto h) {
-        mma_half<C, MT, decltype(h)::value>(acc, wbuf + (win & 1) * C * kTileBytes, lds + (win & 1) * slice,
-                                            kXPitch, xr, col_lane, kq);
+        F::template mma<C, MT, decltype(h)::value>(acc, wbuf + (win & 1) * C * F::kBytes, lds + (win & 1) * slice,
+                                                   kXPitch, xr, col_lane, kq);
     };
     // window win: its first half is in LDS (and, with `barrier`, every
     // wavefront's x rows of it); waits for the second half (at most `after`
@@ -1107,10 +1207,10 @@ nvfp4_skinny_split(SplitArgs sa) {
         issue_w(0);
         issue_x(1);
         issue_w(1);
-        wait_vm<kXLoads + kDmaPerTile * C + kDmaHalf1>();   // window 0's x rows and first half have landed
+        wait_vm<kXLoads + F::kDma * C + F::kDmaSecond>();   // window 0's x rows and first half have landed
         lds_barrier();                                      // ... for every wavefront
-        compute(0, std::integral_constant<int, kXLoads + kDmaPerTile * C>{});
-        wait_vm<kDmaHalf1>();
+        compute(0, std::integral_constant<int, kXLoads + F::kDma * C>{});
+        wait_vm<F::kDmaSecond>();
         lds_barrier();
         compute(1, std::integral_constant<int, 0>{});
     } else {
@@ -1118,18 +1218,18 @@ nvfp4_skinny_split(SplitArgs sa) {
         // flight.
         issue_x(0);
         issue_w(0);
-        wait_vm<kDmaHalf1>();                       // x rows and the first half of window 0
+        wait_vm<F::kDmaSecond>();                       // x rows and the first half of window 0
         lds_barrier();
         int win = 0;
         for (; win + 1 < nwin; ++win) {
             issue_x(win + 1);
             issue_w(win + 1);
-            wait_vm<kXLoads + kDmaPerTile * C + kDmaHalf1>();   // window win's first half has landed
-            compute(win, std::integral_constant<int, kXLoads + kDmaPerTile * C>{});
-            wait_vm<kDmaPerTile * C>();             // this wavefront's x rows of win + 1 have landed
+            wait_vm<kXLoads + F::kDma * C + F::kDmaSecond>();   // window win's first half has landed
+            compute(win, std::integral_constant<int, kXLoads + F::kDma * C>{});
+            wait_vm<F::kDma * C>();             // this wavefront's x rows of win + 1 have landed
             lds_barrier();                          // ... and everyone's; buffer win & 1 is free
         }
-        wait_vm<kDmaHalf1>();
+        wait_vm<F::kDmaSecond>();
         compute(win, std::integral_constant<int, 0>{});
     }
 
@@ -1246,9 +1346,23 @@ nvfp4_skinny_split(SplitArgs sa) {
     }
 }
 
-// LDS bytes of the many-row kernel (dynamic part).
-size_t split_lds_bytes(int64_t m, int w, int c) {
-    return 2 * size_t(m) * kXPitch * sizeof(uint16_t) + size_t(w) * 2 * c * kTileBytes;
+template <int C, int MT, int W, bool OUT_F32, bool MULTI>
+__global__ void __launch_bounds__(64 * W)
+nvfp4_skinny_split(SplitArgs sa) {
+    split_body<Nvfp4Window, C, MT, W, OUT_F32, MULTI>(sa);
+}
+
+// The many-row kernel on FP8 block-scaled weights (a.t is 1).
+template <int MT, int W, bool OUT_F32>
+__global__ void __launch_bounds__(64 * W)
+fp8_w8a16_split(SplitArgs sa) {
+    split_body<Fp8Window, 1, MT, W, OUT_F32, false>(sa);
+}
+
+// LDS bytes of the many-row kernel (dynamic part); tile_bytes: a window of
+// one column tile.
+size_t split_lds_bytes(int64_t m, int w, int c, int tile_bytes = kTileBytes) {
+    return 2 * size_t(m) * kXPitch * sizeof(uint16_t) + size_t(w) * 2 * c * tile_bytes;
 }
 
 using KernelFn = void (*)(Args);
@@ -1352,6 +1466,19 @@ SplitFn pick_split(int mt, int c, int w, int y_dtype) {
     return mt == 1 ? pick_s_w<1>(c, w, y_dtype) : pick_s_w<2>(c, w, y_dtype);
 }
 
+template <int MT>
+SplitFn pick_f8s_w(int w, bool f) {
+    if (w == 2) return f ? fp8_w8a16_split<MT, 2, true> : fp8_w8a16_split<MT, 2, false>;
+    if (w == 4) return f ? fp8_w8a16_split<MT, 4, true> : fp8_w8a16_split<MT, 4, false>;
+    return f ? fp8_w8a16_split<MT, 6, true> : fp8_w8a16_split<MT, 6, false>;
+}
+
+// The FP8 many-row kernel; w: wavefronts per workgroup (2, 4 or 6)
+SplitFn pick_fp8_split(int mt, int w, int y_dtype) {
+    const bool f = y_dtype == NVFP4_OUT_F32;
+    return mt == 1 ? pick_f8s_w<1>(w, f) : pick_f8s_w<2>(w, f);
+}
+
 constexpr int kMaxDevices = 64;
 constexpr size_t kWorkBytes = size_t(32) << 20;      // tagged group sums of the many-row kernel
 constexpr size_t kGenWords = kWorkBytes / sizeof(uint64_t) / kGenBlock;   // one per block of them
@@ -1432,6 +1559,9 @@ int setup_device(int dev) {
             for (int c = 1; c <= 2; ++c)
                 for (int w = 4; w <= 8; w += 2)
                     if (!allow_full_lds(pick_split(mt, c, w, od))) return NVFP4_ERR_HIP;
+            if (!(od & kMulti))
+                for (int w = 2; w <= 6; w += 2)
+                    if (!allow_full_lds(pick_fp8_split(mt, w, od))) return NVFP4_ERR_HIP;
         }
     int st = nvfp4::gemm_setup();
     if (st == NVFP4_OK) st = nvfp4::w8a16_setup();
@@ -1550,6 +1680,62 @@ int gemm_partials(float** part, size_t* bytes, int* cus) {
         *part = g_dev[dev].gemm_part;
         *bytes = kGemmPartBytes;
     }
+    return NVFP4_OK;
+}
+
+int launch_fp8_split(const void* x, const uint8_t* w, const float* s, void* y, int64_t m, int64_t n, int64_t k,
+                     int y_dtype, int waves, int group, int wg_waves, bool whole, void* stream, bool* launched) {
+    *launched = false;
+    int st = nvfp4_init();
+    if (st != NVFP4_OK) return st;
+    int dev = 0;
+    st = current_device(&dev);
+    if (st != NVFP4_OK) return st;
+    const Workspace& ws = g_dev[dev].heap;
+    const int64_t seg = k / waves;
+    if (m < 1 || m > 32 || seg % kChunkK != 0 || (wg_waves != 2 && wg_waves != 4 && wg_waves != 6))
+        return NVFP4_OK;
+    const int mt = m <= 16 ? 1 : 2;
+    const size_t lds = split_lds_bytes(m, wg_waves, 1, Fp8Window::kBytes);
+    if (lds + 256 > size_t(kMaxLdsBytes)) return NVFP4_OK;
+    const int split = waves / group;
+    const int64_t groups = (n + 16 * wg_waves - 1) / (16 * wg_waves);
+    int parts = 1;
+    int64_t region = 0;
+    if (split > 1 && !whole) {
+        const int64_t slot = int64_t(wg_waves) * mt * 4 * kWave;     // words of one workgroup
+        region = ((split - 1) * slot + kGenBlock - 1) / kGenBlock * kGenBlock;
+        const size_t words = size_t(groups) * size_t(region);
+        if (!ws.sums || words * sizeof(uint64_t) > ws.sum_bytes || words / kGenBlock > ws.gen_words)
+            return NVFP4_OK;
+        parts = split;
+    }
+    Args a{};
+    a.x = static_cast<const uint16_t*>(x);
+    a.wp = w;
+    a.sc = reinterpret_cast<const uint8_t*>(s);
+    a.y = y;
+    a.t = 1.0f;
+    a.m = static_cast<int>(m);
+    a.n = static_cast<int>(n);
+    a.k = static_cast<int>(k);
+    a.k_per_wave = static_cast<int>(seg);
+    a.group = group;
+    SplitArgs sa;
+    sa.a = a;
+    sa.work = reinterpret_cast<uint64_t*>(ws.sums);
+    sa.gens = ws.gens;
+    sa.region = static_cast<int>(region);
+    sa.status = ws.status;
+    sa.split = split;
+    sa.parts = parts;
+    sa.spin_limit = g_test_split_timeout ? kTestSpinLimit : kSpinLimit;
+    sa.test_mode = g_test_split_timeout;
+    sa.groups = static_cast<int>(groups);
+    hipLaunchKernelGGL(pick_fp8_split(mt, wg_waves, y_dtype), dim3(static_cast<unsigned>(groups * parts)),
+                       dim3(static_cast<unsigned>(kWave * wg_waves)), lds, static_cast<hipStream_t>(stream), sa);
+    if (hipGetLastError() != hipSuccess) return NVFP4_ERR_HIP;
+    *launched = true;
     return NVFP4_OK;
 }
 

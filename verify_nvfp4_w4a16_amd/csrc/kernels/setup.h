@@ -30,6 +30,15 @@ int gemm_partials(float** part, size_t* bytes, int* cus);
 // once to y_dtype: the group sums of a K-split product added in group order.
 int launch_ordered_sum(const float* part, int parts, int64_t mn, float t, void* y, int y_dtype, void* stream);
 
+// The many-row kernel on FP8 block-scaled weights (W8A16, at most 32 rows):
+// K in `waves` segments, `group` of them per segment group (the FP8 tile),
+// wg_waves (2, 4 or 6) wavefronts of 16 columns per workgroup, the segment
+// groups meeting through nvfp4_init's workspace, or with `whole` all in one
+// workgroup.  *launched is false, and nothing was launched, where it cannot
+// run (segments not whole 512-k windows, LDS, no workspace).
+int launch_fp8_split(const void* x, const uint8_t* w, const float* s, void* y, int64_t m, int64_t n, int64_t k,
+                     int y_dtype, int waves, int group, int wg_waves, bool whole, void* stream, bool* launched);
+
 // Several products of one (N, K) in one launch of the skinny kernels
 // (blockIdx.y picks one: a table row, a second weight over the same x, or a
 // slice of rows of one product) and the de-interleaved store.

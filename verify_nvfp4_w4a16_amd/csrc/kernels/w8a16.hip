@@ -16,6 +16,12 @@
 // k; the segment chains are added in the two-level order of the (N, K) tile,
 // so a row's bits do not depend on M or on the other rows ("10 Kernels" 10.1).
 //
+// Where x does not fit the LDS, fp8_w8a16_linear runs the NVFP4 many-row
+// kernel's FP8 form instead (fp8_w8a16_split, nvfp4_linear.hip): x in 512-k
+// windows shared by the workgroup's 16-column wavefronts, the codes and scales
+// by direct-to-LDS loads, the same MFMA inputs, block chains and two-level
+// order, the segment groups meeting through the tagged exchange.
+//
 // fp8_w8a16_gemm_kernel is the same product for any row count (the pages'
 // w8a16_gemm_n128_m128 and pipelined forms for prefill chunks), laid out like
 // nvfp4_gemm_kernel: one workgroup of eight wavefronts per CU owns 128 rows x
@@ -48,15 +54,6 @@ struct W8Args {
     float* part;           // parts > 1: group sums [parts][M][N]; workgroup (x, y) runs group y
     int parts;
 };
-
-// Eight e4m3 codes (two dwords) as the bf16 B operand, exactly.
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
-    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
-    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
-    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
-    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
-    return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
 
 template <int MT, int C, bool XLDS>
 struct W8Chunk {
@@ -529,6 +526,28 @@ extern "C" int fp8_w8a16_linear(const void* x_bf16, const uint8_t* w_e4m3, const
     // two tiles 1.1-1.3x faster on 8192 and 24576 columns; the split with two
     // tiles 1.04-1.14x faster on 4096 columns at 32 rows and no faster
     // elsewhere; four tiles never faster than two.
+    if (!xlds) {
+        // The many-row kernel where its segments are whole 512-k windows: x
+        // comes in windows shared by a workgroup's columns and the codes by
+        // direct-to-LDS loads.  Every segment group in one workgroup where
+        // that still gives each CU a workgroup (the most wavefronts per
+        // workgroup that do and whose LDS fits), else four wavefronts with the
+        // groups meeting through the workspace.  Same bits as the kernel
+        // below.  Measured on MI355X on the decode round's shapes against it:
+        // 1.11-1.46x faster at 16 and 32 rows (24576x4096 at 16 rows: 22.3
+        // against 32.6 us), 0.96-1.3x at 8 rows.
+        const int cus = nvfp4::device_cus();
+        bool launched = false;
+        for (int w : {6, 4, 2}) {
+            if (n / (16 * w) < cus) continue;
+            st = nvfp4::launch_fp8_split(x_bf16, w_e4m3, block_scales, y, m, n, k, y_dtype, waves, group, w, true,
+                                         stream, &launched);
+            if (st != NVFP4_OK || launched) return st;
+        }
+        st = nvfp4::launch_fp8_split(x_bf16, w_e4m3, block_scales, y, m, n, k, y_dtype, waves, group, 4, false,
+                                     stream, &launched);
+        if (st != NVFP4_OK || launched) return st;
+    }
     int c = 1, parts = 1;
     float* buf = nullptr;
     if (!xlds) {

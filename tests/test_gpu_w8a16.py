@@ -123,6 +123,25 @@ def test_w8a16_gemm_rows_equal_linear_rows_and_parity():
         _parity(_gemm(xd, wd, sd, 70, n, k, torch.float32), x[:70], codes, scales, cols, f"w8a16 gemm {n}x{k} fp32")
 
 
+def test_w8a16_many_row_form_fp32_and_ragged_groups():
+    # The many-row form at each of its dispatches, fp32 and bf16 output:
+    # 4096 columns (segment groups meeting through the exchange), 8192
+    # (whole K, two wavefronts), 24704 (whole K, six wavefronts, the last
+    # workgroup's columns past N); rows equal the FP8 GEMM's, parity on
+    # sampled columns including the last ones.
+    for n, k, ms in [(4096, 4096, (9, 16, 32)), (8192, 4096, (16, 17)), (24704, 4096, (16,))]:
+        codes, scales = nv.fp8_pack(workload.weights_f32(n, k, 500 + n // 128))
+        wd, sd = upload_u8(codes), torch.from_numpy(scales).to(DEV)
+        x = workload.activations_bf16(32, k, 600 + n // 128, outliers=True)
+        cols = np.unique(np.concatenate([np.arange(16), np.arange(n - 48, n), workload.rng(n + 2).integers(0, n, 64)]))
+        for m in ms:
+            xd = upload_bits(x[:m])
+            for out in (torch.float32, torch.bfloat16):
+                y = _run(xd, wd, sd, m, n, k, out)
+                assert torch.equal(bits(y), bits(_gemm(xd, wd, sd, m, n, k, out))), (n, k, m, out)
+                _parity(y, x[:m], codes, scales, cols, f"w8a16 many-row {n}x{k}")
+
+
 def test_w8a16_gemm_contract_and_errors():
     assert nv.fp8_gemm_shape_ok(0, 128, 128) and nv.fp8_gemm_shape_ok(4096, 8192, 4096)
     assert not nv.fp8_gemm_shape_ok(64, 100, 128) and not nv.fp8_gemm_shape_ok(64, 128, 100)

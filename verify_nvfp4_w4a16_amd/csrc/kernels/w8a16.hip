@@ -516,16 +516,6 @@ extern "C" int fp8_w8a16_linear(const void* x_bf16, const uint8_t* w_e4m3, const
     const int mt = m <= 16 ? 1 : 2;
     const size_t x_bytes = size_t(m) * (k + 8) * sizeof(uint16_t);
     const bool xlds = x_bytes <= kXLdsMax;
-    // Where x is read from memory each workgroup reads its x slice once for
-    // its 16 c columns: two column tiles per wavefront halve those reads
-    // where 32-column workgroups still cover the CUs.  Where they do not and
-    // there are two row tiles (x reads largest), K is split into the tile's
-    // segment groups instead, one per workgroup, their sums added in order
-    // by a second kernel through the buffer nvfp4_init allocates (same bits).
-    // Measured on MI355X at 16 and 32 rows on the decode round's shapes:
-    // two tiles 1.1-1.3x faster on 8192 and 24576 columns; the split with two
-    // tiles 1.04-1.14x faster on 4096 columns at 32 rows and no faster
-    // elsewhere; four tiles never faster than two.
     if (!xlds) {
         // The many-row kernel where its segments are whole 512-k windows: x
         // comes in windows shared by a workgroup's columns and the codes by
@@ -548,6 +538,16 @@ extern "C" int fp8_w8a16_linear(const void* x_bf16, const uint8_t* w_e4m3, const
                                      stream, &launched);
         if (st != NVFP4_OK || launched) return st;
     }
+    // Otherwise, where x is read from memory, each workgroup reads its x
+    // slice once for its 16 c columns: two column tiles per wavefront halve
+    // those reads where 32-column workgroups still cover the CUs.  Where they do not and
+    // there are two row tiles (x reads largest), K is split into the tile's
+    // segment groups instead, one per workgroup, their sums added in order
+    // by a second kernel through the buffer nvfp4_init allocates (same bits).
+    // Measured on MI355X at 16 and 32 rows on the decode round's shapes:
+    // two tiles 1.1-1.3x faster on 8192 and 24576 columns; the split with two
+    // tiles 1.04-1.14x faster on 4096 columns at 32 rows and no faster
+    // elsewhere; four tiles never faster than two.
     int c = 1, parts = 1;
     float* buf = nullptr;
     if (!xlds) {

@@ -78,8 +78,8 @@ struct GemmArgs {
     int m, n, k;
     int k_per_wave;         // segment length
     int group;              // segments per segment group
-    float* part;            // parts > 1: group sums [parts][M][N] (fp32, t not applied)
-    int parts;              // workgroups along K (blockIdx.z): 1, or one per segment group
+    float* part;            // parts > 1: group sums or segment chains [parts][M][N] (fp32, t not applied)
+    int parts;              // workgroups along K (blockIdx.z): 1, one per segment group, or one per segment
 };
 
 // The B operands of one 128-k block for a lane's kC columns: with NVFP4
@@ -318,7 +318,8 @@ nvfp4_gemm_kernel(GemmArgs a) {
     }
 
     if (a.parts > 1) {
-        // one group's sum per output; launch_ordered_sum adds the groups in order
+        // one group's sum (or one segment's chain) per output; launch_ordered_sum
+        // adds them in the two-level order
         float* dst = a.part + (int64_t)blockIdx.z * a.m * a.n;
 #pragma unroll
         for (int t = 0; t < kMT; ++t)
@@ -352,19 +353,33 @@ nvfp4_gemm_kernel(GemmArgs a) {
         }
 }
 
-// The group sums of a K-split product [parts][M][N] added in group order
-// (the second level of the tile's order), times t, one rounding: each thread
-// four consecutive outputs of the flattened [M][N].
+// The partial sums of a K-split product [parts][M][N] added in the tile's
+// two-level order, times t, one rounding: `group` consecutive parts form a
+// group (1: each part is already a group sum), each group summed in part
+// order, then the group sums in group order, the first of each as it is.
+// Each thread four consecutive outputs of the flattened [M][N].
 template <bool OUT_F32>
 __global__ void __launch_bounds__(256)
-nvfp4_gemm_reduce(const float* part, int parts, int64_t mn, float t, void* y) {
+nvfp4_gemm_reduce(const float* part, int parts, int group, int64_t mn, float t, void* y) {
     const int64_t i0 = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
     if (i0 >= mn) return;
     const int cnt = mn - i0 < 4 ? static_cast<int>(mn - i0) : 4;
     float tot[4];
     for (int j = 0; j < cnt; ++j) tot[j] = part[i0 + j];
-    for (int q = 1; q < parts; ++q)
-        for (int j = 0; j < cnt; ++j) tot[j] = tot[j] + part[(int64_t)q * mn + i0 + j];
+    if (group == 1) {
+        for (int q = 1; q < parts; ++q)
+            for (int j = 0; j < cnt; ++j) tot[j] = tot[j] + part[(int64_t)q * mn + i0 + j];
+    } else {
+        float grp[4];
+        for (int q = 1; q < group; ++q)
+            for (int j = 0; j < cnt; ++j) tot[j] = tot[j] + part[(int64_t)q * mn + i0 + j];
+        for (int g = group; g < parts; g += group) {
+            for (int j = 0; j < cnt; ++j) grp[j] = part[(int64_t)g * mn + i0 + j];
+            for (int q = g + 1; q < g + group; ++q)
+                for (int j = 0; j < cnt; ++j) grp[j] = grp[j] + part[(int64_t)q * mn + i0 + j];
+            for (int j = 0; j < cnt; ++j) tot[j] = tot[j] + grp[j];
+        }
+    }
     for (int j = 0; j < cnt; ++j) {
         const float r = tot[j] * t;
         if (OUT_F32)
@@ -461,6 +476,12 @@ int gemm_launch(const void* x, const void* w, const uint8_t* scales, float t, vo
             size_t(tile.split) * size_t(m) * size_t(n) * sizeof(float) <= bytes) {
             a.part = part;
             a.parts = tile.split;
+            // Where the segment groups still leave half the CUs idle, one
+            // workgroup per segment instead; the reduce then forms the
+            // group sums first (same order, same bits).
+            if (2 * row_tiles * col_tiles * tile.split <= int64_t(cus) && tile.waves > tile.split &&
+                size_t(tile.waves) * size_t(m) * size_t(n) * sizeof(float) <= bytes)
+                a.parts = tile.waves;
         }
     }
     const dim3 grid(static_cast<unsigned>(col_tiles), static_cast<unsigned>(row_tiles),
@@ -468,7 +489,8 @@ int gemm_launch(const void* x, const void* w, const uint8_t* scales, float t, vo
     hipLaunchKernelGGL(pick_gemm(bf16w, y_dtype), grid, dim3(kThreads), bf16w ? kGemmLdsBf : kGemmLdsNv,
                        static_cast<hipStream_t>(stream), a);
     if (hipGetLastError() != hipSuccess) return NVFP4_ERR_HIP;
-    if (a.parts > 1) return nvfp4::launch_ordered_sum(a.part, a.parts, m * n, t, y, y_dtype, stream);
+    if (a.parts > 1)
+        return nvfp4::launch_ordered_sum(a.part, a.parts, m * n, t, y, y_dtype, stream, a.parts / tile.split);
     return NVFP4_OK;
 }
 
@@ -476,11 +498,13 @@ int gemm_launch(const void* x, const void* w, const uint8_t* scales, float t, vo
 
 namespace nvfp4 {
 
-int launch_ordered_sum(const float* part, int parts, int64_t mn, float t, void* y, int y_dtype, void* stream) {
+int launch_ordered_sum(const float* part, int parts, int64_t mn, float t, void* y, int y_dtype, void* stream,
+                       int group) {
+    if (group < 1 || parts % group != 0) return NVFP4_ERR_SHAPE;
     const int64_t blocks = (mn + 1023) / 1024;
     auto red = y_dtype == NVFP4_OUT_F32 ? nvfp4_gemm_reduce<true> : nvfp4_gemm_reduce<false>;
     hipLaunchKernelGGL(red, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream),
-                       part, parts, mn, t, y);
+                       part, parts, group, mn, t, y);
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 

@@ -28,7 +28,11 @@ int gemm_partials(float** part, size_t* bytes, int* cus);
 
 // y[i] = t * (((part[0][i] + part[1][i]) + part[2][i]) + ...), i < mn, rounded
 // once to y_dtype: the group sums of a K-split product added in group order.
-int launch_ordered_sum(const float* part, int parts, int64_t mn, float t, void* y, int y_dtype, void* stream);
+// With group > 1 the parts are segment chains, `group` consecutive ones
+// forming a group: each group is summed in order first, then the group sums
+// (the tile's two-level order).  SHAPE if group does not divide parts.
+int launch_ordered_sum(const float* part, int parts, int64_t mn, float t, void* y, int y_dtype, void* stream,
+                       int group = 1);
 
 // The many-row kernel on FP8 block-scaled weights (W8A16, at most 32 rows):
 // K in `waves` segments, `group` of them per segment group (the FP8 tile),

@@ -435,10 +435,12 @@ int nvfp4_gemm_shape_ok(int64_t m, int64_t n, int64_t k);
  * every M ("10 Kernels" 10.1).  No allocation (the first call on a device
  * runs nvfp4_init's set-up unless it has run), no host sync.  Workgroups own
  * 128 rows x 128 columns; when that gives workgroups for at most half the
- * CUs and the tile has split > 1, each workgroup takes one segment group and a second
- * kernel adds the group sums in order through the device buffer nvfp4_init
- * allocates (same bits): such calls on one device must not overlap in time
- * (calls on one stream, or on streams ordered by events, never do).
+ * CUs and the tile has split > 1, each workgroup takes one segment group
+ * (one segment where even the groups would leave half the CUs idle) and a
+ * second kernel adds the partial sums in the tile's order through the device
+ * buffer nvfp4_init allocates (same bits): such calls on one device must not
+ * overlap in time (calls on one stream, or on streams ordered by events,
+ * never do).
  * Errors: NULL, SHAPE, ALIGN, DTYPE, HIP, DEVICE, TILEFILE.
  */
 int nvfp4_gemm(const void* x_bf16, const uint8_t* w_packed, const uint8_t* scales_e4m3,

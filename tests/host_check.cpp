@@ -90,6 +90,10 @@ static void contract_cases() {
     CHECK(nvfp4_linear_shape_ok(1, 1, (int64_t(1) << 20) + 256) == NVFP4_ERR_SHAPE);
     CHECK(nvfp4_gemm_shape_ok(4096, 8192, 4096) == NVFP4_OK && nvfp4_gemm_shape_ok(65535 * 128 + 1, 1, 256) != 0);
     CHECK(nvfp4_gemm_shape_ok(1, 1, 100) == NVFP4_ERR_SHAPE && nvfp4_gemm_shape_ok(-1, 1, 256) == NVFP4_ERR_SHAPE);
+    CHECK(fp8_w8a16_gemm_shape_ok(0, 128, 128) == NVFP4_OK && fp8_w8a16_gemm_shape_ok(65535 * 128, 128, 128) == NVFP4_OK);
+    CHECK(fp8_w8a16_gemm_shape_ok(65535 * 128 + 1, 128, 128) == NVFP4_ERR_SHAPE);
+    CHECK(fp8_w8a16_gemm_shape_ok(64, 100, 128) == NVFP4_ERR_SHAPE && fp8_w8a16_gemm_shape_ok(64, 128, 64) == NVFP4_ERR_SHAPE);
+    CHECK(fp8_w8a16_gemm_shape_ok(int64_t(1) << 22, int64_t(1) << 19, 128) == NVFP4_ERR_SHAPE);   // M * N above 2^40
     for (int st = 1; st >= -40; --st) CHECK(nvfp4_strerror(st) != nullptr);
 }
 

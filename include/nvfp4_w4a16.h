@@ -513,8 +513,9 @@ int nvfp4_gemm_library(const void* x_bf16, const void* w_bf16, float tensor_scal
  * w_bf16_scratch (device, caller-owned, N * K * 2 bytes, 16-byte aligned; its
  * contents are overwritten) by nvfp4_dequant_bf16 without the tensor scale,
  * then nvfp4_gemm_library (those rows carry the library's bits, within the
- * same error bound).  expand_min_m = 0 takes 1,024, the pages' boundary and
- * on MI355X about where expanding per call starts to pay; the scratch may be
+ * same error bound).  expand_min_m = 0 takes 768: the pages put the boundary
+ * at about 1,024 rows; on MI355X expanding per call is ahead from 768 rows on
+ * the decode round's four shapes (mixed at 384..512).  The scratch may be
  * NULL when M stays below the threshold.  A caller that keeps the expanded
  * weight calls nvfp4_gemm_library directly.  Shape contract: nvfp4_gemm's.
  * Errors: SHAPE (also a negative expand_min_m), NULL, and those of the calls

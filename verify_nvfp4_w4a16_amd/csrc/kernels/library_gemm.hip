@@ -135,11 +135,13 @@ extern "C" int nvfp4_matmul_expand(const void* x_bf16, const uint8_t* w_packed, 
                                    float tensor_scale, void* y, int64_t m, int64_t n, int64_t k, int y_dtype,
                                    void* w_bf16_scratch, int64_t expand_min_m, void* stream) {
     if (expand_min_m < 0) return NVFP4_ERR_SHAPE;
-    // From about 1,024 rows on, expanding once per call and running the
-    // library GEMM is ahead of nvfp4_gemm on MI355X (measured on the decode
-    // round's shapes: 77-213 us against 110-302 us at 1,024 rows, about half
-    // the time at 4,096).
-    const int64_t from = expand_min_m == 0 ? 1024 : expand_min_m;
+    // From 768 rows on, expanding once per call and running the library GEMM
+    // is ahead of nvfp4_matmul on MI355X on all four decode-round shapes
+    // (same-box, order-balanced: 66-186 us against 88-233 us at 768 rows,
+    // 76-203 against 94-282 at 1,024, about half the time at 4,096; at 384
+    // and 512 rows it depends on the shape, within 10 %).  The pages put the
+    // boundary at about 1,024 rows.
+    const int64_t from = expand_min_m == 0 ? 768 : expand_min_m;
     if (m < from) return nvfp4_matmul(x_bf16, w_packed, scales_e4m3, tensor_scale, y, m, n, k, y_dtype, stream);
     int st = nvfp4_gemm_shape_ok(m, n, k);
     if (st != NVFP4_OK) return st;

@@ -241,16 +241,17 @@ def test_tile_info_depends_on_shape_only():
 def test_default_split_fills_the_chip():
     # Segment groups: enough 128-column workgroups for every one of 256 CUs,
     # at most one group per segment; a function of N (and K through waves).
-    for n, k, split in [(4096, 4096, 8), (12288, 4096, 4), (32768, 4096, 1), (16384, 4096, 2),
+    for n, k, split in [(4096, 2048, 8), (12288, 2048, 4), (32768, 4096, 1), (16384, 4096, 2),
                         (65536, 4096, 1), (151552, 4096, 1), (4096, 256, 2), (16, 1024, 8)]:
         t = nv.table_tile(n, k)
         assert t.split == min(split, t.waves), (n, k, t)
 
 
 def test_builtin_table_entries():
-    # Sweep-picked segment counts and groupings of the decode round's products.
+    # Sweep-picked segment counts and groupings of the decode round's products
+    # and of the row-invariance and fused-QKV configurations.
     for n, k, waves, split, mwaves in [(8192, 4096, 8, 4, 0), (4096, 8192, 8, 4, 4), (24576, 4096, 4, 1, 6),
-                                       (4096, 12288, 8, 4, 4)]:
+                                       (4096, 12288, 8, 4, 4), (4096, 4096, 8, 4, 4), (12288, 4096, 8, 2, 8)]:
         t = nv.table_tile(n, k)
         assert (t.cols, t.waves, t.split, t.mwaves) == (16, waves, split, mwaves), (n, k, t)
 

@@ -111,7 +111,8 @@ def test_gemm_k_split_rows_equal_unsplit():
 def test_gemm_ragged_rows_random_codes():
     # Partial row tiles (M = 200, 129, 1), columns past N, every code and
     # scale byte incl. subnormal scales and zero groups, split shapes.
-    for n, k, m in [(333, 1024, 200), (4111, 512, 129), (17, 256, 1), (1000, 2048, 300)]:
+    # (24704 columns at 200 rows: 64-row tiles, ragged in rows and columns)
+    for n, k, m in [(333, 1024, 200), (4111, 512, 129), (17, 256, 1), (1000, 2048, 300), (24704, 1024, 200)]:
         packed, scales = workload.random_codes(n, k, n + k)
         scales[:, ::5] = 0
         w = Weight(packed, scales, 0.0371)

@@ -10,7 +10,9 @@
 // blocks, waited for by count, one barrier per block); each wavefront decodes
 // the weights of its 32 columns from LDS into registers and multiplies them
 // with 64 rows of x (v_mfma_f32_16x16x32_bf16, 4 x 2 tiles), so one decoded
-// operand serves four MFMAs.  Column tiles are the fastest grid dimension, so
+// operand serves four MFMAs.  nvfp4_gemm64_kernel is the same body on 64-row
+// tiles (four wavefronts, two workgroups per CU) for row counts whose
+// 128-row tiles would leave a partial second round of workgroups.  Column tiles are the fastest grid dimension, so
 // the eight XCDs (workgroups dealt round-robin) each keep one eighth of the
 // weight columns in their L2 across the row tiles.
 //
@@ -40,18 +42,12 @@
 
 namespace {
 
-constexpr int kRows = 128;              // rows per workgroup
 constexpr int kCols = 128;              // columns per workgroup
 constexpr int kMT = 4;                  // 16-row tiles per wavefront
 constexpr int kC = 2;                   // 16-column tiles per wavefront
 constexpr int kWavesN = kCols / (16 * kC);             // wavefronts across the columns
-constexpr int kWaves = (kRows / (16 * kMT)) * kWavesN;  // 2 (rows) x 4 (columns)
-constexpr int kThreads = kWaves * kWave;
 constexpr int kPitch = kBlockK;         // LDS row of an x block: 16 pieces of 8 k, swizzled
-constexpr int kXRowsPerWave = kRows / kWaves;           // x rows each wavefront stages
-constexpr int kXLoads = kXRowsPerWave / 4;              // 1 KB direct loads (4 rows) per wavefront per block
 constexpr int kXBufs = 3;               // x blocks in the LDS ring
-constexpr size_t kXBytes = kXBufs * size_t(kRows) * kPitch * sizeof(uint16_t);
 // NVFP4 weights come into LDS too, three 128-k blocks deep: per block the
 // packed bytes of the 128 columns (eight 1 KB column tiles: lane l of tile c
 // holds column 16 c + l % 16, 32-k quarter l / 16) and their scale bytes
@@ -60,12 +56,25 @@ constexpr size_t kXBytes = kXBufs * size_t(kRows) * kPitch * sizeof(uint16_t);
 constexpr int kWStages = 3;
 constexpr int kWPacked = kCols * kBlockK / 2;
 constexpr int kWStage = kWPacked + (kCols / 16) * 256;
-constexpr size_t kGemmLdsNv = kXBytes + size_t(kWStages) * kWStage;
-constexpr size_t kGemmLdsBf = kXBytes;
-constexpr int kWTilesPerWave = kCols / 16 / kWaves;    // weight column tiles each wavefront stages
-constexpr int kWLoads = 2 * kWTilesPerWave;             // its direct loads per block (packed, scales)
-static_assert(kWTilesPerWave >= 1 && kWTilesPerWave * kWaves * 16 == kCols, "weight staging");
-static_assert(kXLoads >= 1 && kXLoads * 4 * kWaves == kRows, "x staging");
+
+// A workgroup tile of ROWS rows x kCols columns: 128 (eight wavefronts, one
+// workgroup per CU) or 64 (four wavefronts, two workgroups per CU); each
+// wavefront keeps 64 rows x 32 columns.
+template <int ROWS>
+struct GemmTile {
+    static constexpr int kRows = ROWS;
+    static constexpr int kWaves = (ROWS / (16 * kMT)) * kWavesN;     // (rows) x 4 (columns)
+    static constexpr int kThreads = kWaves * kWave;
+    static constexpr int kXRowsPerWave = ROWS / kWaves;              // x rows each wavefront stages
+    static constexpr int kXLoads = kXRowsPerWave / 4;                // 1 KB direct loads (4 rows) per block
+    static constexpr size_t kXBytes = kXBufs * size_t(ROWS) * kPitch * sizeof(uint16_t);
+    static constexpr size_t kLdsNv = kXBytes + size_t(kWStages) * kWStage;
+    static constexpr size_t kLdsBf = kXBytes;
+    static constexpr int kWTilesPerWave = kCols / 16 / kWaves;       // weight column tiles each wavefront stages
+    static constexpr int kWLoads = 2 * kWTilesPerWave;                // its direct loads per block (packed, scales)
+    static_assert(kWTilesPerWave >= 1 && kWTilesPerWave * kWaves * 16 == kCols, "weight staging");
+    static_assert(kXLoads >= 1 && kXLoads * 4 * kWaves == ROWS, "x staging");
+};
 
 constexpr int64_t kChunkedMaxM = 64;    // nvfp4_matmul: 32-row slices of the skinny product up to here
 
@@ -99,10 +108,13 @@ struct BRegs<true> {
     u32x4 w[kC][4];
 };
 
-template <bool BF16W, bool OUT_F32>
-__global__ void __launch_bounds__(kThreads, 1)
-nvfp4_gemm_kernel(GemmArgs a) {
-    extern __shared__ __align__(16) uint16_t xs[];     // [2][kRows][kPitch]
+template <int ROWS, bool BF16W, bool OUT_F32>
+__device__ __forceinline__ void gemm_body(const GemmArgs& a) {
+    using T = GemmTile<ROWS>;
+    constexpr int kRows = T::kRows, kWaves = T::kWaves, kXRowsPerWave = T::kXRowsPerWave, kXLoads = T::kXLoads,
+                  kWTilesPerWave = T::kWTilesPerWave, kWLoads = T::kWLoads;
+    constexpr size_t kXBytes = T::kXBytes;
+    extern __shared__ __align__(16) uint16_t xs[];     // [kXBufs][kRows][kPitch], then the weight ring
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -353,6 +365,19 @@ nvfp4_gemm_kernel(GemmArgs a) {
         }
 }
 
+template <bool BF16W, bool OUT_F32>
+__global__ void __launch_bounds__(GemmTile<128>::kThreads, 1)
+nvfp4_gemm_kernel(GemmArgs a) {
+    gemm_body<128, BF16W, OUT_F32>(a);
+}
+
+// The same product on 64-row workgroup tiles, two workgroups per CU.
+template <bool BF16W, bool OUT_F32>
+__global__ void __launch_bounds__(GemmTile<64>::kThreads, 2)
+nvfp4_gemm64_kernel(GemmArgs a) {
+    gemm_body<64, BF16W, OUT_F32>(a);
+}
+
 // The partial sums of a K-split product [parts][M][N] added in the tile's
 // two-level order, times t, one rounding: `group` consecutive parts form a
 // group (1: each part is already a group sum), each group summed in part
@@ -425,9 +450,15 @@ nvfp4_dequant_kernel(const uint8_t* wp, const uint8_t* sc, float t, uint16_t* ds
 
 using GemmFn = void (*)(GemmArgs);
 
-GemmFn pick_gemm(bool bf16w, int y_dtype) {
-    if (bf16w) return y_dtype == NVFP4_OUT_F32 ? nvfp4_gemm_kernel<true, true> : nvfp4_gemm_kernel<true, false>;
-    return y_dtype == NVFP4_OUT_F32 ? nvfp4_gemm_kernel<false, true> : nvfp4_gemm_kernel<false, false>;
+// rows: the workgroup tile's rows, 128 or 64
+GemmFn pick_gemm(bool bf16w, int y_dtype, int rows) {
+    const bool f = y_dtype == NVFP4_OUT_F32;
+    if (rows == 64) {
+        if (bf16w) return f ? nvfp4_gemm64_kernel<true, true> : nvfp4_gemm64_kernel<true, false>;
+        return f ? nvfp4_gemm64_kernel<false, true> : nvfp4_gemm64_kernel<false, false>;
+    }
+    if (bf16w) return f ? nvfp4_gemm_kernel<true, true> : nvfp4_gemm_kernel<true, false>;
+    return f ? nvfp4_gemm_kernel<false, true> : nvfp4_gemm_kernel<false, false>;
 }
 
 int gemm_launch(const void* x, const void* w, const uint8_t* scales, float t, void* y, int64_t m, int64_t n,
@@ -458,36 +489,57 @@ int gemm_launch(const void* x, const void* w, const uint8_t* scales, float t, vo
     a.group = tile.waves / tile.split;
     a.part = nullptr;
     a.parts = 1;
-    const int64_t col_tiles = (n + kCols - 1) / kCols, row_tiles = (m + kRows - 1) / kRows;
+    float* part = nullptr;
+    size_t bytes = 0;
+    int cus = 256;
+    if (tile.split > 1) {
+        st = nvfp4::gemm_partials(&part, &bytes, &cus);
+        if (st != NVFP4_OK) return st;
+    } else {
+        cus = nvfp4::device_cus();
+    }
+    const int64_t col_tiles = (n + kCols - 1) / kCols;
     // Tiles for at most half the CUs (one workgroup per CU): one workgroup
     // per segment group instead (the tile's split), the group sums added in
     // order by a second kernel, so the bits do not change.  Needs the
     // partial-sum buffer nvfp4_init allocates.  (Measured on MI355X: faster
     // at 256..512 rows on the decode round's products; with tiles for every
     // CU, e.g. 4096 columns at 1024 rows, the extra partial-sum traffic costs
-    // more than the split gains.)
-    if (tile.split > 1) {
-        float* part = nullptr;
-        size_t bytes = 0;
-        int cus = 256;
-        st = nvfp4::gemm_partials(&part, &bytes, &cus);
-        if (st != NVFP4_OK) return st;
-        if (part && 2 * row_tiles * col_tiles <= int64_t(cus) &&
+    // more than the split gains.)  Where the segment groups still leave half
+    // the CUs idle, one workgroup per segment instead; the reduce then forms
+    // the group sums first (same order, same bits).
+    auto parts_for = [&](int64_t row_tiles) {
+        int parts = 1;
+        if (tile.split > 1 && part && 2 * row_tiles * col_tiles <= int64_t(cus) &&
             size_t(tile.split) * size_t(m) * size_t(n) * sizeof(float) <= bytes) {
-            a.part = part;
-            a.parts = tile.split;
-            // Where the segment groups still leave half the CUs idle, one
-            // workgroup per segment instead; the reduce then forms the
-            // group sums first (same order, same bits).
+            parts = tile.split;
             if (2 * row_tiles * col_tiles * tile.split <= int64_t(cus) && tile.waves > tile.split &&
                 size_t(tile.waves) * size_t(m) * size_t(n) * sizeof(float) <= bytes)
-                a.parts = tile.waves;
+                parts = tile.waves;
         }
+        return parts;
+    };
+    // 64-row tiles (two workgroups per CU) up to 256 rows where the 128-row
+    // plan would need more than one round of workgroups: measured on MI355X
+    // (same-box, order-balanced) 8192x4096 at 256 rows 37.7 against 45.5 us,
+    // 24576x4096 81.0 against 90.8; elsewhere the 128-row tiles were level
+    // or ahead (64-row tiles 3-9 % slower at 1,024 rows, 10-20 % at 128).
+    int rows = 128;
+    int64_t row_tiles = (m + 127) / 128;
+    a.parts = parts_for(row_tiles);
+    if (m <= 256 && row_tiles * col_tiles * a.parts > int64_t(cus)) {
+        rows = 64;
+        row_tiles = (m + 63) / 64;
+        a.parts = parts_for(row_tiles);
     }
+    if (a.parts > 1) a.part = part;
     const dim3 grid(static_cast<unsigned>(col_tiles), static_cast<unsigned>(row_tiles),
                     static_cast<unsigned>(a.parts));
-    hipLaunchKernelGGL(pick_gemm(bf16w, y_dtype), grid, dim3(kThreads), bf16w ? kGemmLdsBf : kGemmLdsNv,
-                       static_cast<hipStream_t>(stream), a);
+    const size_t lds = rows == 64 ? (bf16w ? GemmTile<64>::kLdsBf : GemmTile<64>::kLdsNv)
+                                  : (bf16w ? GemmTile<128>::kLdsBf : GemmTile<128>::kLdsNv);
+    const int threads = rows == 64 ? GemmTile<64>::kThreads : GemmTile<128>::kThreads;
+    hipLaunchKernelGGL(pick_gemm(bf16w, y_dtype, rows), grid, dim3(threads), lds, static_cast<hipStream_t>(stream),
+                       a);
     if (hipGetLastError() != hipSuccess) return NVFP4_ERR_HIP;
     if (a.parts > 1)
         return nvfp4::launch_ordered_sum(a.part, a.parts, m * n, t, y, y_dtype, stream, a.parts / tile.split);
@@ -510,11 +562,18 @@ int launch_ordered_sum(const float* part, int parts, int64_t mn, float t, void* 
 
 int gemm_setup() {
     for (int bw = 0; bw <= 1; ++bw)
-        for (int od = 0; od <= 1; ++od)
-            if (hipFuncSetAttribute(reinterpret_cast<const void*>(pick_gemm(bw != 0, od)),
+        for (int od = 0; od <= 1; ++od) {
+            if (hipFuncSetAttribute(reinterpret_cast<const void*>(pick_gemm(bw != 0, od, 128)),
                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    static_cast<int>(bw ? kGemmLdsBf : kGemmLdsNv)) != hipSuccess)
+                                    static_cast<int>(bw ? GemmTile<128>::kLdsBf : GemmTile<128>::kLdsNv)) !=
+                hipSuccess)
                 return NVFP4_ERR_HIP;
+            if (hipFuncSetAttribute(reinterpret_cast<const void*>(pick_gemm(bw != 0, od, 64)),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    static_cast<int>(bw ? GemmTile<64>::kLdsBf : GemmTile<64>::kLdsNv)) !=
+                hipSuccess)
+                return NVFP4_ERR_HIP;
+        }
     return NVFP4_OK;
 }
 
